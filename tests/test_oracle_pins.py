@@ -1,0 +1,529 @@
+"""Pins of the CPU oracle against things other than itself: format
+definitions and library conversions, hand-worked fixtures, brute force on tiny
+inputs, closed forms and invariants. Each test is chosen so that a plausible
+mistake in the oracle (a dropped term, a wrong sign or index, a transposed
+operand, a wrong tie rule) fails it. CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import tsd_synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- decoders
+def test_fp8_golden_points(orc):
+    for line in open(os.path.join(GOLDEN, "fp8_e4m3_ocp.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = orc.decode_fp8_e4m3(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == float(val), code
+            assert math.copysign(1.0, got) == math.copysign(1.0, float(val))
+
+
+def test_fp8_exhaustive_against_torch(orc):
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([orc.decode_fp8_e4m3(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert nan.sum() == 2  # 0x7F and 0xFF only
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.nanmax(np.abs(got)) == 448.0
+
+
+def test_bf16_exhaustive_against_torch(orc):
+    codes = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = codes.view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.decode_bf16(c) for c in range(65536)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_fp16_exhaustive_against_numpy(orc):
+    ref = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    ref = ref.astype(np.float64)
+    got = np.array([orc.decode_fp16(c) for c in range(65536)])
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+# ------------------------------------------------------------- slot mapping
+def _golden_slots():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "slot_mapping.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        rows.append(tuple(int(x) for x in line.split()))
+    return rows
+
+
+PT_GOLDEN = np.array([[3, 0, 2], [1, 4, 5]], np.int32)
+
+
+def test_slot_golden(orc):
+    for b, t, want in _golden_slots():
+        assert orc.slot(PT_GOLDEN, b, t, 64, 6) == want
+    assert orc.slot(np.array([[9]], np.int32), 0, 5, 64, 6) == -1
+    assert orc.slot(np.array([[-1]], np.int32), 0, 5, 64, 6) == -1
+
+
+def test_ds_scores_read_the_mapped_slot(orc):
+    """Label value = its own slot number (exact in fp16); one channel, unit
+    query -> each score must be the golden slot of that token."""
+    slots = 6 * 64
+    label = torch.arange(slots, dtype=torch.float32).to(torch.float16)
+    label = label.view(slots, 1, 1).view(torch.int16).numpy().view(np.uint16)
+    q = torch.zeros(2, 1, 4, dtype=torch.float16)
+    q[:, 0, 2] = 1.0
+    qc = q.view(torch.int16).numpy().view(np.uint16)
+    chan = np.array([[2]], np.int32)
+    lens = np.array([192, 192], np.int32)
+    s = orc.ds_scores(qc, "fp16", chan, label, "fp16", PT_GOLDEN, lens, 6)
+    for b, t, want in _golden_slots():
+        assert s[b, t] == want
+
+
+def test_ds_scores_stop_at_length_and_skip_stale_tail(orc):
+    label = np.ones((6 * 64, 1, 1), np.uint16) * 0x3C00  # fp16 1.0
+    q = np.ones((1, 1, 1), np.uint16) * 0x3C00
+    pt = np.array([[3, 99, -4]], np.int32)  # only page 3 is live
+    s = orc.ds_scores(q, "fp16", np.array([[0]], np.int32), label, "fp16",
+                      pt, np.array([10], np.int32), 6, score_stride=20)
+    assert (s[0, :10] == 1.0).all() and np.isnan(s[0, 10:]).all()
+
+
+# ------------------------------------------------------------------- scores
+def _f64(t):
+    return t.to(torch.float64).numpy()
+
+
+def _ident_cfg(**kw):
+    base = dict(name="pin", mode="qsa", B=2, L=200, H_q=8, H_kv=2, D=32,
+                top_k=16, chunks=3, kv_enc="fp8_e4m3", seed=11, H_i=4, D_i=32)
+    base.update(kw)
+    return tsd_synth.Config(**base)
+
+
+def _identity_pages(wl):
+    """Rewrite a workload so request b's pages are physically contiguous and
+    in order (slot of token t of request b = b * cap * 64 + t)."""
+    pt = wl["page_table"].clone()
+    B, cap = pt.shape
+    perm_slots = []
+    for b in range(B):
+        for j in range(cap):
+            p = int(pt[b, j])
+            perm_slots.extend(range(p * 64, p * 64 + 64))
+            pt[b, j] = b * cap + j
+    idx = torch.tensor(perm_slots)
+    out = dict(wl)
+    for key in ("index_k", "k_pool", "v_pool", "label_pool"):
+        if key in wl and wl[key] is not None:
+            out[key] = wl[key][idx].contiguous()
+    pages = idx.view(-1, 64)[:, 0] // 64
+    for key in ("k_scale", "v_scale"):
+        if wl.get(key) is not None:
+            out[key] = wl[key][pages].contiguous()
+    out["page_table"] = pt
+    return out
+
+
+def test_qsa_scores_brute_force_einsum(orc):
+    wl = tsd_synth.make(_ident_cfg(lens=(200, 77)))
+    h = tsd_synth.to_host(wl)
+    s = orc.qsa_scores(h["index_q"], h["index_w"], h["index_k"],
+                       h["page_table"], h["seq_lens"], h["num_pages"])
+    iq = _f64(wl["index_q"].view(torch.float8_e4m3fn))
+    ik = _f64(wl["index_k"].view(torch.float8_e4m3fn))
+    w = wl["index_w"].to(torch.float64).numpy()
+    for b in range(2):
+        n = int(wl["seq_lens"][b])
+        t = np.arange(n)
+        slots = wl["page_table"][b].numpy()[t // 64] * 64 + t % 64
+        dots = np.einsum("hd,td->ht", iq[b], ik[slots])
+        ref = np.einsum("h,ht->t", w[b], np.maximum(dots, 0.0))
+        np.testing.assert_allclose(s[b, :n], ref, rtol=1e-13, atol=1e-12)
+
+
+def test_qsa_special_cases(orc):
+    # one head, unit weight, positive dots: the score is the plain dot product
+    D = 16
+    one = 0x38  # fp8 1.0
+    iq = np.full((1, 1, D), one, np.uint8)
+    ik = np.zeros((64, D), np.uint8)
+    vals = torch.tensor([0.5, 1.0, 2.0, 3.0]).to(torch.float8_e4m3fn).view(torch.uint8)
+    for t in range(64):
+        ik[t] = vals[t % 4].item()
+    w = np.ones((1, 1), np.float32)
+    pt = np.zeros((1, 1), np.int32)
+    s = orc.qsa_scores(iq, w, ik, pt, np.array([64], np.int32), 1)
+    assert np.array_equal(s[0], [D * [0.5, 1, 2, 3][t % 4] for t in range(64)])
+    # negative dots are cut to zero by the ReLU, whatever the weight
+    ikn = ik | 0x80
+    s = orc.qsa_scores(iq, w * 5, ikn, pt, np.array([64], np.int32), 1)
+    assert (s[0] == 0.0).all()
+    # two heads: only the positive head contributes, scaled by its weight
+    iq2 = np.stack([np.full(D, one, np.uint8), np.full(D, one | 0x80, np.uint8)])[None]
+    w2 = np.array([[0.25, 7.0]], np.float32)
+    s = orc.qsa_scores(iq2, w2, ik, pt, np.array([64], np.int32), 1)
+    assert np.array_equal(s[0], [0.25 * D * [0.5, 1, 2, 3][t % 4] for t in range(64)])
+
+
+def test_qsa_causal_rows(orc):
+    wl = tsd_synth.make(_ident_cfg(B=1, lens=(150,), rows_per_req=1))
+    h = tsd_synth.to_host(wl)
+    R = 3
+    iq = np.repeat(h["index_q"], R, axis=0)
+    iw = np.repeat(h["index_w"], R, axis=0)
+    qpos = np.array([0, 63, 149], np.int32)
+    s = orc.qsa_scores(iq, iw, h["index_k"], h["page_table"], h["seq_lens"],
+                       h["num_pages"], rows_per_req=R, q_pos=qpos)
+    full = orc.qsa_scores(h["index_q"], h["index_w"], h["index_k"],
+                          h["page_table"], h["seq_lens"], h["num_pages"])
+    for i, p in enumerate(qpos):
+        assert np.array_equal(s[i, :p + 1], full[0, :p + 1])
+        assert np.isnan(s[i, p + 1:]).all()
+
+
+def test_score_points_match_full(orc):
+    wl = tsd_synth.make(_ident_cfg(lens=(200, 77)))
+    h = tsd_synth.to_host(wl)
+    full = orc.qsa_scores(h["index_q"], h["index_w"], h["index_k"],
+                          h["page_table"], h["seq_lens"], h["num_pages"])
+    rows = np.array([0, 1, 0, 1]); ts = np.array([0, 76, 199, 3])
+    pts = orc.qsa_score_points(h["index_q"], h["index_w"], h["index_k"],
+                               h["page_table"], h["seq_lens"], h["num_pages"],
+                               rows, ts)
+    assert np.array_equal(pts, full[rows, ts])
+    with pytest.raises(orc.OracleError):
+        orc.qsa_score_points(h["index_q"], h["index_w"], h["index_k"],
+                             h["page_table"], h["seq_lens"], h["num_pages"],
+                             np.array([1]), np.array([77]))
+
+
+def _ds_cfg(**kw):
+    base = dict(name="pin", mode="ds", B=2, L=300, H_q=8, H_kv=2, D=32,
+                top_k=20, chunks=3, kv_enc="bf16", seed=5, r=6, n_outlier=3,
+                outlier_scale=6.0)
+    base.update(kw)
+    return tsd_synth.Config(**base)
+
+
+def test_ds_scores_brute_force(orc):
+    wl = tsd_synth.make(_ds_cfg(lens=(300, 65)))
+    h = tsd_synth.to_host(wl)
+    s = orc.ds_scores(h["q"], "bf16", h["channel_idx"], h["label_pool"],
+                      "bf16", h["page_table"], h["seq_lens"], h["num_pages"])
+    q = _f64(wl["q"]); lab = _f64(wl["label_pool"])
+    ch = wl["channel_idx"].numpy()
+    G = 4
+    for b in range(2):
+        n = int(wl["seq_lens"][b])
+        t = np.arange(n)
+        slots = wl["page_table"][b].numpy()[t // 64] * 64 + t % 64
+        for g in range(2):
+            qs = q[b, g * G:(g + 1) * G][:, ch[g]].sum(axis=0)
+            ref = lab[slots, g, :] @ qs
+            np.testing.assert_allclose(s[b * 2 + g, :n], ref, rtol=1e-13,
+                                       atol=1e-12)
+
+
+def test_ds_full_channels_give_group_logits(orc):
+    """r = D with identity channels: the label score is (sum of the group's
+    query heads) . K_t, i.e. the group's summed attention logits."""
+    wl = tsd_synth.make(_ds_cfg(r=32, lens=(130, 64)))
+    h = tsd_synth.to_host(wl)
+    assert (h["channel_idx"] == np.arange(32)).all()
+    s = orc.ds_scores(h["q"], "bf16", h["channel_idx"], h["label_pool"],
+                      "bf16", h["page_table"], h["seq_lens"], h["num_pages"])
+    q = _f64(wl["q"]); k = _f64(wl["k_pool"])
+    for b in range(2):
+        for g in range(2):
+            n = int(wl["seq_lens"][b])
+            t = np.arange(n)
+            slots = wl["page_table"][b].numpy()[t // 64] * 64 + t % 64
+            logits = np.einsum("hd,td->ht", q[b, g * 4:(g + 1) * 4], k[slots, g])
+            np.testing.assert_allclose(s[b * 2 + g, :n], logits.sum(0),
+                                       rtol=1e-12, atol=1e-10)
+
+
+def test_scores_invariant_under_page_permutation(orc):
+    wl = tsd_synth.make(_ident_cfg(lens=(200, 77)))
+    wi = _identity_pages(wl)
+    a, b = tsd_synth.to_host(wl), tsd_synth.to_host(wi)
+    sa = orc.qsa_scores(a["index_q"], a["index_w"], a["index_k"],
+                        a["page_table"], a["seq_lens"], a["num_pages"])
+    sb = orc.qsa_scores(b["index_q"], b["index_w"], b["index_k"],
+                        b["page_table"], b["seq_lens"], b["num_pages"])
+    assert np.array_equal(np.nan_to_num(sa, nan=-1), np.nan_to_num(sb, nan=-1))
+
+
+# -------------------------------------------------------------------- top-k
+def _brute_topk(s, k):
+    order = sorted(range(len(s)), key=lambda t: (-s[t], t))[:k]
+    out = sorted(order)
+    return out + [-1] * (k - len(out))
+
+
+def test_topk_brute_force_small(orc):
+    rng = np.random.default_rng(0)
+    values = np.array([-np.inf, -2.0, -0.0, 0.0, 0.5, 1.0, 1.0, np.inf],
+                      np.float32)
+    for trial in range(300):
+        n = int(rng.integers(0, 11))
+        s = rng.choice(values, size=max(n, 1)).astype(np.float32)[:n]
+        for k in range(1, 12):
+            idx, cnt = orc.topk(np.pad(s, (0, 12 - n))[None], [n], k)
+            assert list(idx[0]) == _brute_topk(list(s), k)
+            assert cnt[0] == min(k, n)
+
+
+def test_topk_invariants_random(orc):
+    rng = np.random.default_rng(1)
+    for n, k in [(5000, 100), (4096, 256), (300, 300), (100, 1000)]:
+        s = rng.normal(size=n).astype(np.float32)
+        s[rng.integers(0, n, 50)] = s[7]  # ties, some at the threshold
+        idx, cnt = orc.topk(s[None], [n], k)
+        m = min(k, n)
+        sel = idx[0, :m]
+        assert cnt[0] == m and (idx[0, m:] == -1).all()
+        assert (np.diff(sel) > 0).all()
+        mask = np.zeros(n, bool); mask[sel] = True
+        if m < n:
+            thr = s[mask].min()
+            assert thr >= s[~mask].max()
+            ties_in = np.where(mask & (s == thr))[0]
+            ties_out = np.where(~mask & (s == thr))[0]
+            if len(ties_out):
+                assert ties_in.max() < ties_out.min()
+
+
+def test_topk_signed_zero_tie_and_empty_rows(orc):
+    s = np.array([[-0.0, 0.0, -0.0, 0.0]], np.float32)
+    idx, cnt = orc.topk(s, [4], 2)
+    assert list(idx[0]) == [0, 1]  # -0 and +0 are one value: lowest indices win
+    idx, cnt = orc.topk(np.zeros((2, 4), np.float32), [0, -3], 3)
+    assert (idx == -1).all() and (cnt == 0).all()
+    with pytest.raises(orc.OracleError):
+        orc.topk(np.array([[1.0, np.nan]], np.float32), [2], 1)
+
+
+# ---------------------------------------------------------------- attention
+def _decoded_kv(wl, key, scale_key):
+    x = wl[key]
+    if x.dtype == torch.uint8:
+        v = x.view(torch.float8_e4m3fn).to(torch.float64)
+        sc = wl[scale_key].to(torch.float64)
+        v = v * sc.repeat_interleave(64)[:, None, None]
+        return v
+    return x.to(torch.float64)
+
+
+def _attn_case(kv_enc, lens, **kw):
+    cfg = _ident_cfg(kv_enc=kv_enc, lens=lens, D=64, **kw)
+    wl = tsd_synth.make(cfg)
+    if kv_enc != "fp8_e4m3":
+        wl["q_enc"] = kv_enc
+    return wl
+
+
+def _all_selected(wl):
+    B = wl["B"]
+    n = int(wl["seq_lens"].max())
+    idx = np.full((B, 1, n), -1, np.int32)
+    cnt = np.zeros((B, 1), np.int32)
+    for b in range(B):
+        lb = int(wl["seq_lens"][b])
+        idx[b, 0, :lb] = np.arange(lb)
+        cnt[b, 0] = lb
+    return idx, cnt
+
+
+@pytest.mark.parametrize("kv_enc", ["fp8_e4m3", "bf16"])
+def test_full_selection_is_dense_attention_sdpa(orc, kv_enc):
+    wl = _attn_case(kv_enc, (200, 77))
+    h = tsd_synth.to_host(wl)
+    idx, cnt = _all_selected(wl)
+    o, lse = orc.sparse_attention(h["q"], h["q_enc"], h["k_pool"], h["v_pool"],
+                                  h["kv_enc"], h.get("k_scale"),
+                                  h.get("v_scale"), h["page_table"],
+                                  h["seq_lens"], h["num_pages"], idx, cnt, 1)
+    dense, dlse = orc.dense_attention(h["q"], h["q_enc"], h["k_pool"],
+                                      h["v_pool"], h["kv_enc"],
+                                      h.get("k_scale"), h.get("v_scale"),
+                                      h["page_table"], h["seq_lens"],
+                                      h["num_pages"])
+    np.testing.assert_allclose(o[:, :, 0], dense, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[:, :, 0], dlse, rtol=0, atol=1e-12)
+    # independent reference: torch SDPA on CPU float64 over decoded values
+    K = _decoded_kv(wl, "k_pool", "k_scale")
+    V = _decoded_kv(wl, "v_pool", "v_scale")
+    q = wl["q"].to(torch.float64)
+    G = wl["H_q"] // wl["H_kv"]
+    for b in range(wl["B"]):
+        n = int(wl["seq_lens"][b])
+        t = torch.arange(n)
+        slots = wl["page_table"][b].long()[t // 64] * 64 + t % 64
+        Kb = K[slots].permute(1, 0, 2).repeat_interleave(G, 0)  # [H_q, n, D]
+        Vb = V[slots].permute(1, 0, 2).repeat_interleave(G, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[b][:, None, :], Kb, Vb)[:, 0]
+        np.testing.assert_allclose(o[b, :, 0], ref.numpy(), rtol=0, atol=1e-12)
+        logits = (q[b][:, None, :] @ Kb.transpose(1, 2))[:, 0] / math.sqrt(wl["D"])
+        np.testing.assert_allclose(lse[b, :, 0],
+                                   torch.logsumexp(logits, -1).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_single_token_and_identical_keys(orc):
+    wl = _attn_case("bf16", (130,), B=1)
+    h = tsd_synth.to_host(wl)
+    V = _decoded_kv(wl, "v_pool", None).numpy()
+    K = _decoded_kv(wl, "k_pool", None).numpy()
+    q = wl["q"].to(torch.float64).numpy()
+    pt = h["page_table"]
+    t = 70
+    slot = pt[0, t // 64] * 64 + t % 64
+    idx = np.array([[[t]]], np.int32)
+    o, lse = orc.sparse_attention(h["q"], "bf16", h["k_pool"], h["v_pool"],
+                                  "bf16", None, None, pt, h["seq_lens"],
+                                  h["num_pages"], idx, np.array([[1]]), 1)
+    G = 4
+    for hq in range(wl["H_q"]):
+        assert np.array_equal(o[0, hq, 0], V[slot, hq // G])
+        z = q[0, hq] @ K[slot, hq // G] / math.sqrt(wl["D"])
+        assert abs(lse[0, hq, 0] - z) < 1e-12
+    # identical keys: uniform weights, output = mean of the values
+    kp = h["k_pool"].copy()
+    sel = [3, 64, 100, 129]
+    slots = [pt[0, s // 64] * 64 + s % 64 for s in sel]
+    for s in slots:
+        kp[s] = kp[slots[0]]
+    o, lse = orc.sparse_attention(h["q"], "bf16", kp, h["v_pool"], "bf16",
+                                  None, None, pt, h["seq_lens"],
+                                  h["num_pages"], np.array([[sel]], np.int32),
+                                  np.array([[4]]), 1)
+    for hq in range(wl["H_q"]):
+        np.testing.assert_allclose(o[0, hq, 0], V[slots, hq // G].mean(0),
+                                   rtol=0, atol=1e-12)
+
+
+def test_constant_values_give_constant_output(orc):
+    wl = _attn_case("fp8_e4m3", (190, 64))
+    h = tsd_synth.to_host(wl)
+    vp = np.full_like(h["v_pool"], 0x38)  # every value 1.0 before scaling
+    vs = np.full_like(h["v_scale"], 0.75)
+    idx, cnt = _all_selected(wl)
+    o, lse = orc.sparse_attention(h["q"], "bf16", h["k_pool"], vp, "fp8_e4m3",
+                                  h["k_scale"], vs, h["page_table"],
+                                  h["seq_lens"], h["num_pages"], idx, cnt, 4)
+    np.testing.assert_allclose(o, 0.75, rtol=0, atol=1e-12)
+
+
+# -------------------------------------------------------------------- merge
+@pytest.mark.parametrize("C", [1, 2, 3, 7, 16, 64, 190])
+def test_any_chunk_split_merges_to_unsplit(orc, C):
+    wl = _attn_case("fp8_e4m3", (190, 64))
+    h = tsd_synth.to_host(wl)
+    idx, cnt = _all_selected(wl)
+    args = (h["q"], "bf16", h["k_pool"], h["v_pool"], "fp8_e4m3", h["k_scale"],
+            h["v_scale"], h["page_table"], h["seq_lens"], h["num_pages"], idx,
+            cnt)
+    o1, l1 = orc.sparse_attention(*args, 1)
+    oc, lc = orc.sparse_attention(*args, C)
+    B, H = o1.shape[:2]
+    out, lse = orc.lse_merge(oc.reshape(B * H, C, -1), lc.reshape(B * H, C))
+    np.testing.assert_allclose(out, o1[:, :, 0].reshape(B * H, -1), rtol=0,
+                               atol=1e-12)
+    np.testing.assert_allclose(lse, l1[:, :, 0].ravel(), rtol=0, atol=1e-12)
+    if C > 64:  # request 1 has 64 tokens: some chunks are empty
+        assert np.isinf(lc[1]).any() and (oc[1][np.isinf(lc[1])] == 0).all()
+
+
+def test_random_uneven_cuts_merge_to_unsplit(orc):
+    wl = _attn_case("bf16", (190,), B=1)
+    h = tsd_synth.to_host(wl)
+    rng = np.random.default_rng(3)
+    full = np.arange(190, dtype=np.int32)
+    base = (h["q"], "bf16", h["k_pool"], h["v_pool"], "bf16", None, None,
+            h["page_table"], h["seq_lens"], h["num_pages"])
+    o1, l1 = orc.sparse_attention(*base, full[None, None], np.array([[190]]), 1)
+    for _ in range(5):
+        cuts = np.sort(rng.choice(np.arange(1, 190), size=6, replace=False))
+        segs = np.split(full, cuts)
+        parts = [orc.sparse_attention(*base, s[None, None].copy(),
+                                      np.array([[len(s)]]), 1) for s in segs]
+        op = np.stack([p[0][0, :, 0] for p in parts], axis=1)  # [H, C, D]
+        lp = np.stack([p[1][0, :, 0] for p in parts], axis=1)
+        out, lse = orc.lse_merge(op, lp)
+        np.testing.assert_allclose(out, o1[0, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l1[0, :, 0], rtol=0, atol=1e-12)
+
+
+def test_merge_empty_and_identity(orc):
+    o = np.random.default_rng(0).normal(size=(3, 1, 8))
+    l = np.array([[0.3], [-2.0], [5.0]])
+    out, lse = orc.lse_merge(o, l)
+    assert np.array_equal(out, o[:, 0]) and np.array_equal(lse, l[:, 0])
+    out, lse = orc.lse_merge(np.ones((1, 4, 8)), np.full((1, 4), -np.inf))
+    assert (out == 0).all() and lse[0] == -np.inf
+    # an empty chunk next to a real one leaves the real one unchanged
+    o2 = np.concatenate([o[:1], np.zeros((1, 1, 8))], axis=1)
+    out, lse = orc.lse_merge(o2, np.array([[0.3, -np.inf]]))
+    assert np.array_equal(out[0], o[0, 0]) and lse[0] == 0.3
+
+
+def test_empty_request_gives_empty_chunks(orc):
+    wl = _attn_case("fp8_e4m3", (0, 64))
+    h = tsd_synth.to_host(wl)
+    idx, cnt = _all_selected(wl)
+    o, lse = orc.sparse_attention(h["q"], "bf16", h["k_pool"], h["v_pool"],
+                                  "fp8_e4m3", h["k_scale"], h["v_scale"],
+                                  h["page_table"], h["seq_lens"],
+                                  h["num_pages"], idx, cnt, 2)
+    assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
+    assert np.isfinite(lse[1]).all()
+
+
+# ---------------------------------------------------------- whole decode step
+def test_decode_step_topk_at_least_context_is_dense(orc):
+    cfg = _ident_cfg(lens=(150, 90), top_k=256, chunks=5, D=64)
+    wl = tsd_synth.make(cfg)
+    h = tsd_synth.to_host(wl)
+    r = orc.decode_step(h)
+    dense, dlse = orc.dense_attention(h["q"], "bf16", h["k_pool"], h["v_pool"],
+                                      "fp8_e4m3", h["k_scale"], h["v_scale"],
+                                      h["page_table"], h["seq_lens"],
+                                      h["num_pages"])
+    np.testing.assert_allclose(r["out"], dense, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["out_lse"], dlse, rtol=0, atol=1e-12)
+    assert list(r["count"].ravel()) == [150, 90]
+
+
+def test_chunk_partition_hand_worked(orc):
+    """10 selected tokens in 4 chunks are cut into contiguous runs of 2, 3, 2
+    and 3 entries of the ascending list (hand-worked from the balanced
+    partition floor(c*m/C)); each partial is attention over its run alone."""
+    wl = _attn_case("bf16", (190,), B=1)
+    h = tsd_synth.to_host(wl)
+    sel = np.array([1, 5, 9, 40, 63, 64, 100, 120, 150, 189], np.int32)
+    runs = [sel[0:2], sel[2:5], sel[5:7], sel[7:10]]
+    base = (h["q"], "bf16", h["k_pool"], h["v_pool"], "bf16", None, None,
+            h["page_table"], h["seq_lens"], h["num_pages"])
+    o4, l4 = orc.sparse_attention(*base, sel[None, None], np.array([[10]]), 4)
+    for c, run in enumerate(runs):
+        o1, l1 = orc.sparse_attention(*base, run[None, None].copy(),
+                                      np.array([[len(run)]]), 1)
+        assert np.array_equal(o4[0, :, c], o1[0, :, 0])
+        assert np.array_equal(l4[0, :, c], l1[0, :, 0])
