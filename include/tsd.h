@@ -1,0 +1,274 @@
+/*
+ * tsd.h -- C ABI of libtsd.so, top-k sparse decode attention for AMD MI355X
+ * (gfx950).
+ *
+ * The decode path is four calls, each an asynchronous launch on the caller's
+ * HIP stream:
+ *
+ *   sparse_index_score  score every cached token of every query row with a
+ *                       cheap key (double-sparsity label K, or a QSA-style
+ *                       FP8 index K);
+ *   topk_select         exact top-k per row, lowest token index first among
+ *                       equal scores, listed in ascending index order;
+ *   sparse_gqa_decode   gather the selected tokens' K/V from the 64-token
+ *                       paged cache and run GQA attention over them, split
+ *                       into chunks, with FP32 partial outputs and LSEs;
+ *   lse_merge           combine the chunks with an FP32 log-sum-exp merge.
+ *
+ * Where the operations come from (page title, section):
+ *   - "QSA HiSparse -- SGLang plugin", Supported versions / Run: FP8 E4M3
+ *     KV cache in 64-token pages, up to 8 running requests.
+ *   - "QSA cache sharding" (sglang PR #43527), Implementation: the request
+ *     token mapping into cache pages; exact Top-K with deterministic token-ID
+ *     tie-breaking; sparse attention over the selected tokens; FP32
+ *     log-sum-exp merge of partial outputs; fixed-address buffers and
+ *     consumers bounded by lengths for CUDA-graph replay.
+ *   - "Context parallelism for QSA attention and the sparse indexer" (sglang
+ *     PR #39721), Motivation: the indexer scores index keys and selects
+ *     top-k per query row, for decode and for chunked-prefill rows; sparse
+ *     GQA attention over the selection.
+ *   - "Support double sparsity" (sglang PR #1459), Speedup Evaluation and
+ *     the forward_extend traceback: label K = K at per-head heavy channels
+ *     ([tokens, heads, heavy channels]); heavy-token count = top-k.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is caller-owned DEVICE memory unless stated.
+ *     The library allocates nothing, never synchronises the stream, never
+ *     reads device memory on the host and keeps no state, so a sequence of
+ *     calls can be captured into a HIP graph and calls are thread-safe.
+ *   - Return 0 on success. A negative value (TSD_E_*) means the host-side
+ *     arguments were rejected and NOTHING was launched. A positive value is
+ *     the hipError_t of a failed launch.
+ *   - Paged pools are token-major and slot-addressed: token t of request b
+ *     lives at slot = page_table[b * pt_stride + t / 64] * 64 + t % 64.
+ *     page_size must be 64.
+ *   - Lengths and indices live in device memory, so kernels bound every
+ *     access themselves: a length is clamped to what the host arguments can
+ *     hold (pt_stride * 64 tokens, score_stride / max_len entries); page-table
+ *     entries at or past ceil(len / 64) are never read (stale tails are
+ *     fine); a page id outside [0, num_pages) or a selected index outside
+ *     [0, len) is skipped rather than dereferenced (that data is a caller
+ *     error and its contribution is dropped).
+ */
+#ifndef TSD_H
+#define TSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TSD_ABI_VERSION 1
+
+/* Element encodings. FP8 is OCP E4M3 "FN" (bias 7, max 448, no inf). */
+enum {
+  TSD_BF16 = 1,
+  TSD_FP16 = 2,
+  TSD_FP8_E4M3 = 3
+};
+
+/* Status codes (negative: rejected on the host, nothing launched). */
+enum {
+  TSD_OK = 0,
+  TSD_E_NULL = -1,        /* a required pointer is NULL                      */
+  TSD_E_DTYPE = -2,       /* unsupported or inconsistent element encoding    */
+  TSD_E_SHAPE = -3,       /* a size is negative, zero where it must not be,
+                             or exceeds a supported bound                    */
+  TSD_E_PAGE_SIZE = -4,   /* page_size != 64                                 */
+  TSD_E_GQA = -5,         /* H_q % H_kv != 0, or H_sel not in {1, H_kv}      */
+  TSD_E_K = -6,           /* top_k outside [1, 4096]                         */
+  TSD_E_CHUNKS = -7,      /* chunks outside [1, 64]                          */
+  TSD_E_WORKSPACE = -8,   /* workspace NULL or smaller than required         */
+  TSD_E_UNSUPPORTED = -9, /* a valid but unsupported configuration (D, r...) */
+  TSD_E_MODE = -10,       /* unknown score mode                              */
+  TSD_E_ABI = -11         /* args struct built for another ABI version       */
+};
+
+/* Supported bounds of this version. */
+#define TSD_HEAD_DIM 128    /* D of K/V and of the index keys                */
+#define TSD_MAX_INDEX_HEADS 16
+#define TSD_MAX_TOPK 4096
+#define TSD_MAX_CHUNKS 64
+#define TSD_MAX_GQA_GROUP 16
+#define TSD_PAGE_SIZE 64
+
+/* ------------------------------------------------------------------------
+ * sparse_index_score
+ *
+ * Mode TSD_SCORE_DS_LABEL (double sparsity). One row per (request b, KV
+ * head g), row = b * H_kv + g, n = seq_lens[b] keys:
+ *   scores[row][t] = sum_{j<r} qs[b,g,j] * label_pool[slot(b,t)][g][j],
+ *   qs[b,g,j]      = sum_{h = g*G .. g*G+G-1} q[b][h][channel_idx[g][j]],
+ * G = H_q / H_kv (the query of a GQA group is the sum of its heads).
+ *   q            [B, H_q, D]        bf16 or fp16 (q_dtype), D == 128
+ *   channel_idx  [H_kv, r]          int32, each in [0, D), 1 <= r <= 128
+ *   label_pool   [num_pages*64, H_kv, r]  same encoding as q
+ *
+ * Mode TSD_SCORE_QSA_INDEX (index keys). One row per query row i, request
+ * b = i / rows_per_req, rows = B * rows_per_req:
+ *   scores[i][t] = sum_{h<H_i} index_w[i][h] *
+ *                  max(0, sum_{d<D_i} index_q[i][h][d] * index_k[slot(b,t)][d])
+ * for t < n_i, n_i = seq_lens[b] (q_pos == NULL: decode rows) or
+ * min(q_pos[i] + 1, seq_lens[b]) (causal chunked-prefill rows; q_pos < 0
+ * gives 0 keys).
+ *   index_q      [rows, H_i, D_i]   FP8 E4M3 codes, H_i <= 16, D_i == 128
+ *   index_w      [rows, H_i]        f32
+ *   index_k_pool [num_pages*64, D_i] FP8 E4M3 codes (unit scale)
+ *   q_pos        [rows] int32 or NULL
+ *
+ * Output: scores f32 [rows, score_stride]. Exactly the entries t < n of
+ * every row are written -- also when n <= top_k -- and the tail of each row
+ * is left untouched. A key on an out-of-range page scores -inf.
+ * row_lens_out (optional, int32 [rows]) receives each row's n, the count
+ * topk_select takes as its row length.
+ * ------------------------------------------------------------------------ */
+enum { TSD_SCORE_DS_LABEL = 1, TSD_SCORE_QSA_INDEX = 2 };
+
+typedef struct tsd_score_args {
+  int32_t abi_version;           /* TSD_ABI_VERSION                          */
+  int32_t mode;                  /* TSD_SCORE_*                              */
+  /* batch view of the paged cache */
+  int32_t B;                     /* requests, >= 0                           */
+  int32_t page_size;             /* 64                                       */
+  const int32_t *page_table;     /* [B, pt_stride] physical page ids        */
+  int64_t pt_stride;             /* >= 1                                     */
+  const int32_t *seq_lens;       /* [B] cached tokens per request           */
+  int64_t num_pages;             /* pages in every pool                      */
+  /* double sparsity (mode DS_LABEL) */
+  const void *q;
+  int32_t q_dtype;               /* TSD_BF16 | TSD_FP16                      */
+  int32_t H_q;
+  int32_t H_kv;
+  int32_t D;
+  const int32_t *channel_idx;
+  int32_t r;
+  int32_t label_dtype;           /* == q_dtype                               */
+  const void *label_pool;
+  /* index keys (mode QSA_INDEX) */
+  const uint8_t *index_q;
+  const float *index_w;
+  const uint8_t *index_k_pool;
+  const int32_t *q_pos;          /* NULL for decode                          */
+  int32_t rows_per_req;          /* >= 1                                     */
+  int32_t H_i;
+  int32_t D_i;
+  int32_t reserved0;
+  /* output */
+  float *scores;
+  int64_t score_stride;          /* >= 1                                     */
+  int32_t *row_lens_out;         /* [rows] or NULL                           */
+} tsd_score_args;
+
+int sparse_index_score(const tsd_score_args *a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * topk_select
+ *
+ * For each row, n = clamp(row_lens[row], 0, min(max_len, stride)) and
+ * m = min(k, n): idx[row][0 .. m) are the indices of the m largest of
+ * scores[row][0 .. n), in strictly ascending order; among equal scores the
+ * lower index is taken. idx[row][m .. k) = -1; count[row] = m (count may be
+ * NULL). Scores compare as floats: -0 and +0 are equal; +-inf are allowed;
+ * NaN is outside the contract.
+ *   scores   [rows, stride] f32          row_lens [rows] int32
+ *   idx      [rows, k] int32             count    [rows] int32 or NULL
+ *   max_len  host-side bound on every row length (sizes the launch)
+ *   ws       device workspace of at least topk_select_workspace_bytes()
+ *            bytes, caller-owned; its contents need no initialisation and
+ *            are scratch after the call (one workspace per concurrent call)
+ * 1 <= k <= 4096; rows >= 0; stride >= max_len >= 0.
+ * ------------------------------------------------------------------------ */
+size_t topk_select_workspace_bytes(int rows, int max_len, int k);
+
+int topk_select(const float *scores, int64_t stride, int rows,
+                const int32_t *row_lens, int max_len, int k, int32_t *idx,
+                int32_t *count, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sparse_gqa_decode
+ *
+ * For request b, query head h, KV head g = h / G (G = H_q / H_kv) and chunk
+ * c < chunks of the selection sel = idx[b][s][0 .. m), s = 0 if H_sel == 1
+ * (one list shared by all KV heads) else g, m = clamp(count[b][s], 0, k):
+ *   tokens  sel[floor(c*m/C) .. floor((c+1)*m/C))   (C = chunks)
+ *   z_t     = softmax_scale * sum_d q[b][h][d] * Khat[slot(b,t)][g][d]
+ *   lse_part[b][h][c]  = log sum_t exp(z_t)                  (natural log)
+ *   o_part[b][h][c][:] = sum_t exp(z_t - lse) * Vhat[slot(b,t)][g][:]
+ * Khat/Vhat = the stored value (bf16/fp16), or the FP8 code times
+ * k_scale / v_scale of the token's physical page. An empty chunk (or a
+ * request with no selection) writes o = 0 and lse = -inf. Only pages below
+ * ceil(len / 64) are read.
+ *   q        [B, H_q, D] bf16 or fp16, D == 128
+ *   k_pool   [num_pages*64, H_kv, D]   bf16 | fp16 | fp8 (kv_dtype)
+ *   v_pool   same as k_pool
+ *   k_scale, v_scale [num_pages] f32 (FP8 only; NULL otherwise)
+ *   idx      [B, H_sel, k] int32 ascending, -1 padded   count [B, H_sel]
+ *   o_part   [B, H_q, chunks, D] f32     lse_part [B, H_q, chunks] f32
+ * For a 16-bit cache q must have the cache's encoding; an FP8 cache takes
+ * bf16 or fp16 queries. H_q % H_kv == 0, G <= 16, 1 <= chunks <= 64,
+ * 1 <= k <= 4096.
+ * ------------------------------------------------------------------------ */
+typedef struct tsd_attn_args {
+  int32_t abi_version;           /* TSD_ABI_VERSION                          */
+  int32_t B;
+  int32_t H_q;
+  int32_t H_kv;
+  int32_t D;
+  int32_t q_dtype;
+  const void *q;
+  const void *k_pool;
+  const void *v_pool;
+  int32_t kv_dtype;
+  int32_t page_size;             /* 64                                       */
+  const float *k_scale;
+  const float *v_scale;
+  const int32_t *page_table;
+  int64_t pt_stride;
+  const int32_t *seq_lens;
+  int64_t num_pages;
+  const int32_t *idx;
+  const int32_t *count;
+  int32_t H_sel;                 /* 1 or H_kv                                */
+  int32_t k;
+  int32_t chunks;
+  float softmax_scale;           /* usually 1/sqrt(D)                        */
+  float *o_part;
+  float *lse_part;
+} tsd_attn_args;
+
+int sparse_gqa_decode(const tsd_attn_args *a, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * lse_merge
+ *
+ * For each of rows partial sets (rows = B * H_q) with C chunks:
+ *   M = max_c lse_part[row][c],  W = sum_c exp(lse_part[row][c] - M)
+ *   out[row][:] = sum_c exp(lse_part[row][c] - M) * o_part[row][c][:] / W
+ *   out_lse[row] = M + log W
+ * All chunks empty (every lse = -inf): out = 0, out_lse = -inf.
+ *   o_part [rows, C, D] f32   lse_part [rows, C] f32
+ *   out    [rows, D] f32      out_lse  [rows] f32 or NULL
+ * 1 <= C <= 64, 1 <= D <= 512, D % 4 == 0.
+ * ------------------------------------------------------------------------ */
+int lse_merge(const float *o_part, const float *lse_part, int rows, int C,
+              int D, float *out, float *out_lse, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, host only). */
+const char *tsd_strerror(int status);
+
+/* TSD_ABI_VERSION of the built library. */
+int tsd_abi_version(void);
+
+/* sizeof the two argument structs as compiled into the library, so a
+ * binding can check its own layout. */
+size_t tsd_sizeof_score_args(void);
+size_t tsd_sizeof_attn_args(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TSD_H */

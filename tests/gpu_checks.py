@@ -1,0 +1,139 @@
+"""Comparisons of the HIP path against the CPU oracle, shared by the GPU
+tests, the smoke check and the benchmark's spot checks.
+
+Tolerances (max absolute error, FP32 accumulation on both sides):
+  scores:  2e-3 for double-sparsity labels in BF16/FP16, 2e-2 for FP8 index
+           keys;
+  outputs and LSEs: 2e-3 for a BF16/FP16 cache, 2e-2 for an FP8 cache;
+  top-k:   identical index arrays when both sides see the same f32 scores;
+           end to end, the selected sets may differ only among tokens whose
+           oracle score lies within 1e-5 * max(1, |s_k|) of the k-th score
+           s_k, and the set sizes must agree.
+Where the two selections differ, attention is compared with the oracle run
+on the GPU's own selection, so the numerics of the gather and the softmax
+are always checked element by element.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+TIE_WINDOW = 1e-5
+
+
+def score_tol(mode):
+    return 2e-3 if mode == "ds" else 2e-2
+
+
+def out_tol(kv_enc):
+    return 2e-2 if kv_enc == "fp8_e4m3" else 2e-3
+
+
+def oracle_scores(h):
+    if h["mode"] == "ds":
+        return oracle.ds_scores(h["q"], h["q_enc"], h["channel_idx"],
+                                h["label_pool"], h["kv_enc"], h["page_table"],
+                                h["seq_lens"], h["num_pages"])
+    return oracle.qsa_scores(h["index_q"], h["index_w"], h["index_k"],
+                             h["page_table"], h["seq_lens"], h["num_pages"],
+                             rows_per_req=h.get("rows_per_req", 1),
+                             q_pos=h.get("q_pos"))
+
+
+def oracle_row_lens(h):
+    lens = h["seq_lens"].astype(np.int64)
+    if h["mode"] == "ds":
+        return np.repeat(lens, h["channel_idx"].shape[0])
+    R = h.get("rows_per_req", 1)
+    rl = np.repeat(lens, R)
+    if h.get("q_pos") is not None:
+        rl = np.minimum(rl, np.maximum(h["q_pos"].astype(np.int64) + 1, 0))
+    return rl
+
+
+def check_scores(gpu, ref64, row_lens, tol, rows=None):
+    """Entries t < n agree within tol; the rest of each row is untouched
+    (the GPU buffer was pre-filled with NaN)."""
+    rows = range(gpu.shape[0]) if rows is None else rows
+    worst = 0.0
+    for r in rows:
+        n = int(row_lens[r])
+        g = gpu[r, :n].astype(np.float64)
+        assert np.isfinite(g).all(), f"row {r}: non-finite score"
+        err = np.abs(g - ref64[r, :n]).max() if n else 0.0
+        worst = max(worst, err)
+        assert err <= tol, f"row {r}: score error {err}"
+        assert np.isnan(gpu[r, n:]).all(), f"row {r}: tail written"
+    return worst
+
+
+def check_topk_identical(scores32, row_lens, k, gpu_idx, gpu_count, rows=None):
+    """Same f32 scores in -> identical arrays out."""
+    rows = np.arange(scores32.shape[0]) if rows is None else np.asarray(rows)
+    ref_idx, ref_cnt = oracle.topk(scores32[rows], row_lens[rows], k)
+    np.testing.assert_array_equal(gpu_count[rows], ref_cnt)
+    np.testing.assert_array_equal(gpu_idx[rows], ref_idx)
+
+
+def check_sets_within_window(gpu_idx, gpu_cnt, ref_idx, ref_cnt, ref_s32,
+                             row_lens, k, rows=None):
+    """End-to-end selections: equal sizes, differences only at near-ties.
+    Returns the number of rows whose sets differ."""
+    rows = range(gpu_idx.shape[0]) if rows is None else rows
+    differing = 0
+    for r in rows:
+        n = int(row_lens[r])
+        assert gpu_cnt[r] == ref_cnt[r] == min(k, n)
+        m = int(ref_cnt[r])
+        a = set(gpu_idx[r, :m].tolist())
+        b = set(ref_idx[r, :m].tolist())
+        assert (gpu_idx[r, m:] == -1).all()
+        assert (np.diff(gpu_idx[r, :m]) > 0).all()
+        diff = a ^ b
+        if diff:
+            differing += 1
+            s = ref_s32[r, :n].astype(np.float64)
+            sk = np.sort(s)[::-1][m - 1]
+            window = TIE_WINDOW * max(1.0, abs(sk))
+            for t in diff:
+                assert abs(s[t] - sk) <= window, (r, t, s[t], sk)
+    return differing
+
+
+def check_attention_on(h, idx3, cnt2, chunks, o_part, lse_part, tol,
+                       batch=None):
+    """Oracle attention on the GPU's selection vs the GPU partials."""
+    bsel = np.arange(h["q"].shape[0]) if batch is None else np.asarray(batch)
+    sub = dict(h)
+    sub["q"] = h["q"][bsel]
+    sub["page_table"] = h["page_table"][bsel]
+    sub["seq_lens"] = h["seq_lens"][bsel]
+    ro, rl = oracle.sparse_attention(
+        sub["q"], h["q_enc"], h["k_pool"], h["v_pool"], h["kv_enc"],
+        h.get("k_scale"), h.get("v_scale"), sub["page_table"], sub["seq_lens"],
+        h["num_pages"], idx3[bsel], cnt2[bsel], chunks)
+    go = o_part[bsel].astype(np.float64)
+    gl = lse_part[bsel].astype(np.float64)
+    assert (np.isneginf(gl) == np.isneginf(rl)).all(), "empty chunks differ"
+    fin = np.isfinite(rl)
+    err_o = np.abs(go - ro).max()
+    err_l = np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0
+    assert err_o <= tol, f"o_part error {err_o}"
+    assert err_l <= tol, f"lse_part error {err_l}"
+    return ro, rl, max(err_o, err_l)
+
+
+def check_merge(o_part, lse_part, out, out_lse, tol=1e-5):
+    """GPU merge vs oracle merge of the GPU's own partials."""
+    C, D = o_part.shape[-2], o_part.shape[-1]
+    ro, rl = oracle.lse_merge(o_part.reshape(-1, C, D).astype(np.float64),
+                              lse_part.reshape(-1, C).astype(np.float64))
+    go = out.reshape(-1, D).astype(np.float64)
+    gl = out_lse.reshape(-1).astype(np.float64)
+    assert (np.isneginf(gl) == np.isneginf(rl)).all()
+    fin = np.isfinite(rl)
+    err = max(np.abs(go - ro).max(),
+              np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0)
+    assert err <= tol, f"merge error {err}"
+    return err

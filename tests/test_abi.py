@@ -1,0 +1,174 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before launching anything. No call here
+reaches a kernel, so the file runs without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_decode_amd as tsd
+from top_sparse_decode_amd import AttnArgs, ScoreArgs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsd.h")
+LIB = tsd._lib
+
+E = dict(OK=0, NULL=-1, DTYPE=-2, SHAPE=-3, PAGE_SIZE=-4, GQA=-5, K=-6,
+         CHUNKS=-7, WORKSPACE=-8, UNSUPPORTED=-9, MODE=-10, ABI=-11)
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)) - {"if"})
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert {"sparse_index_score", "topk_select", "sparse_gqa_decode",
+            "lse_merge", "topk_select_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(LIB, n), n
+        assert n in tsd.EXPORTS
+
+
+def test_abi_version_and_struct_layout():
+    assert LIB.tsd_abi_version() == 1
+    assert LIB.tsd_sizeof_score_args() == ctypes.sizeof(ScoreArgs)
+    assert LIB.tsd_sizeof_attn_args() == ctypes.sizeof(AttnArgs)
+
+
+def test_strerror_names_every_code():
+    for code in E.values():
+        assert LIB.tsd_strerror(code)
+    assert b"HIP" in LIB.tsd_strerror(3)
+
+
+def _score(**kw):
+    a = ScoreArgs()
+    a.abi_version, a.mode, a.B, a.page_size = 1, 2, 2, 64
+    a.page_table, a.pt_stride, a.seq_lens, a.num_pages = FAKE, 4, FAKE, 8
+    a.index_q, a.index_w, a.index_k_pool = FAKE, FAKE, FAKE
+    a.rows_per_req, a.H_i, a.D_i = 1, 16, 128
+    a.q, a.q_dtype, a.H_q, a.H_kv, a.D = FAKE, 1, 32, 8, 128
+    a.channel_idx, a.r, a.label_dtype, a.label_pool = FAKE, 16, 1, FAKE
+    a.scores, a.score_stride = FAKE, 256
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return LIB.sparse_index_score(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(abi_version=2), "ABI"),
+    (dict(mode=7), "MODE"),
+    (dict(page_size=32), "PAGE_SIZE"),
+    (dict(B=-1), "SHAPE"),
+    (dict(pt_stride=0), "SHAPE"),
+    (dict(score_stride=0), "SHAPE"),
+    (dict(scores=None), "NULL"),
+    (dict(page_table=None), "NULL"),
+    (dict(index_k_pool=None), "NULL"),
+    (dict(H_i=17), "UNSUPPORTED"),
+    (dict(D_i=64), "UNSUPPORTED"),
+    (dict(rows_per_req=0), "SHAPE"),
+    (dict(mode=1, H_q=30), "GQA"),
+    (dict(mode=1, label_dtype=2), "DTYPE"),
+    (dict(mode=1, q_dtype=3, label_dtype=3), "DTYPE"),
+    (dict(mode=1, D=64), "UNSUPPORTED"),
+    (dict(mode=1, r=0), "SHAPE"),
+    (dict(mode=1, channel_idx=None), "NULL"),
+    (dict(mode=1, H_kv=8, r=1024), "UNSUPPORTED"),
+])
+def test_score_rejections(kw, code):
+    assert _score(**kw) == E[code]
+
+
+def test_score_null_args_and_empty_batch():
+    assert LIB.sparse_index_score(None, None) == E["NULL"]
+    # an empty batch is valid and launches nothing
+    assert _score(B=0, scores=None, page_table=None, seq_lens=None) == 0
+
+
+def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, **kw):
+    need = LIB.topk_select_workspace_bytes(rows, max_len, k)
+    args = dict(scores=FAKE, row_lens=FAKE, idx=FAKE, ws=FAKE)
+    args.update(kw)
+    return LIB.topk_select(args["scores"], stride, rows, args["row_lens"],
+                           max_len, k, args["idx"], None, args["ws"],
+                           need if ws_bytes is None else ws_bytes, None)
+
+
+def test_topk_rejections():
+    assert _topk(k=0) == E["K"]
+    assert _topk(k=4097) == E["K"]
+    assert _topk(max_len=200, stride=128) == E["SHAPE"]
+    assert _topk(rows=-1) == E["SHAPE"]
+    assert _topk(ws_bytes=16) == E["WORKSPACE"]
+    assert _topk(ws=None) == E["WORKSPACE"]
+    assert _topk(scores=None) == E["NULL"]
+    assert _topk(rows=70000) == E["UNSUPPORTED"]
+    assert _topk(rows=0, scores=None, row_lens=None, idx=None, ws=None) == 0
+
+
+def test_topk_workspace_size():
+    # 5120 histogram words per row plus two counters per 1024-element slice
+    assert tsd.topk_select_workspace_bytes(8, 262144, 2048) == 8 * (5120 + 512) * 4
+    assert tsd.topk_select_workspace_bytes(1, 1, 1) == (5120 + 2) * 4
+    assert tsd.topk_select_workspace_bytes(0, 100, 5) == 0
+
+
+def _attn(**kw):
+    a = AttnArgs()
+    a.abi_version, a.B, a.H_q, a.H_kv, a.D = 1, 2, 32, 4, 128
+    a.q_dtype, a.q, a.k_pool, a.v_pool = 1, FAKE, FAKE, FAKE
+    a.kv_dtype, a.page_size, a.k_scale, a.v_scale = 3, 64, FAKE, FAKE
+    a.page_table, a.pt_stride, a.seq_lens, a.num_pages = FAKE, 4, FAKE, 8
+    a.idx, a.count, a.H_sel, a.k, a.chunks = FAKE, FAKE, 1, 64, 4
+    a.softmax_scale, a.o_part, a.lse_part = 0.088, FAKE, FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return LIB.sparse_gqa_decode(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(abi_version=0), "ABI"),
+    (dict(H_q=30), "GQA"),
+    (dict(H_sel=2), "GQA"),
+    (dict(H_q=68, H_kv=4), "UNSUPPORTED"),
+    (dict(D=64), "UNSUPPORTED"),
+    (dict(k=0), "K"),
+    (dict(chunks=0), "CHUNKS"),
+    (dict(chunks=65), "CHUNKS"),
+    (dict(kv_dtype=9), "DTYPE"),
+    (dict(q_dtype=3), "DTYPE"),
+    (dict(kv_dtype=2, q_dtype=1), "DTYPE"),
+    (dict(k_scale=None), "NULL"),
+    (dict(idx=None), "NULL"),
+    (dict(page_size=128), "PAGE_SIZE"),
+])
+def test_attn_rejections(kw, code):
+    assert _attn(**kw) == E[code]
+
+
+def test_attn_empty_batch_and_null():
+    assert LIB.sparse_gqa_decode(None, None) == E["NULL"]
+    assert _attn(B=0, q=None, idx=None, page_table=None, seq_lens=None) == 0
+
+
+def test_merge_rejections():
+    m = LIB.lse_merge
+    assert m(FAKE, FAKE, 4, 0, 128, FAKE, None, None) == E["CHUNKS"]
+    assert m(FAKE, FAKE, 4, 65, 128, FAKE, None, None) == E["CHUNKS"]
+    assert m(FAKE, FAKE, -1, 4, 128, FAKE, None, None) == E["SHAPE"]
+    assert m(FAKE, FAKE, 4, 4, 1024, FAKE, None, None) == E["UNSUPPORTED"]
+    assert m(None, FAKE, 4, 4, 128, FAKE, None, None) == E["NULL"]
+    assert m(None, None, 0, 4, 128, None, None, None) == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        tsd.lse_merge(torch.zeros(2, 3, 8), torch.zeros(2, 3), torch.zeros(2, 8))

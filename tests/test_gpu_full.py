@@ -1,0 +1,197 @@
+"""GPU parity at the workloads' full sizes, in the configuration the
+benchmark times. The oracle checks whole rows it can finish in seconds
+(selected requests / query rows: scores, identical top-k, selection window,
+attention on the GPU's selection) and sampled score points on every other
+row; the merge is checked on every row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tsd_synth
+from gpu_checks import (check_attention_on, check_merge, check_scores,
+                        check_sets_within_window, check_topk_identical,
+                        oracle_row_lens, out_tol, score_tol)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import top_sparse_decode_amd  # noqa: F401
+
+
+def _step():
+    import top_sparse_decode_amd.step as step
+    return step
+
+
+def _oracle_rows(h, rows):
+    """Oracle f64 scores of the listed rows only, [len(rows), stride]."""
+    rows = list(rows)
+    if h["mode"] == "ds":
+        H_kv = h["channel_idx"].shape[0]
+        out = []
+        for r in rows:
+            b, g = divmod(r, H_kv)
+            s = oracle.ds_scores(h["q"][b:b + 1], h["q_enc"],
+                                 h["channel_idx"], h["label_pool"],
+                                 h["kv_enc"], h["page_table"][b:b + 1],
+                                 h["seq_lens"][b:b + 1], h["num_pages"])
+            out.append(s[g])
+        return np.stack(out)
+    R = h.get("rows_per_req", 1)
+    out = []
+    for r in rows:
+        b = r // R
+        qp = None if h.get("q_pos") is None else h["q_pos"][r:r + 1]
+        s = oracle.qsa_scores(h["index_q"][r:r + 1], h["index_w"][r:r + 1],
+                              h["index_k"], h["page_table"][b:b + 1],
+                              h["seq_lens"][b:b + 1], h["num_pages"],
+                              rows_per_req=1, q_pos=qp)
+        out.append(s[0])
+    return np.stack(out)
+
+
+def _sampled_points(h, gs, rl, tol, per_row=64, seed=0):
+    rng = np.random.default_rng(seed)
+    rows, ts = [], []
+    for r in range(gs.shape[0]):
+        n = int(rl[r])
+        if n == 0:
+            continue
+        t = rng.integers(0, n, size=per_row)
+        t[0], t[-1] = 0, n - 1
+        rows.extend([r] * per_row)
+        ts.extend(t.tolist())
+    rows, ts = np.array(rows), np.array(ts)
+    if h["mode"] == "ds":
+        ref = oracle.ds_score_points(h["q"], h["q_enc"], h["channel_idx"],
+                                     h["label_pool"], h["kv_enc"],
+                                     h["page_table"], h["seq_lens"],
+                                     h["num_pages"], rows, ts)
+    else:
+        ref = oracle.qsa_score_points(h["index_q"], h["index_w"], h["index_k"],
+                                      h["page_table"], h["seq_lens"],
+                                      h["num_pages"], rows, ts,
+                                      rows_per_req=h.get("rows_per_req", 1),
+                                      q_pos=h.get("q_pos"))
+    err = np.abs(gs[rows, ts].astype(np.float64) - ref).max()
+    assert err <= tol, err
+
+
+def _check_layer(wl, bufs, full_rows, check_batches=None):
+    h = tsd_synth.to_host(wl)
+    B, k, C = wl["B"], wl["top_k"], wl["chunks"]
+    rl = oracle_row_lens(h)
+    np.testing.assert_array_equal(bufs.row_lens.cpu().numpy(), rl)
+    gs = bufs.scores.cpu().numpy()
+    gidx, gcnt = bufs.idx.cpu().numpy(), bufs.count.cpu().numpy()
+    tol = score_tol(wl["mode"])
+    _sampled_points(h, gs, rl, tol)
+    # whole rows
+    ref64 = _oracle_rows(h, full_rows)
+    check_scores(gs[full_rows], ref64, rl[full_rows], tol)
+    check_topk_identical(gs, rl, k, gidx, gcnt, rows=full_rows)
+    ref32 = ref64.astype(np.float32)
+    ridx, rcnt = oracle.topk(ref32, rl[full_rows], k)
+    check_sets_within_window(gidx[full_rows], gcnt[full_rows], ridx, rcnt,
+                             ref32, rl[full_rows], k)
+    op, lp = bufs.o_part.cpu().numpy(), bufs.lse_part.cpu().numpy()
+    if check_batches is None:
+        check_batches = range(B)
+    check_attention_on(h, gidx.reshape(B, bufs.H_sel, k),
+                       gcnt.reshape(B, bufs.H_sel), C, op, lp,
+                       out_tol(wl["kv_enc"]), batch=list(check_batches))
+    check_merge(op, lp, bufs.out.cpu().numpy(), bufs.out_lse.cpu().numpy())
+
+
+def _run(wl):
+    step = _step()
+    bufs = step.StepBuffers(wl)
+    bufs.scores.fill_(float("nan"))
+    step.decode_step(wl, bufs)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def test_full_ds_tiny_b1_l4096():
+    wl = tsd_synth.make("ds_tiny_b1_l4096", DEV)
+    bufs = _run(wl)
+    _check_layer(wl, bufs, full_rows=[0])
+
+
+def test_full_ds_llama31_8b_b3_l60000():
+    wl = tsd_synth.make("ds_llama31_8b_b3_l60000", DEV)
+    bufs = _run(wl)
+    _check_layer(wl, bufs, full_rows=list(range(24)))
+
+
+def test_full_ds_llama7b_b3_l20000_200_steps():
+    """200 decode steps, each appending one token per request: lengths run
+    20,001 .. 20,200 with a fresh query per step; steps 0, 1, 99 and 199 are
+    checked against the oracle."""
+    step = _step()
+    wl = tsd_synth.make("ds_llama7b_b3_l20000_s200", DEV)
+    bufs = step.StepBuffers(wl)
+    base = wl["seq_lens"].clone()
+    checked = {0, 1, 99, 199}
+    for s in range(200):
+        wl["seq_lens"] = base + s
+        wl["q"] = wl["step_q"][s].contiguous()
+        bufs.scores.fill_(float("nan"))
+        step.decode_step(wl, bufs)
+        if s in checked:
+            torch.cuda.synchronize()
+            print(f"step {s} len {int(wl['seq_lens'][0])}", flush=True)
+            _check_layer(wl, bufs, full_rows=[0, 31, 32, 95])
+    torch.cuda.synchronize()
+
+
+def test_full_qsa_decode_b8_l262144():
+    wl = tsd_synth.make("qsa_decode_b8_l262144_k2048", DEV)
+    bufs = _run(wl)
+    _check_layer(wl, bufs, full_rows=[0, 7])
+
+
+def test_full_qsa_decode_b1_l1048576():
+    wl = tsd_synth.make("qsa_decode_b1_l1048576_k2048", DEV)
+    bufs = _run(wl)
+    _check_layer(wl, bufs, full_rows=[0])
+
+
+def test_full_qsa_prefill_r2048_l1048576():
+    """Chunked-prefill indexer pass: 2,048 causal query rows against all
+    1,048,576 index keys, then per-row top-k. Rows 0, 1023 and 2047 are
+    checked whole; every row is sampled."""
+    step = _step()
+    wl = tsd_synth.make("qsa_prefill_r2048_l1048576_k2048", DEV)
+    bufs = step.StepBuffers(wl)
+    bufs.scores.fill_(float("nan"))
+    step.score(wl, bufs)
+    step.select(wl, bufs)
+    torch.cuda.synchronize()
+    h = tsd_synth.to_host(wl)
+    rl = oracle_row_lens(h)
+    np.testing.assert_array_equal(bufs.row_lens.cpu().numpy(), rl)
+    rows = [0, 1023, 2047]
+    gs_rows = bufs.scores[rows].cpu().numpy()
+    ref64 = _oracle_rows(h, rows)
+    check_scores(gs_rows, ref64, rl[rows], score_tol("qsa"))
+    gidx, gcnt = bufs.idx.cpu().numpy(), bufs.count.cpu().numpy()
+    ridx, rcnt = oracle.topk(gs_rows, rl[rows], 2048)
+    np.testing.assert_array_equal(gidx[rows], ridx)
+    np.testing.assert_array_equal(gcnt[rows], rcnt)
+    # sampled points on all rows (the score buffer is copied in slices)
+    rng = np.random.default_rng(1)
+    sample_rows = np.sort(rng.choice(2048, size=64, replace=False))
+    ts = np.array([rng.integers(0, rl[r]) for r in sample_rows])
+    got = bufs.scores[torch.from_numpy(sample_rows).to(DEV),
+                      torch.from_numpy(ts).to(DEV)].cpu().numpy()
+    ref = oracle.qsa_score_points(h["index_q"], h["index_w"], h["index_k"],
+                                  h["page_table"], h["seq_lens"],
+                                  h["num_pages"], sample_rows, ts,
+                                  rows_per_req=2048, q_pos=h["q_pos"])
+    assert np.abs(got - ref).max() <= score_tol("qsa")

@@ -1,0 +1,255 @@
+"""GPU parity of every step of the path against the CPU oracle, through the
+C ABI (via the thin binding), at sizes the oracle finishes in seconds: several
+pages and tiles, ragged tails, empty requests, stale page-table tails,
+partial index-head sets, causal prefill rows, ties and special values."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tsd_synth
+from gpu_checks import (check_attention_on, check_merge, check_scores,
+                        check_sets_within_window, check_topk_identical,
+                        oracle_row_lens, oracle_scores, out_tol, score_tol)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import top_sparse_decode_amd  # noqa: F401  fails loudly without the library
+
+
+def _step():
+    import top_sparse_decode_amd.step as step
+    return step
+
+
+def _run(wl):
+    step = _step()
+    bufs = step.StepBuffers(wl)
+    bufs.scores.fill_(float("nan"))
+    step.decode_step(wl, bufs)
+    torch.cuda.synchronize()
+    return bufs
+
+
+def _full_check(cfg, **over):
+    print(f"case {cfg.name} B={cfg.B} lens={cfg.lens} k={cfg.top_k} "
+          f"C={cfg.chunks} {cfg.kv_enc}", flush=True)
+    wl = tsd_synth.make(cfg, DEV)
+    wl.update(over)
+    bufs = _run(wl)
+    h = tsd_synth.to_host(wl)
+    B, k, C = wl["B"], wl["top_k"], wl["chunks"]
+    rl = oracle_row_lens(h)
+    np.testing.assert_array_equal(bufs.row_lens.cpu().numpy(), rl)
+    gs = bufs.scores.cpu().numpy()
+    ref64 = oracle_scores(h)
+    check_scores(gs, ref64, rl, score_tol(wl["mode"]))
+    gidx, gcnt = bufs.idx.cpu().numpy(), bufs.count.cpu().numpy()
+    check_topk_identical(gs, rl, k, gidx, gcnt)
+    ref32 = ref64.astype(np.float32)
+    ridx, rcnt = oracle.topk(np.nan_to_num(ref32, nan=0.0), rl, k)
+    check_sets_within_window(gidx, gcnt, ridx, rcnt, ref32, rl, k)
+    H_sel = bufs.H_sel
+    op, lp = bufs.o_part.cpu().numpy(), bufs.lse_part.cpu().numpy()
+    check_attention_on(h, gidx.reshape(B, H_sel, k), gcnt.reshape(B, H_sel), C,
+                       op, lp, out_tol(wl["kv_enc"]))
+    check_merge(op, lp, bufs.out.cpu().numpy(), bufs.out_lse.cpu().numpy())
+    if (gidx == ridx).all():
+        ref = oracle.decode_step(h)
+        err = np.abs(bufs.out.cpu().numpy() - ref["out"]).max()
+        assert err <= out_tol(wl["kv_enc"]), err
+    return wl, bufs
+
+
+QSA = "qsa_decode_b8_l262144_k2048"
+DS8B = "ds_llama31_8b_b3_l60000"
+DS7B = "ds_llama7b_b3_l20000_s200"
+
+
+@pytest.mark.parametrize("lens,k,C", [
+    ((5000, 4097, 63), 256, 5),
+    ((1000, 0, 130), 300, 3),
+    ((64, 65, 128), 64, 1),
+    ((2048, 700), 2048, 16),
+])
+def test_qsa_decode_path(lens, k, C):
+    cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=k, chunks=C,
+                           seed=101)
+    _full_check(cfg)
+
+
+def test_qsa_stale_page_table_tail():
+    cfg = tsd_synth.config(QSA, B=2, lens=(700, 129), top_k=100, chunks=4,
+                           stale_tail=True, seed=102)
+    _full_check(cfg)
+
+
+def test_qsa_partial_index_heads():
+    cfg = tsd_synth.config(QSA, B=2, lens=(900, 333), top_k=128, chunks=2,
+                           H_i=5, seed=103)
+    _full_check(cfg)
+
+
+def test_qsa_causal_prefill_rows():
+    cfg = tsd_synth.config(QSA, B=1, lens=(1500,), top_k=200, chunks=4,
+                           seed=104)
+    wl = tsd_synth.make(cfg, DEV)
+    R = 6
+    qpos = torch.tensor([0, 63, 64, 199, 1000, 1499], dtype=torch.int32,
+                        device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    iq = tsd_synth.fp8_codes(torch.randn((R, 16, 128), generator=g, device=DEV))
+    iw = torch.rand((R, 16), generator=g, device=DEV)
+    wl.update(index_q=iq, index_w=iw, rows_per_req=R, q_pos=qpos)
+    step = _step()
+    bufs = step.StepBuffers(wl)
+    bufs.scores.fill_(float("nan"))
+    step.score(wl, bufs)
+    step.select(wl, bufs)
+    torch.cuda.synchronize()
+    h = tsd_synth.to_host(wl)
+    rl = oracle_row_lens(h)
+    np.testing.assert_array_equal(bufs.row_lens.cpu().numpy(), rl)
+    gs = bufs.scores.cpu().numpy()
+    check_scores(gs, oracle_scores(h), rl, score_tol("qsa"))
+    check_topk_identical(gs, rl, 200, bufs.idx.cpu().numpy(),
+                         bufs.count.cpu().numpy())
+
+
+@pytest.mark.parametrize("name,over", [
+    (DS8B, dict(B=2, lens=(3000, 700), top_k=200, chunks=3)),
+    (DS7B, dict(B=3, H_q=6, H_kv=6, lens=(1500, 64, 65), top_k=100, chunks=4,
+                steps=0)),
+    (DS8B, dict(B=2, lens=(777, 300), r=12, n_outlier=12, top_k=64, chunks=2)),
+    ("ds_tiny_b1_l4096", dict(lens=(4096,))),
+])
+def test_ds_decode_path(name, over):
+    cfg = tsd_synth.config(name, seed=111, **over)
+    _full_check(cfg)
+
+
+def test_ds_stale_tail_and_empty_request():
+    cfg = tsd_synth.config(DS8B, B=3, lens=(0, 1000, 65), top_k=128, chunks=3,
+                           stale_tail=True, seed=112)
+    _full_check(cfg)
+
+
+# --------------------------------------------------------------- top-k only
+def _topk_gpu(scores_np, lens, k, max_len=None):
+    import top_sparse_decode_amd as tsd
+    rows, stride = scores_np.shape
+    max_len = stride if max_len is None else max_len
+    s = torch.from_numpy(scores_np).to(DEV)
+    rl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(rows, max_len, k),
+                     dtype=torch.uint8, device=DEV)
+    tsd.topk_select(s, rl, k, max_len, idx, cnt, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def test_topk_special_rows_bit_exact():
+    rng = np.random.default_rng(5)
+    stride, k = 10000, 300
+    rows = []
+    lens = [0, 1, 299, 300, 301, 10000, 10000, 10000, 10000, 9999, 5000]
+    s = rng.normal(size=(len(lens), stride)).astype(np.float32)
+    s[5] = 3.25                                  # all equal
+    s[6] = rng.choice([-0.0, 0.0], size=stride)  # signed zeros only
+    s[7, ::7] = np.inf
+    s[7, 1::7] = -np.inf
+    s[8] = rng.integers(0, 4, size=stride).astype(np.float32)  # heavy ties
+    s[9] = -np.abs(s[9])                         # all negative
+    s[10, :5000] = np.linspace(1, 0, 5000)       # strictly decreasing
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+    assert (gidx[5, :300] == np.arange(300)).all()
+    assert (gidx[0] == -1).all() and gcnt[0] == 0
+
+
+@pytest.mark.parametrize("n,k,levels", [(50000, 3000, 3), (262144, 2048, 50),
+                                        (70000, 4096, 1_000_000)])
+def test_topk_large_rows_with_ties(n, k, levels):
+    rng = np.random.default_rng(n)
+    s = (rng.integers(0, levels, size=(3, n)) / levels).astype(np.float32)
+    lens = [n, n - 1, n // 3]
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+
+
+def test_topk_row_lens_clamped_to_max_len():
+    rng = np.random.default_rng(9)
+    s = rng.normal(size=(2, 5000)).astype(np.float32)
+    gidx, gcnt = _topk_gpu(s, [100000, -5], 50, max_len=4000)
+    ridx, rcnt = oracle.topk(s, [4000, 0], 50)
+    np.testing.assert_array_equal(gidx, ridx)
+    np.testing.assert_array_equal(gcnt, rcnt)
+
+
+# ----------------------------------------------------------- merge and misc
+def test_lse_merge_random_partials():
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(3)
+    rows, C, D = 70, 64, 128
+    o = rng.normal(size=(rows, C, D)).astype(np.float32)
+    lse = (rng.normal(size=(rows, C)) * 5).astype(np.float32)
+    lse[rng.random((rows, C)) < 0.3] = -np.inf
+    lse[3] = -np.inf
+    og = torch.from_numpy(o).to(DEV)
+    lg = torch.from_numpy(lse).to(DEV)
+    out = torch.empty((rows, D), device=DEV)
+    out_lse = torch.empty(rows, device=DEV)
+    tsd.lse_merge(og, lg, out, out_lse)
+    torch.cuda.synchronize()
+    check_merge(o, lse, out.cpu().numpy(), out_lse.cpu().numpy())
+    assert (out[3] == 0).all() and torch.isneginf(out_lse[3])
+
+
+def test_all_equal_scores_pick_lowest_indices():
+    cfg = tsd_synth.config(QSA, B=2, lens=(3000, 200), top_k=256, chunks=4,
+                           seed=120)
+    wl = tsd_synth.make(cfg, DEV)
+    wl["index_k"][:] = wl["index_k"][0]
+    bufs = _run(wl)
+    idx = bufs.idx.cpu().numpy()
+    assert (idx[0] == np.arange(256)).all()
+    assert (idx[1, :200] == np.arange(200)).all() and (idx[1, 200:] == -1).all()
+
+
+def test_runs_are_bitwise_repeatable():
+    cfg = tsd_synth.config(QSA, B=3, lens=(9000, 4097, 130), top_k=512,
+                           chunks=8, seed=121)
+    wl = tsd_synth.make(cfg, DEV)
+    a = _run(wl)
+    outs = [a.out.clone(), a.out_lse.clone(), a.idx.clone(), a.scores.clone()]
+    b = _run(wl)
+    for x, y in zip(outs, [b.out, b.out_lse, b.idx, b.scores]):
+        assert torch.equal(torch.nan_to_num(x, nan=-1.0),
+                           torch.nan_to_num(y, nan=-1.0))
+
+
+def test_selection_covering_context_is_dense_attention():
+    cfg = tsd_synth.config(QSA, B=2, lens=(1000, 77), top_k=1024, chunks=7,
+                           seed=122)
+    wl = tsd_synth.make(cfg, DEV)
+    bufs = _run(wl)
+    h = tsd_synth.to_host(wl)
+    dense, dlse = oracle.dense_attention(h["q"], "bf16", h["k_pool"],
+                                         h["v_pool"], "fp8_e4m3", h["k_scale"],
+                                         h["v_scale"], h["page_table"],
+                                         h["seq_lens"], h["num_pages"])
+    assert np.abs(bufs.out.cpu().numpy() - dense).max() <= out_tol("fp8_e4m3")
+    assert np.abs(bufs.out_lse.cpu().numpy() - dlse).max() <= out_tol("fp8_e4m3")

@@ -1,0 +1,267 @@
+"""Python binding of libtsd.so (top-k sparse decode attention for MI355X).
+
+Argument marshalling only: every function checks tensor placement, dtype and
+contiguity, then calls the C entry point of the same name on the current HIP
+stream (or the one given). All compute runs in the library's gfx950 kernels;
+there is no fallback of any kind, and importing this package raises when the
+built library is missing. Outputs are caller-allocated tensors, so the calls
+allocate nothing and can be captured in a HIP graph.
+
+Stored encodings: bf16 / fp16 tensors as such; FP8 E4M3 tensors either as
+``torch.float8_e4m3fn`` or as their ``uint8`` codes.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtsd.so")
+
+TSD_BF16, TSD_FP16, TSD_FP8_E4M3 = 1, 2, 3
+TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX = 1, 2
+ABI_VERSION = 1
+PAGE_SIZE = 64
+
+_P, _I32, _I64, _F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+
+
+class ScoreArgs(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", _I32), ("mode", _I32), ("B", _I32), ("page_size", _I32),
+        ("page_table", _P), ("pt_stride", _I64), ("seq_lens", _P),
+        ("num_pages", _I64),
+        ("q", _P), ("q_dtype", _I32), ("H_q", _I32), ("H_kv", _I32),
+        ("D", _I32), ("channel_idx", _P), ("r", _I32), ("label_dtype", _I32),
+        ("label_pool", _P),
+        ("index_q", _P), ("index_w", _P), ("index_k_pool", _P), ("q_pos", _P),
+        ("rows_per_req", _I32), ("H_i", _I32), ("D_i", _I32),
+        ("reserved0", _I32),
+        ("scores", _P), ("score_stride", _I64), ("row_lens_out", _P),
+    ]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", _I32), ("B", _I32), ("H_q", _I32), ("H_kv", _I32),
+        ("D", _I32), ("q_dtype", _I32), ("q", _P), ("k_pool", _P),
+        ("v_pool", _P), ("kv_dtype", _I32), ("page_size", _I32),
+        ("k_scale", _P), ("v_scale", _P), ("page_table", _P),
+        ("pt_stride", _I64), ("seq_lens", _P), ("num_pages", _I64),
+        ("idx", _P), ("count", _P), ("H_sel", _I32), ("k", _I32),
+        ("chunks", _I32), ("softmax_scale", _F32), ("o_part", _P),
+        ("lse_part", _P),
+    ]
+
+
+class TsdError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.tsd_strerror(status).decode()} "
+                         f"(status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python top_sparse_decode_amd/build_lib.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "sparse_index_score": (ctypes.c_int, [ctypes.POINTER(ScoreArgs), _P]),
+        "topk_select_workspace_bytes": (ctypes.c_size_t,
+                                        [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+        "topk_select": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, ctypes.c_int,
+                                       ctypes.c_int, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
+        "sparse_gqa_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _P]),
+        "lse_merge": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, _P, _P, _P]),
+        "tsd_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        "tsd_abi_version": (ctypes.c_int, []),
+        "tsd_sizeof_score_args": (ctypes.c_size_t, []),
+        "tsd_sizeof_attn_args": (ctypes.c_size_t, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    if lib.tsd_abi_version() != ABI_VERSION:
+        raise ImportError("libtsd.so ABI version mismatch")
+    if (lib.tsd_sizeof_score_args() != ctypes.sizeof(ScoreArgs)
+            or lib.tsd_sizeof_attn_args() != ctypes.sizeof(AttnArgs)):
+        raise ImportError("libtsd.so argument struct layout mismatch")
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("sparse_index_score", "topk_select_workspace_bytes", "topk_select",
+           "sparse_gqa_decode", "lse_merge", "tsd_strerror", "tsd_abi_version",
+           "tsd_sizeof_score_args", "tsd_sizeof_attn_args")
+
+
+# ----------------------------------------------------------------- helpers
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(name, t, dtype=None, dtypes=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    return t
+
+
+def _half_code(t):
+    return {torch.bfloat16: TSD_BF16, torch.float16: TSD_FP16}[t.dtype]
+
+
+def _kv_code(t):
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return TSD_FP8_E4M3
+    return _half_code(t)
+
+
+_FP8 = (torch.uint8, torch.float8_e4m3fn)
+_HALF = (torch.bfloat16, torch.float16)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise TsdError(fn, rc)
+
+
+# --------------------------------------------------------------- entry points
+def sparse_index_score(mode, scores, page_table, seq_lens, num_pages, *,
+                       q=None, channel_idx=None, label_pool=None,
+                       index_q=None, index_w=None, index_k_pool=None,
+                       q_pos=None, rows_per_req=1, row_lens_out=None,
+                       stream=None):
+    """Score every cached token of every row into ``scores`` [rows, stride].
+
+    mode "ds":  q [B,H_q,128] bf16/fp16, channel_idx [H_kv,r] int32,
+                label_pool [slots,H_kv,r] (q's dtype); rows = B*H_kv.
+    mode "qsa": index_q [rows,H_i,128] fp8, index_w [rows,H_i] f32,
+                index_k_pool [slots,128] fp8, q_pos [rows] int32 or None;
+                rows = B*rows_per_req.
+    ``row_lens_out`` (int32 [rows], optional) receives each row's key count.
+    """
+    _dev("scores", scores, torch.float32)
+    _dev("page_table", page_table, torch.int32)
+    _dev("seq_lens", seq_lens, torch.int32)
+    a = ScoreArgs()
+    a.abi_version, a.page_size = ABI_VERSION, PAGE_SIZE
+    a.B = page_table.shape[0]
+    a.page_table, a.pt_stride = _ptr(page_table), page_table.shape[1]
+    a.seq_lens, a.num_pages = _ptr(seq_lens), int(num_pages)
+    a.scores, a.score_stride = _ptr(scores), scores.shape[-1]
+    a.row_lens_out = _ptr(_dev("row_lens_out", row_lens_out, torch.int32))
+    if mode == "ds":
+        _dev("q", q, dtypes=_HALF)
+        _dev("channel_idx", channel_idx, torch.int32)
+        _dev("label_pool", label_pool, dtypes=_HALF)
+        a.mode = TSD_SCORE_DS_LABEL
+        a.q, a.q_dtype = _ptr(q), _half_code(q)
+        a.H_q, a.D = q.shape[1], q.shape[2]
+        a.H_kv, a.r = channel_idx.shape
+        a.channel_idx = _ptr(channel_idx)
+        a.label_pool, a.label_dtype = _ptr(label_pool), _half_code(label_pool)
+    elif mode == "qsa":
+        _dev("index_q", index_q, dtypes=_FP8)
+        _dev("index_w", index_w, torch.float32)
+        _dev("index_k_pool", index_k_pool, dtypes=_FP8)
+        _dev("q_pos", q_pos, torch.int32)
+        a.mode = TSD_SCORE_QSA_INDEX
+        a.index_q, a.index_w = _ptr(index_q), _ptr(index_w)
+        a.index_k_pool, a.q_pos = _ptr(index_k_pool), _ptr(q_pos)
+        a.rows_per_req = int(rows_per_req)
+        a.H_i, a.D_i = index_q.shape[1], index_q.shape[2]
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    _check("sparse_index_score", _lib.sparse_index_score(ctypes.byref(a),
+                                                         _stream(stream)))
+
+
+def topk_select_workspace_bytes(rows, max_len, k):
+    return int(_lib.topk_select_workspace_bytes(int(rows), int(max_len), int(k)))
+
+
+def topk_select(scores, row_lens, k, max_len, idx, count=None, workspace=None,
+                stream=None):
+    """Exact top-k per row of ``scores`` [rows, stride] into ``idx`` [rows, k]
+    (ascending, -1 padded) and ``count`` [rows]. ``workspace`` is a uint8
+    CUDA tensor of at least topk_select_workspace_bytes(rows, max_len, k)."""
+    _dev("scores", scores, torch.float32)
+    _dev("row_lens", row_lens, torch.int32)
+    _dev("idx", idx, torch.int32)
+    _dev("count", count, torch.int32)
+    _dev("workspace", workspace)
+    rows = scores.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("topk_select", _lib.topk_select(
+        _ptr(scores), scores.shape[-1], rows, _ptr(row_lens), int(max_len),
+        int(k), _ptr(idx), _ptr(count), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+
+
+def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
+                      count, chunks, o_part, lse_part, k_scale=None,
+                      v_scale=None, softmax_scale=None, stream=None):
+    """Chunked sparse GQA attention over the selection ``idx`` [B,H_sel,k]
+    into ``o_part`` [B,H_q,chunks,128] and ``lse_part`` [B,H_q,chunks]."""
+    _dev("q", q, dtypes=_HALF)
+    _dev("k_pool", k_pool, dtypes=_HALF + _FP8)
+    _dev("v_pool", v_pool, dtypes=_HALF + _FP8)
+    _dev("page_table", page_table, torch.int32)
+    _dev("seq_lens", seq_lens, torch.int32)
+    _dev("idx", idx, torch.int32)
+    _dev("count", count, torch.int32)
+    _dev("o_part", o_part, torch.float32)
+    _dev("lse_part", lse_part, torch.float32)
+    _dev("k_scale", k_scale, torch.float32)
+    _dev("v_scale", v_scale, torch.float32)
+    a = AttnArgs()
+    a.abi_version, a.page_size = ABI_VERSION, PAGE_SIZE
+    a.B, a.H_q, a.D = q.shape
+    a.H_kv = k_pool.shape[1]
+    a.q, a.q_dtype = _ptr(q), _half_code(q)
+    a.k_pool, a.v_pool, a.kv_dtype = _ptr(k_pool), _ptr(v_pool), _kv_code(k_pool)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.page_table, a.pt_stride = _ptr(page_table), page_table.shape[1]
+    a.seq_lens, a.num_pages = _ptr(seq_lens), int(num_pages)
+    a.idx, a.count = _ptr(idx), _ptr(count)
+    a.H_sel, a.k = idx.shape[1], idx.shape[2]
+    a.chunks = int(chunks)
+    a.softmax_scale = (1.0 / math.sqrt(a.D) if softmax_scale is None
+                       else float(softmax_scale))
+    a.o_part, a.lse_part = _ptr(o_part), _ptr(lse_part)
+    _check("sparse_gqa_decode", _lib.sparse_gqa_decode(ctypes.byref(a),
+                                                       _stream(stream)))
+
+
+def lse_merge(o_part, lse_part, out, out_lse=None, stream=None):
+    """Merge ``o_part`` [..., C, D] / ``lse_part`` [..., C] into ``out``
+    [..., D] and ``out_lse`` [...]."""
+    _dev("o_part", o_part, torch.float32)
+    _dev("lse_part", lse_part, torch.float32)
+    _dev("out", out, torch.float32)
+    _dev("out_lse", out_lse, torch.float32)
+    C, D = o_part.shape[-2], o_part.shape[-1]
+    rows = lse_part.numel() // C if C else 0
+    _check("lse_merge", _lib.lse_merge(_ptr(o_part), _ptr(lse_part), rows, C,
+                                       D, _ptr(out), _ptr(out_lse),
+                                       _stream(stream)))

@@ -1,0 +1,86 @@
+// Device helpers shared by the gfx950 kernels of libtsd.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define TSD_DEVICE __device__ __forceinline__
+
+namespace tsd {
+
+constexpr int kWave = 64;
+constexpr int kPage = 64;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Two OCP E4M3 values held in bytes (2*HI, 2*HI+1) of a dword, converted by
+// the gfx950 hardware converter (OCP encoding on this target).
+template <bool HI>
+TSD_DEVICE float2 fp8x2_to_f32(uint32_t w) {
+  auto r = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  return make_float2(r[0], r[1]);
+}
+
+// Four E4M3 values of one dword.
+TSD_DEVICE void fp8x4_to_f32(uint32_t w, float* out) {
+  float2 a = fp8x2_to_f32<false>(w);
+  float2 b = fp8x2_to_f32<true>(w);
+  out[0] = a.x; out[1] = a.y; out[2] = b.x; out[3] = b.y;
+}
+
+TSD_DEVICE float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+TSD_DEVICE float fp16_to_f32(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
+// 16-bit element -> f32 for the two 16-bit encodings (is_bf16 selects).
+TSD_DEVICE float half_to_f32(uint16_t h, bool is_bf16) {
+  return is_bf16 ? bf16_to_f32(h) : fp16_to_f32(h);
+}
+
+// Order-preserving map f32 -> u32 (larger float -> larger key); -0 is
+// folded onto +0 first so that the two compare equal, as floats do.
+TSD_DEVICE uint32_t order_key(float x) {
+  uint32_t b = __float_as_uint(x);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+TSD_DEVICE float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+TSD_DEVICE float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+TSD_DEVICE uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+TSD_DEVICE uint32_t wave_inclusive_scan(uint32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    uint32_t n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
+// Clamp a device-side length to [0, cap].
+TSD_DEVICE int64_t clamp_len(int64_t n, int64_t cap) {
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
+}  // namespace tsd

@@ -1,0 +1,26 @@
+// Internal launchers of libtsd.so (host side). Arguments have already been
+// validated by the C-ABI entry points when these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "tsd.h"
+
+namespace tsd {
+
+hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s);
+hipError_t launch_ds_scan(const tsd_score_args& a, hipStream_t s);
+
+size_t topk_workspace(int rows, int max_len, int k);
+hipError_t launch_topk(const float* scores, int64_t stride, int rows,
+                       const int32_t* row_lens, int max_len, int k,
+                       int32_t* idx, int32_t* count, void* ws,
+                       hipStream_t s);
+
+hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s);
+
+hipError_t launch_lse_merge(const float* o_part, const float* lse_part,
+                            int rows, int C, int D, float* out,
+                            float* out_lse, hipStream_t s);
+
+}  // namespace tsd

@@ -1,0 +1,186 @@
+// C-ABI entry points of libtsd.so: host-side validation, then the launch.
+// Validation never touches the HIP runtime or device memory, so every error
+// path returns before anything is enqueued (and can be exercised on a host
+// without a GPU).
+#include <limits>
+
+#include "launch.h"
+#include "tsd.h"
+
+namespace {
+
+constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
+
+bool half_enc(int e) { return e == TSD_BF16 || e == TSD_FP16; }
+bool any_enc(int e) { return half_enc(e) || e == TSD_FP8_E4M3; }
+
+int check_batch_view(int32_t B, int32_t page_size, const int32_t* pt,
+                     int64_t pt_stride, const int32_t* lens,
+                     int64_t num_pages) {
+  if (B < 0 || pt_stride < 1 || num_pages < 0) return TSD_E_SHAPE;
+  if (page_size != TSD_PAGE_SIZE) return TSD_E_PAGE_SIZE;
+  if (B > 0 && (!pt || !lens)) return TSD_E_NULL;
+  if (B > 65535) return TSD_E_UNSUPPORTED;
+  return TSD_OK;
+}
+
+int validate_score(const tsd_score_args* a) {
+  if (!a) return TSD_E_NULL;
+  if (a->abi_version != TSD_ABI_VERSION) return TSD_E_ABI;
+  if (a->mode != TSD_SCORE_DS_LABEL && a->mode != TSD_SCORE_QSA_INDEX)
+    return TSD_E_MODE;
+  int rc = check_batch_view(a->B, a->page_size, a->page_table, a->pt_stride,
+                            a->seq_lens, a->num_pages);
+  if (rc) return rc;
+  if (a->score_stride < 1) return TSD_E_SHAPE;
+  if (a->B > 0 && !a->scores) return TSD_E_NULL;
+  if (a->mode == TSD_SCORE_DS_LABEL) {
+    if (a->B > 0 && (!a->q || !a->channel_idx || !a->label_pool))
+      return TSD_E_NULL;
+    if (!half_enc(a->q_dtype) || a->label_dtype != a->q_dtype)
+      return TSD_E_DTYPE;
+    if (a->H_q < 1 || a->H_kv < 1 || a->r < 1 || a->D < 1) return TSD_E_SHAPE;
+    if (a->H_q % a->H_kv) return TSD_E_GQA;
+    if (a->D != TSD_HEAD_DIM || a->r > a->D) return TSD_E_UNSUPPORTED;
+    if (a->H_kv > 128 || static_cast<int64_t>(a->H_kv) * a->r > 4096)
+      return TSD_E_UNSUPPORTED;
+    if (a->pt_stride > kMaxGrid) return TSD_E_UNSUPPORTED;
+  } else {
+    if (a->B > 0 && (!a->index_q || !a->index_w || !a->index_k_pool))
+      return TSD_E_NULL;
+    if (a->rows_per_req < 1 || a->H_i < 1 || a->D_i < 1) return TSD_E_SHAPE;
+    if (a->H_i > TSD_MAX_INDEX_HEADS || a->D_i != TSD_HEAD_DIM)
+      return TSD_E_UNSUPPORTED;
+    const int64_t rows = static_cast<int64_t>(a->B) * a->rows_per_req;
+    if (rows > kMaxGrid) return TSD_E_UNSUPPORTED;
+    const int64_t waves = rows * ((a->pt_stride + 3) / 4);
+    if (waves / 4 + 1 > kMaxGrid) return TSD_E_UNSUPPORTED;
+  }
+  return TSD_OK;
+}
+
+int validate_topk(const float* scores, int64_t stride, int rows,
+                  const int32_t* row_lens, int max_len, int k, int32_t* idx,
+                  void* ws, size_t ws_bytes) {
+  if (rows < 0 || max_len < 0 || stride < 1 || stride < max_len)
+    return TSD_E_SHAPE;
+  if (k < 1 || k > TSD_MAX_TOPK) return TSD_E_K;
+  if (rows > 65535) return TSD_E_UNSUPPORTED;
+  if (rows == 0) return TSD_OK;
+  if (!scores || !row_lens || !idx) return TSD_E_NULL;
+  if (!ws || ws_bytes < tsd::topk_workspace(rows, max_len, k))
+    return TSD_E_WORKSPACE;
+  return TSD_OK;
+}
+
+int validate_attn(const tsd_attn_args* a) {
+  if (!a) return TSD_E_NULL;
+  if (a->abi_version != TSD_ABI_VERSION) return TSD_E_ABI;
+  int rc = check_batch_view(a->B, a->page_size, a->page_table, a->pt_stride,
+                            a->seq_lens, a->num_pages);
+  if (rc) return rc;
+  if (a->H_q < 1 || a->H_kv < 1 || a->D < 1) return TSD_E_SHAPE;
+  if (a->H_q % a->H_kv) return TSD_E_GQA;
+  if (a->H_sel != 1 && a->H_sel != a->H_kv) return TSD_E_GQA;
+  if (a->H_q / a->H_kv > TSD_MAX_GQA_GROUP) return TSD_E_UNSUPPORTED;
+  if (a->D != TSD_HEAD_DIM) return TSD_E_UNSUPPORTED;
+  if (a->H_kv > 65535) return TSD_E_UNSUPPORTED;
+  if (a->k < 1 || a->k > TSD_MAX_TOPK) return TSD_E_K;
+  if (a->chunks < 1 || a->chunks > TSD_MAX_CHUNKS) return TSD_E_CHUNKS;
+  if (!any_enc(a->kv_dtype) || !half_enc(a->q_dtype)) return TSD_E_DTYPE;
+  if (a->kv_dtype != TSD_FP8_E4M3 && a->q_dtype != a->kv_dtype)
+    return TSD_E_DTYPE;
+  if (a->B == 0) return TSD_OK;
+  if (!a->q || !a->k_pool || !a->v_pool || !a->idx || !a->count ||
+      !a->o_part || !a->lse_part)
+    return TSD_E_NULL;
+  if (a->kv_dtype == TSD_FP8_E4M3 && (!a->k_scale || !a->v_scale))
+    return TSD_E_NULL;
+  return TSD_OK;
+}
+
+int validate_merge(const float* o_part, const float* lse_part, int rows,
+                   int C, int D, float* out) {
+  if (rows < 0 || D < 1) return TSD_E_SHAPE;
+  if (C < 1 || C > TSD_MAX_CHUNKS) return TSD_E_CHUNKS;
+  if (D > 512) return TSD_E_UNSUPPORTED;
+  if (rows == 0) return TSD_OK;
+  if (!o_part || !lse_part || !out) return TSD_E_NULL;
+  return TSD_OK;
+}
+
+int launch_status(hipError_t e) {
+  return e == hipSuccess ? TSD_OK : static_cast<int>(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_index_score(const tsd_score_args* a, hipStream_t stream) {
+  const int rc = validate_score(a);
+  if (rc) return rc;
+  if (a->B == 0) return TSD_OK;
+  if (a->mode == TSD_SCORE_DS_LABEL)
+    return launch_status(tsd::launch_ds_scan(*a, stream));
+  return launch_status(tsd::launch_qsa_scan(*a, stream));
+}
+
+size_t topk_select_workspace_bytes(int rows, int max_len, int k) {
+  if (rows <= 0 || max_len < 0) return 0;
+  return tsd::topk_workspace(rows, max_len, k);
+}
+
+int topk_select(const float* scores, int64_t stride, int rows,
+                const int32_t* row_lens, int max_len, int k, int32_t* idx,
+                int32_t* count, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  const int rc = validate_topk(scores, stride, rows, row_lens, max_len, k,
+                               idx, ws, ws_bytes);
+  if (rc) return rc;
+  if (rows == 0) return TSD_OK;
+  return launch_status(tsd::launch_topk(scores, stride, rows, row_lens,
+                                        max_len, k, idx, count, ws, stream));
+}
+
+int sparse_gqa_decode(const tsd_attn_args* a, hipStream_t stream) {
+  const int rc = validate_attn(a);
+  if (rc) return rc;
+  if (a->B == 0) return TSD_OK;
+  return launch_status(tsd::launch_sparse_gqa(*a, stream));
+}
+
+int lse_merge(const float* o_part, const float* lse_part, int rows, int C,
+              int D, float* out, float* out_lse, hipStream_t stream) {
+  const int rc = validate_merge(o_part, lse_part, rows, C, D, out);
+  if (rc) return rc;
+  if (rows == 0) return TSD_OK;
+  return launch_status(
+      tsd::launch_lse_merge(o_part, lse_part, rows, C, D, out, out_lse, stream));
+}
+
+const char* tsd_strerror(int status) {
+  switch (status) {
+    case TSD_OK: return "success";
+    case TSD_E_NULL: return "a required pointer is NULL";
+    case TSD_E_DTYPE: return "unsupported or inconsistent element encoding";
+    case TSD_E_SHAPE: return "invalid size or stride";
+    case TSD_E_PAGE_SIZE: return "page_size must be 64";
+    case TSD_E_GQA: return "H_q must be a multiple of H_kv and H_sel 1 or H_kv";
+    case TSD_E_K: return "top_k must lie in [1, 4096]";
+    case TSD_E_CHUNKS: return "chunks must lie in [1, 64]";
+    case TSD_E_WORKSPACE: return "workspace missing or too small";
+    case TSD_E_UNSUPPORTED: return "configuration not supported by this build";
+    case TSD_E_MODE: return "unknown score mode";
+    case TSD_E_ABI: return "argument struct from another ABI version";
+    default:
+      return status > 0 ? "HIP launch failed (status is the hipError_t)"
+                        : "unknown status";
+  }
+}
+
+int tsd_abi_version(void) { return TSD_ABI_VERSION; }
+size_t tsd_sizeof_score_args(void) { return sizeof(tsd_score_args); }
+size_t tsd_sizeof_attn_args(void) { return sizeof(tsd_attn_args); }
+
+}  // extern "C"

@@ -206,6 +206,7 @@ def heavy_channels(k_pool: torch.Tensor, seq_lens, page_table, r: int,
     acc = torch.zeros((H_kv, D), dtype=torch.float64, device=k_pool.device)
     cnt = 0
     B = page_table.shape[0]
+    page_table = page_table.to(k_pool.device)
     t = torch.arange(prefix_len, device=k_pool.device)
     for b in range(B):
         n = min(prefix_len, int(seq_lens[b]))
