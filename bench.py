@@ -1,0 +1,183 @@
+"""Benchmark of one sparse-decode step on one MI355X.
+
+A step is the whole path over one batch: sparse_index_score -> topk_select
+-> sparse_gqa_decode -> lse_merge, on one layer's inputs. Steps rotate over
+``--replicas`` layers with their own pools so the bytes scanned between two
+visits of the same layer exceed the 256 MB Infinity Cache. Inputs are seeded
+synthetic tensors already resident in HBM when the timed region starts.
+
+Prints one JSON line: steps/s (whole-job throughput), the model HBM rate of
+the step, the roofline of the dominant kernel (the index-K scan) from HIP
+events on the launch stream, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = ("sparse-decode steps/s + achieved HBM GB/s (% roofline) at 262K ctx, "
+          "top_k=2048")
+
+
+def model_bytes(cfg):
+    """Algorithmic bytes of one step: the index (or label) keys of every
+    cached token plus the K and V rows of the selected tokens."""
+    B, L, k = cfg.B, (cfg.lens[0] if cfg.lens else cfg.L), cfg.top_k
+    kv_b = 1 if cfg.kv_enc == "fp8_e4m3" else 2
+    if cfg.mode == "qsa":
+        index = B * L * cfg.D_i                      # FP8 index key per token
+        gather = B * k * cfg.H_kv * cfg.D * 2 * kv_b  # shared selection
+    else:
+        index = B * L * cfg.H_kv * cfg.r * kv_b      # label per token and head
+        gather = B * cfg.H_kv * k * cfg.D * 2 * kv_b  # per-head selection
+    return index, gather
+
+
+def cpu_baseline(layer, seconds):
+    """The CPU oracle (single thread, as it stands) on whole requests of one
+    step, until about ``seconds`` of work; scaled to steps/s."""
+    import numpy as np  # noqa: F401
+
+    import oracle
+    import tsd_synth
+    h = tsd_synth.to_host(layer)
+    B = h["B"]
+    done, t0 = 0, time.perf_counter()
+    for b in range(B):
+        sub = dict(h)
+        sub["B"] = 1
+        for key in ("q", "page_table", "seq_lens"):
+            sub[key] = h[key][b:b + 1]
+        if h["mode"] == "qsa":
+            sub["index_q"], sub["index_w"] = h["index_q"][b:b + 1], h["index_w"][b:b + 1]
+        oracle.decode_step(sub)
+        done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": (done / B) / el, "unit": "steps/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} of {B} requests of one step (each: every cached "
+                      f"token scored, exact top-{h['top_k']}, sparse attention "
+                      f"over {h['H_q']} heads, merge) in {el:.1f} s, scaled to "
+                      f"steps/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="qsa_decode_b8_l262144_k2048")
+    ap.add_argument("--replicas", type=int, default=0,
+                    help="layer replicas (0: enough for >= 1 GB between reuse)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path "
+              "(sharding is described in the design notes); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd.step as step
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    cfg = tsd_synth.config(args.workload)
+    index_b, gather_b = model_bytes(cfg)
+    R = args.replicas or max(1, math.ceil(1e9 / index_b))
+    layers = [tsd_synth.make(cfg, dev, layer=i) for i in range(R)]
+    bufs = step.StepBuffers(layers[0])
+    plans = [step.Plan(layer, bufs) for layer in layers]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        plans[i % R].run(stream)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, no instrumentation
+    K = args.steps
+    t0 = time.perf_counter()
+    for i in range(K):
+        plans[i % R].run(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # kernel durations: the same K steps with HIP events bracketing each call
+    names = ("sparse_index_score", "topk_select", "sparse_gqa_decode",
+             "lse_merge")
+    evs = {n: [(torch.cuda.Event(enable_timing=True),
+                torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+           for n in names}
+    cur = [0]
+
+    def before(n):
+        evs[n][cur[0]][0].record(stream)
+
+    def after(n):
+        evs[n][cur[0]][1].record(stream)
+
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        cur[0] = i
+        plans[i % R].run(stream, before=before, after=after)
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t1
+    us = {n: 1e3 * sum(a.elapsed_time(b) for a, b in evs[n]) / K for n in names}
+
+    step_s = wall / K
+    scan_s = us["sparse_index_score"] * 1e-6
+    achieved = index_b / scan_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": 1.0 / step_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if cfg.kv_enc == "fp8_e4m3" else cfg.kv_enc,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.B, "context": cfg.L,
+                   "top_k": cfg.top_k, "chunks": cfg.chunks, "H_q": cfg.H_q,
+                   "H_kv": cfg.H_kv, "head_dim": cfg.D, "kv_cache": cfg.kv_enc,
+                   "index_heads": cfg.H_i if cfg.mode == "qsa" else None,
+                   "heavy_channels": cfg.r if cfg.mode == "ds" else None,
+                   "page_size": 64, "layer_replicas": R},
+        "model_bytes_per_step": index_b + gather_b,
+        "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
+        "step_frac_of_hbm": (index_b + gather_b) / step_s / 1e9 / HBM_PEAK_GBPS,
+        "kernel_us": us,
+        "instrumented_ms_per_step": wall_ev / K * 1e3,
+        "roofline": {"bound": "hbm", "kernel": "sparse_index_score",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "bytes_per_launch": index_b, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

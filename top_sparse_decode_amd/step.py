@@ -88,3 +88,93 @@ def decode_step(layer, bufs, stream=None):
     select(layer, bufs, stream)
     attend(layer, bufs, stream)
     merge(layer, bufs, stream)
+
+
+class Plan:
+    """The four C calls of one layer with their arguments marshalled once.
+
+    ``run(stream)`` issues sparse_index_score, topk_select, sparse_gqa_decode
+    and lse_merge straight through the C ABI on ``stream`` (a torch stream),
+    so repeated steps pay only the foreign-call cost. Per-call hooks
+    (``before``/``after``, called with the call's name) let a caller bracket
+    individual calls with events on the same stream."""
+
+    def __init__(self, layer, bufs):
+        import ctypes
+
+        from . import (ABI_VERSION, PAGE_SIZE, AttnArgs, ScoreArgs,
+                       TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX, _half_code,
+                       _kv_code, _lib)
+        P = ctypes.c_void_p
+        p = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
+        self._lib, self._keep = _lib, (layer, bufs)
+        a = ScoreArgs()
+        a.abi_version, a.page_size = ABI_VERSION, PAGE_SIZE
+        a.B = layer["page_table"].shape[0]
+        a.page_table, a.pt_stride = p(layer["page_table"]), layer["page_table"].shape[1]
+        a.seq_lens, a.num_pages = p(layer["seq_lens"]), int(layer["num_pages"])
+        a.scores, a.score_stride = p(bufs.scores), bufs.scores.shape[-1]
+        a.row_lens_out = p(bufs.row_lens)
+        if layer["mode"] == "ds":
+            a.mode = TSD_SCORE_DS_LABEL
+            q = layer["q"]
+            a.q, a.q_dtype = p(q), _half_code(q)
+            a.H_q, a.D = q.shape[1], q.shape[2]
+            a.H_kv, a.r = layer["channel_idx"].shape
+            a.channel_idx = p(layer["channel_idx"])
+            a.label_pool = p(layer["label_pool"])
+            a.label_dtype = _half_code(layer["label_pool"])
+        else:
+            a.mode = TSD_SCORE_QSA_INDEX
+            ik = layer.get("index_k_pool", layer.get("index_k"))
+            a.index_q, a.index_w = p(layer["index_q"]), p(layer["index_w"])
+            a.index_k_pool, a.q_pos = p(ik), p(layer.get("q_pos"))
+            a.rows_per_req = layer.get("rows_per_req", 1)
+            a.H_i, a.D_i = layer["index_q"].shape[1], layer["index_q"].shape[2]
+        self.score_args = a
+        k = layer["top_k"]
+        self.topk_args = (p(bufs.scores), bufs.scores.shape[-1], bufs.rows,
+                          p(bufs.row_lens), bufs.max_len, k, p(bufs.idx),
+                          p(bufs.count), p(bufs.ws), bufs.ws.numel())
+        t = AttnArgs()
+        q = layer["q"]
+        t.abi_version, t.page_size = ABI_VERSION, PAGE_SIZE
+        t.B, t.H_q, t.D = q.shape
+        t.H_kv = layer["k_pool"].shape[1]
+        t.q, t.q_dtype = p(q), _half_code(q)
+        t.k_pool, t.v_pool = p(layer["k_pool"]), p(layer["v_pool"])
+        t.kv_dtype = _kv_code(layer["k_pool"])
+        t.k_scale, t.v_scale = p(layer.get("k_scale")), p(layer.get("v_scale"))
+        t.page_table, t.pt_stride = a.page_table, a.pt_stride
+        t.seq_lens, t.num_pages = a.seq_lens, a.num_pages
+        t.idx, t.count, t.H_sel, t.k = p(bufs.idx), p(bufs.count), bufs.H_sel, k
+        t.chunks = layer["chunks"]
+        t.softmax_scale = 1.0 / (t.D ** 0.5)
+        t.o_part, t.lse_part = p(bufs.o_part), p(bufs.lse_part)
+        self.attn_args = t
+        C, D = bufs.o_part.shape[-2], bufs.o_part.shape[-1]
+        self.merge_args = (p(bufs.o_part), p(bufs.lse_part),
+                           bufs.lse_part.numel() // C, C, D, p(bufs.out),
+                           p(bufs.out_lse))
+        self._score_ref = ctypes.byref(self.score_args)
+        self._attn_ref = ctypes.byref(self.attn_args)
+
+    def run(self, stream=None, before=None, after=None):
+        import ctypes
+
+        from . import TsdError
+        s = stream if stream is not None else torch.cuda.current_stream()
+        h = ctypes.c_void_p(s.cuda_stream)
+        lib = self._lib
+        calls = (("sparse_index_score", lambda: lib.sparse_index_score(self._score_ref, h)),
+                 ("topk_select", lambda: lib.topk_select(*self.topk_args, h)),
+                 ("sparse_gqa_decode", lambda: lib.sparse_gqa_decode(self._attn_ref, h)),
+                 ("lse_merge", lambda: lib.lse_merge(*self.merge_args, h)))
+        for name, fn in calls:
+            if before:
+                before(name)
+            rc = fn()
+            if rc:
+                raise TsdError(name, rc)
+            if after:
+                after(name)
