@@ -83,6 +83,12 @@ def main():
                     help="layer replicas (0: enough for >= 1 GB between reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time HIP-graph replays of the step instead of eager "
+                         "launches")
+    ap.add_argument("--unfused", action="store_true",
+                    help="time sparse_index_score + topk_select instead of "
+                         "sparse_index_topk")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -103,7 +109,10 @@ def main():
     R = args.replicas or max(1, math.ceil(1e9 / index_b))
     layers = [tsd_synth.make(cfg, dev, layer=i) for i in range(R)]
     bufs = step.StepBuffers(layers[0])
-    plans = [step.Plan(layer, bufs) for layer in layers]
+    plans = [step.Plan(layer, bufs, fused=not args.unfused) for layer in layers]
+    # the instrumented pass issues the calls separately, so the events around
+    # sparse_index_score bracket the scan kernel alone
+    plans_sep = [step.Plan(layer, bufs, fused=False) for layer in layers]
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -111,36 +120,58 @@ def main():
         plans[i % R].run(stream)
     torch.cuda.synchronize()
 
-    # timed region: K steps, no instrumentation
     K = args.steps
+    # eager steps (the four C calls launched from the host each step)
     t0 = time.perf_counter()
     for i in range(K):
         plans[i % R].run(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
 
-    # kernel durations: the same K steps with HIP events bracketing each call
+    # the same step captured once per layer into a HIP graph and replayed
+    graphs = []
+    if args.graph:
+        for plan in plans:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                plan.run(torch.cuda.current_stream())
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        wall_graph = time.perf_counter() - t0
+    wall = wall_graph if graphs else wall_eager
+
+    # kernel durations: for each call, K back-to-back launches (rotating the
+    # layers) between two HIP events on the launch stream; the average per
+    # launch is the call's device time including its dispatch
+    from top_sparse_decode_amd import TsdError
     names = ("sparse_index_score", "topk_select", "sparse_gqa_decode",
              "lse_merge")
-    evs = {n: [(torch.cuda.Event(enable_timing=True),
-                torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-           for n in names}
-    cur = [0]
-
-    def before(n):
-        evs[n][cur[0]][0].record(stream)
-
-    def after(n):
-        evs[n][cur[0]][1].record(stream)
-
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(K):
-        cur[0] = i
-        plans[i % R].run(stream, before=before, after=after)
-    torch.cuda.synchronize()
-    wall_ev = time.perf_counter() - t1
-    us = {n: 1e3 * sum(a.elapsed_time(b) for a, b in evs[n]) / K for n in names}
+    fused_plans = plans if not args.unfused else [
+        step.Plan(layer, bufs, fused=True) for layer in layers]
+    table = [dict(p.calls(stream)) for p in plans_sep]
+    for p, f in zip(table, fused_plans):
+        p["sparse_index_topk"] = dict(f.calls(stream))["sparse_index_topk"]
+    us = {}
+    for name in names + ("sparse_index_topk",):
+        for i in range(args.warmup):
+            plans_sep[i % R].run(stream)  # leave consistent buffers behind
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            rc = table[i % R][name]()
+            if rc:
+                raise TsdError(name, rc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = e0.elapsed_time(e1) * 1e3 / K
 
     step_s = wall / K
     scan_s = us["sparse_index_score"] * 1e-6
@@ -168,7 +199,9 @@ def main():
         "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
         "step_frac_of_hbm": (index_b + gather_b) / step_s / 1e9 / HBM_PEAK_GBPS,
         "kernel_us": us,
-        "instrumented_ms_per_step": wall_ev / K * 1e3,
+        "launch_mode": "hip_graph" if graphs else "eager",
+        "score_select": "separate calls" if args.unfused else "sparse_index_topk",
+        "eager_steps_per_s": K / wall_eager,
         "roofline": {"bound": "hbm", "kernel": "sparse_index_score",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -180,13 +180,32 @@ int sparse_index_score(const tsd_score_args *a, hipStream_t stream);
  *   ws       device workspace of at least topk_select_workspace_bytes()
  *            bytes, caller-owned; its contents need no initialisation and
  *            are scratch after the call (one workspace per concurrent call)
- * 1 <= k <= 4096; rows >= 0; stride >= max_len >= 0.
+ * 1 <= k <= 4096; 0 <= rows <= 65535; stride >= max_len >= 0;
+ * max_len <= 16,777,216.
  * ------------------------------------------------------------------------ */
 size_t topk_select_workspace_bytes(int rows, int max_len, int k);
 
 int topk_select(const float *scores, int64_t stride, int rows,
                 const int32_t *row_lens, int max_len, int k, int32_t *idx,
                 int32_t *count, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sparse_index_topk
+ *
+ * sparse_index_score followed by topk_select on the scores it writes, with
+ * identical results, in fewer passes: the index scan also builds the first
+ * radix-digit histogram of every row, so the selection skips its own
+ * histogram pass and one read of the scores (QSA_INDEX mode; DS_LABEL runs
+ * the two steps back to back). The scores are still written to a->scores.
+ *   a->row_lens_out  required: receives each row's key count
+ *   rows             B * H_kv (DS) or B * rows_per_req (QSA)
+ *   max_len          min(a->score_stride, a->pt_stride * 64)
+ *   ws / ws_bytes    topk_select_workspace_bytes(rows, max_len, k) bytes
+ *   idx, count, k    as for topk_select
+ * ------------------------------------------------------------------------ */
+int sparse_index_topk(const tsd_score_args *a, int k, int32_t *idx,
+                      int32_t *count, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * sparse_gqa_decode

@@ -92,6 +92,28 @@ def test_score_null_args_and_empty_batch():
     assert _score(B=0, scores=None, page_table=None, seq_lens=None) == 0
 
 
+def test_fused_score_topk_rejections():
+    def call(k=10, row_lens=True, ws_bytes=None, **kw):
+        a = ScoreArgs()
+        a.abi_version, a.mode, a.B, a.page_size = 1, 2, 2, 64
+        a.page_table, a.pt_stride, a.seq_lens, a.num_pages = FAKE, 4, FAKE, 8
+        a.index_q, a.index_w, a.index_k_pool = FAKE, FAKE, FAKE
+        a.rows_per_req, a.H_i, a.D_i = 1, 16, 128
+        a.scores, a.score_stride = FAKE, 256
+        a.row_lens_out = FAKE if row_lens else None
+        for key, v in kw.items():
+            setattr(a, key, v)
+        need = LIB.topk_select_workspace_bytes(2, 256, max(1, k))
+        return LIB.sparse_index_topk(ctypes.byref(a), k, FAKE, None, FAKE,
+                                     need if ws_bytes is None else ws_bytes,
+                                     None)
+    assert call(row_lens=False) == E["NULL"]
+    assert call(k=0) == E["K"]
+    assert call(ws_bytes=8) == E["WORKSPACE"]
+    assert call(page_size=16) == E["PAGE_SIZE"]
+    assert call(B=0, scores=None, page_table=None, seq_lens=None) == 0
+
+
 def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, **kw):
     need = LIB.topk_select_workspace_bytes(rows, max_len, k)
     args = dict(scores=FAKE, row_lens=FAKE, idx=FAKE, ws=FAKE)
@@ -110,13 +132,23 @@ def test_topk_rejections():
     assert _topk(ws=None) == E["WORKSPACE"]
     assert _topk(scores=None) == E["NULL"]
     assert _topk(rows=70000) == E["UNSUPPORTED"]
+    assert _topk(max_len=(1 << 24) + 1, stride=(1 << 24) + 1) == E["UNSUPPORTED"]
     assert _topk(rows=0, scores=None, row_lens=None, idx=None, ws=None) == 0
 
 
+def _ws_words(rows, max_len):
+    # 4096- and 1024-bin histograms per row, one counter per 4096-element
+    # chunk, padding to 8 bytes, then a 512-entry list of 8-byte pairs per chunk
+    nch = max(1, -(-max_len // 4096))
+    off = rows * 5120 + rows * nch
+    off += off & 1
+    return off + 2 * rows * nch * 512
+
+
 def test_topk_workspace_size():
-    # 5120 histogram words per row plus two counters per 1024-element slice
-    assert tsd.topk_select_workspace_bytes(8, 262144, 2048) == 8 * (5120 + 512) * 4
-    assert tsd.topk_select_workspace_bytes(1, 1, 1) == (5120 + 2) * 4
+    assert tsd.topk_select_workspace_bytes(8, 262144, 2048) == 4 * _ws_words(8, 262144)
+    assert tsd.topk_select_workspace_bytes(1, 1, 1) == 4 * _ws_words(1, 1)
+    assert tsd.topk_select_workspace_bytes(2048, 1 << 20, 2048) == 4 * _ws_words(2048, 1 << 20)
     assert tsd.topk_select_workspace_bytes(0, 100, 5) == 0
 
 

@@ -253,3 +253,62 @@ def test_selection_covering_context_is_dense_attention():
                                          h["seq_lens"], h["num_pages"])
     assert np.abs(bufs.out.cpu().numpy() - dense).max() <= out_tol("fp8_e4m3")
     assert np.abs(bufs.out_lse.cpu().numpy() - dlse).max() <= out_tol("fp8_e4m3")
+
+
+def test_graph_replay_matches_eager():
+    """The four calls captured in a HIP graph, replayed with fresh inputs
+    copied in between (and eager work between replays), match the eager
+    results of the same inputs on every replay."""
+    step = _step()
+    cfg = tsd_synth.config(QSA, B=3, lens=(6000, 4097, 130), top_k=512,
+                           chunks=8, seed=130)
+    wl = tsd_synth.make(cfg, DEV)
+    bufs = step.StepBuffers(wl)
+    plan = step.Plan(wl, bufs)
+    plan.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(torch.cuda.current_stream())
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(3)
+    for rep in range(4):
+        # mutate the query rows and the lengths in place, as a decode loop does
+        wl["index_q"].copy_(tsd_synth.fp8_codes(
+            torch.randn(wl["index_q"].shape, generator=gen, device=DEV)))
+        wl["q"].copy_(torch.randn(wl["q"].shape, generator=gen,
+                                  device=DEV).to(torch.bfloat16))
+        wl["seq_lens"].copy_(torch.tensor([6000 - 7 * rep, 4097 - rep, 130 + rep],
+                                          dtype=torch.int32, device=DEV))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (bufs.idx, bufs.count, bufs.out, bufs.out_lse)]
+        plan.run()
+        torch.cuda.synchronize()
+        for a, b in zip(got, (bufs.idx, bufs.count, bufs.out, bufs.out_lse)):
+            assert torch.equal(a, b), f"replay {rep} differs from eager"
+
+
+@pytest.mark.parametrize("name,over", [
+    (QSA, dict(B=3, lens=(9000, 4097, 130), top_k=512, chunks=8)),
+    (QSA, dict(B=2, lens=(700, 129), top_k=100, chunks=4, stale_tail=True)),
+    (QSA, dict(B=2, lens=(2048, 50), top_k=2048, chunks=16)),
+    (DS8B, dict(B=2, lens=(3000, 700), top_k=200, chunks=3)),
+    (DS7B, dict(B=2, H_q=8, H_kv=8, lens=(1500, 65), top_k=100, chunks=4,
+                steps=0)),
+])
+def test_fused_score_select_matches_separate_calls(name, over):
+    step = _step()
+    wl = tsd_synth.make(tsd_synth.config(name, seed=140, **over), DEV)
+    a = step.StepBuffers(wl)
+    b = step.StepBuffers(wl)
+    a.scores.fill_(float("nan"))
+    b.scores.fill_(float("nan"))
+    step.score(wl, a)
+    step.select(wl, a)
+    step.score_select(wl, b)
+    torch.cuda.synchronize()
+    for x, y in ((a.row_lens, b.row_lens), (a.idx, b.idx), (a.count, b.count)):
+        assert torch.equal(x, y)
+    assert torch.equal(torch.nan_to_num(a.scores, nan=-7.0),
+                       torch.nan_to_num(b.scores, nan=-7.0))

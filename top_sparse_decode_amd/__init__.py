@@ -77,6 +77,9 @@ def _load():
         "topk_select": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, ctypes.c_int,
                                        ctypes.c_int, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
+        "sparse_index_topk": (ctypes.c_int, [ctypes.POINTER(ScoreArgs),
+                                             ctypes.c_int, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
         "sparse_gqa_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _P]),
         "lse_merge": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _P, _P, _P]),
@@ -97,7 +100,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTS = ("sparse_index_score", "topk_select_workspace_bytes", "topk_select",
+EXPORTS = ("sparse_index_score", "sparse_index_topk",
+           "topk_select_workspace_bytes", "topk_select",
            "sparse_gqa_decode", "lse_merge", "tsd_strerror", "tsd_abi_version",
            "tsd_sizeof_score_args", "tsd_sizeof_attn_args")
 
@@ -146,20 +150,9 @@ def _check(fn, rc):
 
 
 # --------------------------------------------------------------- entry points
-def sparse_index_score(mode, scores, page_table, seq_lens, num_pages, *,
-                       q=None, channel_idx=None, label_pool=None,
-                       index_q=None, index_w=None, index_k_pool=None,
-                       q_pos=None, rows_per_req=1, row_lens_out=None,
-                       stream=None):
-    """Score every cached token of every row into ``scores`` [rows, stride].
-
-    mode "ds":  q [B,H_q,128] bf16/fp16, channel_idx [H_kv,r] int32,
-                label_pool [slots,H_kv,r] (q's dtype); rows = B*H_kv.
-    mode "qsa": index_q [rows,H_i,128] fp8, index_w [rows,H_i] f32,
-                index_k_pool [slots,128] fp8, q_pos [rows] int32 or None;
-                rows = B*rows_per_req.
-    ``row_lens_out`` (int32 [rows], optional) receives each row's key count.
-    """
+def _score_args(mode, scores, page_table, seq_lens, num_pages, q, channel_idx,
+                label_pool, index_q, index_w, index_k_pool, q_pos,
+                rows_per_req, row_lens_out):
     _dev("scores", scores, torch.float32)
     _dev("page_table", page_table, torch.int32)
     _dev("seq_lens", seq_lens, torch.int32)
@@ -192,8 +185,48 @@ def sparse_index_score(mode, scores, page_table, seq_lens, num_pages, *,
         a.H_i, a.D_i = index_q.shape[1], index_q.shape[2]
     else:
         raise ValueError(f"unknown mode {mode!r}")
+    return a
+
+
+def sparse_index_score(mode, scores, page_table, seq_lens, num_pages, *,
+                       q=None, channel_idx=None, label_pool=None,
+                       index_q=None, index_w=None, index_k_pool=None,
+                       q_pos=None, rows_per_req=1, row_lens_out=None,
+                       stream=None):
+    """Score every cached token of every row into ``scores`` [rows, stride].
+
+    mode "ds":  q [B,H_q,128] bf16/fp16, channel_idx [H_kv,r] int32,
+                label_pool [slots,H_kv,r] (q's dtype); rows = B*H_kv.
+    mode "qsa": index_q [rows,H_i,128] fp8, index_w [rows,H_i] f32,
+                index_k_pool [slots,128] fp8, q_pos [rows] int32 or None;
+                rows = B*rows_per_req.
+    ``row_lens_out`` (int32 [rows], optional) receives each row's key count.
+    """
+    a = _score_args(mode, scores, page_table, seq_lens, num_pages, q,
+                    channel_idx, label_pool, index_q, index_w, index_k_pool,
+                    q_pos, rows_per_req, row_lens_out)
     _check("sparse_index_score", _lib.sparse_index_score(ctypes.byref(a),
                                                          _stream(stream)))
+
+
+def sparse_index_topk(mode, scores, page_table, seq_lens, num_pages, k, idx,
+                      count, workspace, row_lens_out, *, q=None,
+                      channel_idx=None, label_pool=None, index_q=None,
+                      index_w=None, index_k_pool=None, q_pos=None,
+                      rows_per_req=1, stream=None):
+    """sparse_index_score then topk_select on its scores (same results, fewer
+    passes). ``row_lens_out`` is required; ``workspace`` as for topk_select
+    with max_len = min(scores.shape[-1], page_table.shape[1] * 64)."""
+    a = _score_args(mode, scores, page_table, seq_lens, num_pages, q,
+                    channel_idx, label_pool, index_q, index_w, index_k_pool,
+                    q_pos, rows_per_req, row_lens_out)
+    _dev("idx", idx, torch.int32)
+    _dev("count", count, torch.int32)
+    _dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("sparse_index_topk", _lib.sparse_index_topk(
+        ctypes.byref(a), int(k), _ptr(idx), _ptr(count), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def topk_select_workspace_bytes(rows, max_len, k):

@@ -8,10 +8,25 @@
 
 namespace tsd {
 
-hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s);
+// hist1 (optional): first-digit top-k histograms [rows][4096] to accumulate
+// the scores into (the top-k workspace base); rows with n <= hist_k skip it.
+hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
+                           uint32_t* hist1 = nullptr, int hist_k = 0);
 hipError_t launch_ds_scan(const tsd_score_args& a, hipStream_t s);
 
 size_t topk_workspace(int rows, int max_len, int k);
+int topk_max_len();  // largest max_len topk_select accepts
+// The stages of launch_topk: clear the histograms, histogram digit 1, then
+// filter + resolve (the first two may be replaced by a scan that builds
+// the digit-1 histogram itself).
+hipError_t launch_topk_clear(void* ws, int rows, hipStream_t s);
+hipError_t launch_topk_hist1(const float* scores, int64_t stride, int rows,
+                             const int32_t* row_lens, int max_len, int k,
+                             void* ws, hipStream_t s);
+hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
+                              const int32_t* row_lens, int max_len, int k,
+                              int32_t* idx, int32_t* count, void* ws,
+                              hipStream_t s);
 hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        const int32_t* row_lens, int max_len, int k,
                        int32_t* idx, int32_t* count, void* ws,

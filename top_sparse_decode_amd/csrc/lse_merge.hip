@@ -3,47 +3,49 @@
 // with FP32 log-sum-exp normalisation):
 //   M = max_c lse_c, W = sum_c exp(lse_c - M),
 //   out = sum_c exp(lse_c - M) * o_c / W, out_lse = M + log W.
-// One wave per row; each lane owns D/64 (rounded up) output dimensions, the
-// per-chunk weights are computed once per lane from the row's LSEs.
+// One workgroup per (row, 128 output dimensions). The first wave turns the
+// row's C <= 64 LSEs (one per lane) into normalised weights in LDS; then
+// every thread owns one output dimension and issues its C loads of o_part
+// independently, so the whole merge is a single memory round trip.
 #include "device_common.h"
 #include "launch.h"
 
 namespace tsd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRowsPerBlock = kThreads / kWave;
+constexpr int kThreads = 128;
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
-    int rows, int C, int D, float* __restrict__ out,
-    float* __restrict__ out_lse) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const float* lse = lse_part + static_cast<int64_t>(row) * C;
-  // max over chunks (C <= 64: one chunk per lane)
-  const float mine = lane < C ? lse[lane] : -__builtin_inff();
-  const float M = wave_max(mine);
-  float* o = out + static_cast<int64_t>(row) * D;
-  if (M == -__builtin_inff()) {
-    for (int d = lane; d < D; d += kWave) o[d] = 0.f;
-    if (lane == 0 && out_lse) out_lse[row] = -__builtin_inff();
-    return;
-  }
-  const float wl = lane < C ? expf(mine - M) : 0.f;
-  const float W = wave_sum(wl);
-  const float inv = 1.f / W;
-  const float* op = o_part + static_cast<int64_t>(row) * C * D;
-  for (int d = lane; d < D; d += kWave) {
-    float acc = 0.f;
-    for (int c = 0; c < C; ++c) {
-      const float a = __shfl(wl, c, kWave);
-      if (a != 0.f) acc += a * op[static_cast<int64_t>(c) * D + d];
+    int C, int D, float* __restrict__ out, float* __restrict__ out_lse) {
+  __shared__ float w_s[64];
+  __shared__ float empty_s;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < kWave) {
+    const float* lse = lse_part + static_cast<int64_t>(row) * C;
+    const float mine = tid < C ? lse[tid] : -__builtin_inff();
+    const float M = wave_max(mine);
+    const bool empty = M == -__builtin_inff();
+    const float e = (!empty && tid < C) ? expf(mine - M) : 0.f;
+    const float W = wave_sum(e);
+    if (tid < C) w_s[tid] = empty ? 0.f : e / W;
+    if (tid == 0) {
+      empty_s = empty ? 1.f : 0.f;
+      if (out_lse && blockIdx.y == 0)
+        out_lse[row] = empty ? -__builtin_inff() : M + logf(W);
     }
-    o[d] = acc * inv;
   }
-  if (lane == 0 && out_lse) out_lse[row] = M + logf(W);
+  __syncthreads();
+  const int d = blockIdx.y * kThreads + tid;
+  if (d >= D) return;
+  const float* op = o_part + static_cast<int64_t>(row) * C * D + d;
+  float acc = 0.f;
+  if (empty_s == 0.f) {
+#pragma unroll 8
+    for (int c = 0; c < C; ++c) acc += w_s[c] * op[static_cast<int64_t>(c) * D];
+  }
+  out[static_cast<int64_t>(row) * D + d] = acc;
 }
 
 }  // namespace
@@ -52,9 +54,10 @@ hipError_t launch_lse_merge(const float* o_part, const float* lse_part,
                             int rows, int C, int D, float* out,
                             float* out_lse, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(lse_merge_kernel, dim3(blocks), dim3(kThreads), 0, s,
-                     o_part, lse_part, rows, C, D, out, out_lse);
+  dim3 grid(static_cast<uint32_t>(rows),
+            static_cast<uint32_t>((D + kThreads - 1) / kThreads));
+  hipLaunchKernelGGL(lse_merge_kernel, grid, dim3(kThreads), 0, s, o_part,
+                     lse_part, C, D, out, out_lse);
   return hipGetLastError();
 }
 

@@ -4,19 +4,22 @@
 // tokens, partial outputs merged by FP32 log-sum-exp; "Context parallelism
 // for QSA attention and the sparse indexer": a sparse GQA call per block).
 //
-// One workgroup per (request b, KV head g, chunk c) handles the G query
-// heads of the group over the chunk's run of the ascending selection list,
-// 64 tokens at a time:
-//   1. the tile's slots are resolved from the page table (an index outside
-//      [0, len) or a page outside [0, num_pages) is masked, never read);
-//   2. the 64 K rows and V rows are gathered into LDS with 16-byte loads
-//      (a token's row is contiguous in the token-major pool);
-//   3. lane j of each wave forms z = scale * q_h . Khat_j for its heads;
-//   4. an online softmax (base-2 internally) updates the running max and
-//      sum per head, the V page scale is folded into the probabilities;
-//   5. each thread accumulates one output dimension of up to 8 heads.
-// FP8 K/V are decoded by the hardware converter and scaled by their page's
-// f32 scale; BF16/FP16 are widened exactly. All arithmetic is FP32.
+// One workgroup (4 waves) per (request b, KV head g, chunk c) handles the G
+// query heads of the group over the chunk's run of the ascending selection
+// list, one tile of tokens at a time (128 tokens for FP8 rows, 64 for 16-bit
+// rows, so a tile's K and V fit LDS):
+//   1. the tile's slots are resolved from the page table; an index outside
+//      [0, len) or a page outside [0, num_pages) is masked and never read;
+//   2. the K and V rows are gathered into LDS with 16-byte loads (a token's
+//      row is contiguous in the token-major pool), masked rows zero-filled;
+//   3. logits S = Q K^T on MFMA: v_mfma_f32_16x16x32_{bf16,f16} with the
+//      group's query heads as M (padded to 16), 16 tokens as N and 32 head
+//      dims per instruction as K. FP8 K is widened exactly to the query's
+//      16-bit type, so the products are exact and accumulate in FP32;
+//   4. an online softmax (base 2) per head updates the running max and sum;
+//      the page's V scale is folded into the probabilities;
+//   5. O += P V on v_mfma_f32_16x16x4_f32 (FP32 operands, no rounding of P),
+//      each wave owning 32 output dimensions of every head.
 #include "device_common.h"
 #include "launch.h"
 
@@ -25,184 +28,209 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kD = 128;
-constexpr int kTile = 64;
-constexpr int kMaxG = 16;
-constexpr int kMaxRowBytes = kD * 2;
-constexpr int kRowPitch = kMaxRowBytes + 16;  // LDS pitch, breaks bank aliasing
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
 template <int ENC>
-struct Enc {
-  static constexpr int kBytes = ENC == TSD_FP8_E4M3 ? 1 : 2;
-  static constexpr int kPer16 = 16 / kBytes;  // elements per 16 bytes
+struct Tile {
+  static constexpr int kEsz = ENC == TSD_FP8_E4M3 ? 1 : 2;
+  static constexpr int kTokens = ENC == TSD_FP8_E4M3 ? 128 : 64;
+  static constexpr int kRowBytes = kD * kEsz;
+  static constexpr int kPitch = kRowBytes + 16;      // LDS row pitch (bytes)
+  static constexpr int kBlocks = kTokens / 16 / 4;   // 16-token blocks per wave
+  static constexpr int kZPitch = kTokens + 1;        // logits / probs pitch
 };
 
-// 16 bytes of a K or V row -> Enc<ENC>::kPer16 floats.
-template <int ENC>
-TSD_DEVICE void decode16(const uint4 x, float* out) {
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+// 8 consecutive 16-bit values (as raw bits) starting at element `e0` of a
+// K row in LDS, in the encoding of the query (QBF: bf16, else fp16).
+template <int ENC, bool QBF>
+TSD_DEVICE uint4 k8_as_q(const uint8_t* row, int e0) {
   if constexpr (ENC == TSD_FP8_E4M3) {
+    const uint2 raw = *reinterpret_cast<const uint2*>(row + e0);
+    float f[8];
+    fp8x4_to_f32(raw.x, f);
+    fp8x4_to_f32(raw.y, f + 4);
+    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) fp8x4_to_f32(w[e], out + 4 * e);
-  } else {
-    constexpr bool bf = ENC == TSD_BF16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      out[2 * e] = half_to_f32(static_cast<uint16_t>(w[e] & 0xFFFF), bf);
-      out[2 * e + 1] = half_to_f32(static_cast<uint16_t>(w[e] >> 16), bf);
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo, hi;
+      if constexpr (QBF) {  // exact: an E4M3 value fits bf16
+        lo = __float_as_uint(f[2 * i]) >> 16;
+        hi = __float_as_uint(f[2 * i + 1]) >> 16;
+      } else {              // exact: an E4M3 value fits fp16
+        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i]));
+        hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i + 1]));
+      }
+      w[i] = lo | (hi << 16);
     }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    return *reinterpret_cast<const uint4*>(row + 2 * e0);
+  }
+}
+
+template <bool QBF>
+TSD_DEVICE v4f mfma_qk(uint4 a, uint4 b, v4f c) {
+  if constexpr (QBF) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(
+        __builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
   }
 }
 
 template <int ENC>
-TSD_DEVICE float elem(const uint8_t* row, int d) {
+TSD_DEVICE float v_elem(const uint8_t* row, int d) {
   if constexpr (ENC == TSD_FP8_E4M3) {
-    const uint32_t b = row[d];
-    return fp8x2_to_f32<false>(b).x;
+    return fp8x2_to_f32<false>(static_cast<uint32_t>(row[d])).x;
   } else {
     const uint16_t h = reinterpret_cast<const uint16_t*>(row)[d];
     return half_to_f32(h, ENC == TSD_BF16);
   }
 }
 
-template <int ENC>
+template <int ENC, bool QBF>
 __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
-    const uint16_t* __restrict__ q, int q_enc, int H_q, int H_kv,
+    const uint16_t* __restrict__ q, int H_q, int H_kv,
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
-    const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, const int32_t* __restrict__ page_table,
-    int64_t pt_stride, const int32_t* __restrict__ seq_lens,
-    int64_t num_pages, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ count, int H_sel, int k, int C,
-    float softmax_scale, float* __restrict__ o_part,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ page_table, int64_t pt_stride,
+    const int32_t* __restrict__ seq_lens, int64_t num_pages,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
+    int H_sel, int k, int C, float softmax_scale, float* __restrict__ o_part,
     float* __restrict__ lse_part) {
-  __shared__ float q_s[kMaxG][kD];
-  __shared__ __align__(16) uint8_t k_s[kTile * kRowPitch];
-  __shared__ __align__(16) uint8_t v_s[kTile * kRowPitch];
-  __shared__ float p_s[kMaxG][kTile];
-  __shared__ int64_t slot_s[kTile];
-  __shared__ float ks_s[kTile], vs_s[kTile];
-  __shared__ float m_s[kMaxG], l_s[kMaxG], alpha_s[kMaxG];
+  using T = Tile<ENC>;
+  constexpr int NT = T::kTokens;
+  constexpr bool fp8 = ENC == TSD_FP8_E4M3;
+  __shared__ __align__(16) uint8_t k_s[NT * T::kPitch];
+  __shared__ __align__(16) uint8_t v_s[NT * T::kPitch];
+  __shared__ float zp_s[16 * T::kZPitch];  // logits, then probabilities
+  __shared__ int64_t slot_s[NT];
+  __shared__ float ks_s[NT], vs_s[NT];
+  __shared__ float m_s[16], l_s[16], alpha_s[16];
 
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = H_q / H_kv;
   const int h0 = g * G;
   const int srow = H_sel == 1 ? 0 : g;
-  int64_t m = count[static_cast<int64_t>(b) * H_sel + srow];
-  m = clamp_len(m, k);
+  const int64_t m = clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
   const int64_t lo = c * m / C, hi = (c + 1) * m / C;
   const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
   const int32_t* sel = idx + (static_cast<int64_t>(b) * H_sel + srow) * k;
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
-  constexpr bool fp8 = ENC == TSD_FP8_E4M3;
-  constexpr int esz = Enc<ENC>::kBytes;
-  constexpr int row_bytes = kD * esz;
   const float zscale = softmax_scale * kLog2e;
 
-  for (int i = tid; i < G * kD; i += kThreads) {
-    const int hh = i / kD, d = i % kD;
-    q_s[hh][d] = half_to_f32(q[(static_cast<int64_t>(b) * H_q + h0 + hh) * kD + d],
-                             q_enc == TSD_BF16);
+  const int col = lane & 15;   // MFMA row (A) / column (B) index
+  const int grp = lane >> 4;   // MFMA k-group / output row group
+
+  // Q operand: head `col` of the group, dims 32*grp .. 32*grp+31 in four
+  // 8-wide steps; rows past G are zero.
+  uint4 qa[4];
+  {
+    const bool live = col < G;
+    const uint4* qp = reinterpret_cast<const uint4*>(
+        q + (static_cast<int64_t>(b) * H_q + h0 + (live ? col : 0)) * kD +
+        32 * grp);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qa[s] = live ? qp[s] : make_uint4(0, 0, 0, 0);
   }
-  if (tid < G) {
+  if (tid < 16) {
     m_s[tid] = -__builtin_inff();
     l_s[tid] = 0.f;
   }
-  // output ownership: dimension d of heads hs, hs + 2, ...
-  const int od = tid % kD, hs = tid / kD;
-  float acc[kMaxG / 2];
-#pragma unroll
-  for (int i = 0; i < kMaxG / 2; ++i) acc[i] = 0.f;
-  __syncthreads();
+  // PV accumulators: O[4*grp + v][32*wave + 16*j + col]
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 
-  for (int64_t base = lo; base < hi; base += kTile) {
-    const int tn = static_cast<int>(hi - base < kTile ? hi - base : kTile);
-    // 1. resolve slots
-    if (tid < kTile) {
+  for (int64_t base = lo; base < hi; base += NT) {
+    const int tn = static_cast<int>(hi - base < NT ? hi - base : NT);
+    // 1. resolve slots and page scales
+    if (tid < NT) {
       int64_t slot = -1;
-      float ks = 0.f, vs = 0.f;
+      float ksc = 0.f, vsc = 0.f;
       if (tid < tn) {
         const int64_t t = sel[base + tid];
         if (t >= 0 && t < n) {
           const int32_t page = pt[t / kPage];
           if (page >= 0 && page < num_pages) {
             slot = static_cast<int64_t>(page) * kPage + t % kPage;
-            ks = fp8 ? k_scale[page] : 1.f;
-            vs = fp8 ? v_scale[page] : 1.f;
+            ksc = fp8 ? k_scale[page] : 1.f;
+            vsc = fp8 ? v_scale[page] : 1.f;
           }
         }
       }
       slot_s[tid] = slot;
-      ks_s[tid] = ks;
-      vs_s[tid] = vs;
+      ks_s[tid] = ksc;
+      vs_s[tid] = vsc;
     }
     __syncthreads();
-    // 2. gather K and V rows
-    constexpr int vec_per_row = row_bytes / 16;
-    for (int i = tid; i < kTile * vec_per_row; i += kThreads) {
-      const int j = i / vec_per_row, v = i % vec_per_row;
+    // 2. gather K and V rows (16-byte vectors; masked rows become zeros)
+    constexpr int vpr = T::kRowBytes / 16;
+#pragma unroll
+    for (int i = tid; i < NT * vpr; i += kThreads) {
+      const int j = i / vpr, v = i % vpr;
       const int64_t slot = slot_s[j];
+      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
       if (slot >= 0) {
-        const int64_t off = (slot * H_kv + g) * row_bytes + 16 * v;
-        *reinterpret_cast<uint4*>(k_s + j * kRowPitch + 16 * v) =
-            *reinterpret_cast<const uint4*>(k_pool + off);
-        *reinterpret_cast<uint4*>(v_s + j * kRowPitch + 16 * v) =
-            *reinterpret_cast<const uint4*>(v_pool + off);
+        const int64_t off = (slot * H_kv + g) * T::kRowBytes + 16 * v;
+        kx = *reinterpret_cast<const uint4*>(k_pool + off);
+        vx = *reinterpret_cast<const uint4*>(v_pool + off);
       }
+      *reinterpret_cast<uint4*>(k_s + j * T::kPitch + 16 * v) = kx;
+      *reinterpret_cast<uint4*>(v_s + j * T::kPitch + 16 * v) = vx;
     }
     __syncthreads();
-    // 3. logits: lane j, heads wave, wave + 4, ...
-    {
-      float z[kMaxG / 4];
+    // 3. logits on MFMA: wave owns tokens [16*kBlocks*wave, +16*kBlocks)
 #pragma unroll
-      for (int i = 0; i < kMaxG / 4; ++i) z[i] = 0.f;
-      const bool live = lane < tn && slot_s[lane] >= 0;
-      if (live) {
-        const uint8_t* kr = k_s + lane * kRowPitch;
-#pragma unroll 2
-        for (int off = 0; off < row_bytes; off += 16) {
-          constexpr int cnt = Enc<ENC>::kPer16;
-          float kv[cnt];
-          decode16<ENC>(*reinterpret_cast<const uint4*>(kr + off), kv);
-          const int d0 = off / esz;
+    for (int blk = 0; blk < T::kBlocks; ++blk) {
+      const int t0 = 16 * (T::kBlocks * wave + blk);
+      const uint8_t* krow = k_s + (t0 + col) * T::kPitch;
+      v4f s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int i = 0; i < kMaxG / 4; ++i) {
-            const int hh = wave + 4 * i;
-            if (hh < G) {
-              float s = 0.f;
+      for (int st = 0; st < 4; ++st)
+        s = mfma_qk<QBF>(qa[st], k8_as_q<ENC, QBF>(krow, 32 * grp + 8 * st), s);
+      const int t = t0 + col;
+      const bool live = t < tn && slot_s[t] >= 0;
+      const float f = zscale * ks_s[t];
 #pragma unroll
-              for (int e = 0; e < cnt; ++e) s += q_s[hh][d0 + e] * kv[e];
-              z[i] += s;
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < kMaxG / 4; ++i) {
-        const int hh = wave + 4 * i;
-        if (hh < G)
-          p_s[hh][lane] = live ? z[i] * ks_s[lane] * zscale : -__builtin_inff();
-      }
+      for (int v = 0; v < 4; ++v)
+        zp_s[(4 * grp + v) * T::kZPitch + t] = live ? s[v] * f : -__builtin_inff();
     }
     __syncthreads();
-    // 4. online softmax per head (base 2)
+    // 4. online softmax per head (base 2): wave handles heads wave + 4*i
 #pragma unroll
-    for (int i = 0; i < kMaxG / 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int hh = wave + 4 * i;
       if (hh < G) {
-        const float z = p_s[hh][lane];
-        const float tmax = wave_max(z);
+        float z[NT / 64];
+        float tmax = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < NT / 64; ++r) {
+          z[r] = zp_s[hh * T::kZPitch + lane + 64 * r];
+          tmax = fmaxf(tmax, z[r]);
+        }
+        tmax = wave_max(tmax);
         const float m_old = m_s[hh];
         const float m_new = fmaxf(m_old, tmax);
-        float p = 0.f, alpha = 1.f;
+        float psum = 0.f, alpha = 1.f;
         if (m_new != -__builtin_inff()) {
-          p = z == -__builtin_inff() ? 0.f : exp2f(z - m_new);
           alpha = m_old == -__builtin_inff() ? 0.f : exp2f(m_old - m_new);
+#pragma unroll
+          for (int r = 0; r < NT / 64; ++r) {
+            const float p = z[r] == -__builtin_inff() ? 0.f : exp2f(z[r] - m_new);
+            psum += p;
+            zp_s[hh * T::kZPitch + lane + 64 * r] = p * vs_s[lane + 64 * r];
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NT / 64; ++r)
+            zp_s[hh * T::kZPitch + lane + 64 * r] = 0.f;
         }
-        const float psum = wave_sum(p);
-        p_s[hh][lane] = p * vs_s[lane];
+        psum = wave_sum(psum);
         if (lane == 0) {
           m_s[hh] = m_new;
           l_s[hh] = l_s[hh] * alpha + psum;
@@ -211,34 +239,38 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       }
     }
     __syncthreads();
-    // 5. weighted values
-    {
+    // 5. O += P V on FP32 MFMA, 4 tokens per instruction
 #pragma unroll
-      for (int i = 0; i < kMaxG / 2; ++i) {
-        const int hh = hs + 2 * i;
-        if (hh < G) acc[i] *= alpha_s[hh];
-      }
-      for (int j = 0; j < tn; ++j) {
-        if (slot_s[j] < 0) continue;
-        const float v = elem<ENC>(v_s + j * kRowPitch, od);
-#pragma unroll
-        for (int i = 0; i < kMaxG / 2; ++i) {
-          const int hh = hs + 2 * i;
-          if (hh < G) acc[i] += p_s[hh][j] * v;
-        }
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int hh = 4 * grp + v;
+      const float a = hh < G ? alpha_s[hh] : 0.f;
+      acc[0][v] *= a;
+      acc[1][v] *= a;
+    }
+    const bool arow = col < G;
+#pragma unroll 4
+    for (int st = 0; st < NT / 4; ++st) {
+      const int t = 4 * st + grp;
+      const float pa = arow ? zp_s[col * T::kZPitch + t] : 0.f;
+      const uint8_t* vrow = v_s + t * T::kPitch;
+      const float b0 = v_elem<ENC>(vrow, 32 * wave + col);
+      const float b1 = v_elem<ENC>(vrow, 32 * wave + 16 + col);
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b1, acc[1], 0, 0, 0);
     }
     __syncthreads();
   }
 
-  // finalize
+  // finalize: O / l and lse (natural log)
 #pragma unroll
-  for (int i = 0; i < kMaxG / 2; ++i) {
-    const int hh = hs + 2 * i;
+  for (int v = 0; v < 4; ++v) {
+    const int hh = 4 * grp + v;
     if (hh < G) {
       const float l = l_s[hh];
-      const float o = l > 0.f ? acc[i] / l : 0.f;
-      o_part[((static_cast<int64_t>(b) * H_q + h0 + hh) * C + c) * kD + od] = o;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* o = o_part + ((static_cast<int64_t>(b) * H_q + h0 + hh) * C + c) * kD;
+      o[32 * wave + col] = acc[0][v] * inv;
+      o[32 * wave + 16 + col] = acc[1][v] * inv;
     }
   }
   if (tid < G) {
@@ -248,23 +280,32 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
   }
 }
 
-}  // namespace
-
-hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
+template <int ENC, bool QBF>
+hipError_t launch_enc(const tsd_attn_args& a, hipStream_t s) {
   dim3 grid(static_cast<uint32_t>(a.chunks), static_cast<uint32_t>(a.H_kv),
             static_cast<uint32_t>(a.B));
-  auto kern = a.kv_dtype == TSD_FP8_E4M3 ? sparse_gqa_kernel<TSD_FP8_E4M3>
-              : a.kv_dtype == TSD_BF16   ? sparse_gqa_kernel<TSD_BF16>
-                                         : sparse_gqa_kernel<TSD_FP16>;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s,
-                     static_cast<const uint16_t*>(a.q), a.q_dtype, a.H_q,
-                     a.H_kv, static_cast<const uint8_t*>(a.k_pool),
+  hipLaunchKernelGGL((sparse_gqa_kernel<ENC, QBF>), grid, dim3(kThreads), 0,
+                     s, static_cast<const uint16_t*>(a.q), a.H_q, a.H_kv,
+                     static_cast<const uint8_t*>(a.k_pool),
                      static_cast<const uint8_t*>(a.v_pool), a.k_scale,
                      a.v_scale, a.page_table, a.pt_stride, a.seq_lens,
                      a.num_pages, a.idx, a.count, a.H_sel, a.k, a.chunks,
                      a.softmax_scale, a.o_part, a.lse_part);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  const bool qbf = a.q_dtype == TSD_BF16;
+  switch (a.kv_dtype) {
+    case TSD_FP8_E4M3:
+      return qbf ? launch_enc<TSD_FP8_E4M3, true>(a, s)
+                 : launch_enc<TSD_FP8_E4M3, false>(a, s);
+    case TSD_BF16: return launch_enc<TSD_BF16, true>(a, s);
+    default: return launch_enc<TSD_FP16, false>(a, s);
+  }
 }
 
 }  // namespace tsd

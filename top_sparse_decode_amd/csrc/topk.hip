@@ -2,62 +2,90 @@
 // sglang PR #43527, Distributed QSA execution: an exact Top-K whose ties are
 // broken deterministically by token ID), output in ascending index order.
 //
-// Scores are mapped to order-preserving 32-bit keys (-0 folded onto +0).
-// The threshold key T (the k-th largest) is found by an MSD radix select in
-// three digit passes (11 + 11 + 10 bits); each pass builds per-workgroup LDS
-// histograms of the rows' elements that match the prefix found so far and
-// adds them into one global histogram per row with integer atomics, so the
-// counts -- and everything derived from them -- are deterministic. Then each
-// wave counts, over its 1024-element slice, the keys above T and equal to T;
-// a final pass turns those counts into exclusive offsets and every wave
-// compacts its slice in index order with 64-lane ballots: keys above T are
-// kept, keys equal to T are kept while their global tie rank is below the
-// number of ties still needed. Rows with n <= k keep every index.
-//
-// Every pass uses the same grid (row, 4096-element chunk), so a chunk's
-// scores are re-read by the same XCD and tend to hit its L2.
+// Scores map to order-preserving 32-bit keys (-0 folded onto +0). The k-th
+// largest key T is found by an MSD radix select over digits of 12, 10 and
+// 10 bits; all counts are integer atomics, so the result is deterministic.
+//   pass 1 (per 4096-element chunk): histogram of digit 1 -> H1[row].
+//   pass 2 (per chunk): with the threshold digit b1 known from H1, every key
+//          whose digit 1 is >= b1 (above it: certainly kept; equal: a
+//          candidate) is compacted in index order into the chunk's list of
+//          (index, key) pairs, and the candidates' digit 2 is histogrammed
+//          -> H2[row]. Typically 1-3% of a row survives.
+//   pass 3 (one workgroup per row): digit 3 of the list keys matching
+//          (b1, b2) is histogrammed in LDS, giving T and the number of ties
+//          at T to keep. The kept entries are then marked in an LDS bitmap
+//          over the row's indices (2^19 indices per segment) and a popcount
+//          scan of the bitmap writes them out in ascending order.
+// A chunk whose survivors overflow its list is read raw by pass 3 (the same
+// entries, recomputed from the scores), so the result never depends on the
+// list capacity. Rows with n <= k keep every index.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_digits.h"
 
 namespace tsd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWavesPerBlock = kThreads / kWave;
-constexpr int kSub = 1024;                      // elements per wave slice
-constexpr int kChunk = kSub * kWavesPerBlock;   // elements per workgroup
-constexpr int kBins1 = 2048, kBins2 = 2048, kBins3 = 1024;
-constexpr int kHistWords = kBins1 + kBins2 + kBins3;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kChunk = 4096;           // elements per pass-1/2 workgroup
+constexpr int kSub = kChunk / kWaves;  // elements per wave
+constexpr int kPerThread = kChunk / kThreads;
+constexpr int kListCap = 512;          // entries kept per chunk list
+constexpr int kB1 = kTopkB1, kB2 = kTopkB2, kB3 = kTopkB3;
+constexpr int kBins1 = kTopkBins1, kBins2 = kTopkBins2, kBins3 = kTopkBins3;
+constexpr int kShift1 = 32 - kB1, kShift2 = kB3;
+constexpr int kRT = 1024;              // pass-3 threads
+constexpr int kSegBits = 1 << 19;      // indices per bitmap segment
+constexpr int kSegWords = kSegBits / 32;
+constexpr int kMaxChunks = 4096;       // max_len <= 2^24
 
-// Workspace: the three histograms of every row ([rows][5120] words, cleared
-// by each call), then the slice counts ([rows][nsub][2] words, always
-// written before they are read).
-struct RowWs {
-  uint32_t* h1;
-  uint32_t* h2;
-  uint32_t* h3;
-  uint32_t* counts;  // [nsub][2]: keys > T, keys == T
+TSD_DEVICE uint32_t digit1(uint32_t key) { return topk_digit1(key); }
+TSD_DEVICE uint32_t digit2(uint32_t key) {
+  return (key >> kShift2) & (kBins2 - 1);
+}
+TSD_DEVICE uint32_t prefix12(uint32_t key) { return key >> kShift2; }
+
+struct Ws {
+  uint32_t* h1;      // [rows][kBins1]
+  uint32_t* h2;      // [rows][kBins2]
+  uint32_t* counts;  // [rows][nch]  survivors of each chunk
+  uint2* lists;      // [rows][nch][kListCap]  (index, key)
 };
 
-TSD_DEVICE RowWs row_ws(uint32_t* ws, int row, int nsub, int rows) {
-  uint32_t* base = ws + static_cast<int64_t>(row) * kHistWords;
-  uint32_t* cnt = ws + static_cast<int64_t>(rows) * kHistWords +
-                  static_cast<int64_t>(row) * 2 * nsub;
-  return {base, base + kBins1, base + kBins1 + kBins2, cnt};
+__host__ __device__ inline int64_t hist_words(int rows) {
+  return static_cast<int64_t>(rows) * (kBins1 + kBins2);
 }
 
-TSD_DEVICE int64_t row_len(const int32_t* row_lens, int row, int64_t cap) {
-  return clamp_len(row_lens[row], cap);
+__host__ __device__ inline int64_t list_offset_words(int rows, int nch) {
+  const int64_t off = hist_words(rows) + static_cast<int64_t>(rows) * nch;
+  return (off + 1) & ~static_cast<int64_t>(1);  // 8-byte alignment
 }
 
-// Block-wide exclusive scan of one value per thread (256 threads).
-TSD_DEVICE uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds4) {
+__host__ __device__ inline Ws make_ws(void* base, int rows, int nch) {
+  uint32_t* w = static_cast<uint32_t*>(base);
+  Ws ws;
+  ws.h1 = w;
+  ws.h2 = w + static_cast<int64_t>(rows) * kBins1;
+  ws.counts = w + hist_words(rows);
+  ws.lists = reinterpret_cast<uint2*>(w + list_offset_words(rows, nch));
+  return ws;
+}
+
+__host__ __device__ inline int64_t ws_words(int rows, int nch) {
+  return list_offset_words(rows, nch) +
+         2 * static_cast<int64_t>(rows) * nch * kListCap;
+}
+
+// Block-wide exclusive scan of one value per thread.
+template <int NT>
+TSD_DEVICE uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds) {
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const uint32_t inc = wave_inclusive_scan(v, lane);
-  if (lane == kWave - 1) lds4[w] = inc;
+  if (lane == kWave - 1) lds[w] = inc;
   __syncthreads();
   uint32_t before = 0;
-  for (int i = 0; i < w; ++i) before += lds4[i];
+  for (int i = 0; i < w; ++i) before += lds[i];
   __syncthreads();
   return before + inc - v;
 }
@@ -67,22 +95,25 @@ struct BinPick {
   uint32_t above;  // elements in bins strictly above `bin`
 };
 
-// Finds the bin holding the target-th largest element of an LDS histogram:
+// The bin holding the target-th largest element of an LDS histogram:
 // above(bin) < target <= above(bin) + hist[bin]. Threads own runs of bins
-// from the top down; a block scan of the run totals locates the run.
-template <int NB>
+// from the top down; a block scan of the run totals locates the run. If the
+// histogram holds fewer than `target` elements the result is bin 0 with
+// everything above it (the callers' bounds checks keep that harmless).
+template <int NB, int NT>
 TSD_DEVICE BinPick pick_bin(const uint32_t* hist, uint32_t target,
-                            uint32_t* lds4, BinPick* result) {
-  constexpr int per = NB / kThreads;
+                            uint32_t* lds, BinPick* result) {
+  constexpr int per = NB / NT;
   const int t = threadIdx.x;
-  const int top = NB - t * per;  // this thread owns bins [top-per, top)
+  const int top = NB - t * per;  // this thread owns bins [top - per, top)
   uint32_t s = 0;
 #pragma unroll
   for (int i = 1; i <= per; ++i) s += hist[top - i];
   if (t == 0) *result = BinPick{0u, 0u};
-  const uint32_t before = block_exclusive_scan(s, lds4);
+  const uint32_t before = block_exclusive_scan<NT>(s, lds);
   if (before < target && target <= before + s) {
     uint32_t acc = before;
+#pragma unroll
     for (int i = 1; i <= per; ++i) {
       const uint32_t h = hist[top - i];
       if (acc + h >= target) {
@@ -98,46 +129,25 @@ TSD_DEVICE BinPick pick_bin(const uint32_t* hist, uint32_t target,
   return r;
 }
 
-template <int NB>
-TSD_DEVICE void load_hist(uint32_t* lds, const uint32_t* g) {
-  for (int i = threadIdx.x; i < NB; i += kThreads) lds[i] = g[i];
+template <int NB, int NT>
+TSD_DEVICE void load_lds(uint32_t* lds, const uint32_t* g) {
+  for (int i = threadIdx.x; i < NB; i += NT) lds[i] = g[i];
   __syncthreads();
 }
 
-template <int NB>
-TSD_DEVICE void zero_hist(uint32_t* lds) {
-  for (int i = threadIdx.x; i < NB; i += kThreads) lds[i] = 0u;
+template <int NB, int NT>
+TSD_DEVICE void zero_lds(uint32_t* lds) {
+  for (int i = threadIdx.x; i < NB; i += NT) lds[i] = 0u;
   __syncthreads();
 }
 
-template <int NB>
+template <int NB, int NT>
 TSD_DEVICE void flush_hist(const uint32_t* lds, uint32_t* g) {
   __syncthreads();
-  for (int i = threadIdx.x; i < NB; i += kThreads) {
+  for (int i = threadIdx.x; i < NB; i += NT) {
     const uint32_t v = lds[i];
     if (v) atomicAdd(g + i, v);
   }
-}
-
-// Threshold state shared by the passes after the digits are known.
-struct Threshold {
-  uint32_t key;   // T
-  uint32_t need;  // ties at T to keep
-};
-
-TSD_DEVICE Threshold find_threshold(const RowWs& w, int k, uint32_t* hist,
-                                    uint32_t* lds4, BinPick* pick) {
-  load_hist<kBins1>(hist, w.h1);
-  const BinPick p1 = pick_bin<kBins1>(hist, k, lds4, pick);
-  load_hist<kBins2>(hist, w.h2);
-  const BinPick p2 = pick_bin<kBins2>(hist, k - p1.above, lds4, pick);
-  load_hist<kBins3>(hist, w.h3);
-  const BinPick p3 =
-      pick_bin<kBins3>(hist, k - p1.above - p2.above, lds4, pick);
-  Threshold th;
-  th.key = (p1.bin << 21) | (p2.bin << 10) | p3.bin;
-  th.need = k - p1.above - p2.above - p3.above;
-  return th;
 }
 
 __global__ __launch_bounds__(kThreads) void topk_clear_kernel(
@@ -146,212 +156,324 @@ __global__ __launch_bounds__(kThreads) void topk_clear_kernel(
   if (i < words) ws[i] = 0u;
 }
 
-// Pass 1: histogram of the top 11 key bits.
+// Pass 1: histogram of digit 1.
 __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
     const float* __restrict__ scores, int64_t stride,
-    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nsub,
-    uint32_t* __restrict__ ws) {
+    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
+    void* __restrict__ ws_base) {
   __shared__ uint32_t hist[kBins1];
   const int row = blockIdx.y;
-  const int64_t n = row_len(row_lens, row, cap);
+  const int64_t n = clamp_len(row_lens[row], cap);
   const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
   if (n <= k || start >= n) return;
-  const int64_t end = start + kChunk < n ? start + kChunk : n;
   const float* s = scores + row * stride;
-  zero_hist<kBins1>(hist);
-  for (int64_t i = start + threadIdx.x; i < end; i += kThreads)
-    atomicAdd(&hist[order_key(s[i]) >> 21], 1u);
-  flush_hist<kBins1>(hist, row_ws(ws, row, nsub, gridDim.y).h1);
+  float v[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t i = start + threadIdx.x + j * kThreads;
+    v[j] = i < n ? s[i] : 0.f;
+  }
+  zero_lds<kBins1, kThreads>(hist);
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t i = start + threadIdx.x + j * kThreads;
+    if (i < n) atomicAdd(&hist[digit1(order_key(v[j]))], 1u);
+  }
+  const Ws ws = make_ws(ws_base, gridDim.y, nch);
+  flush_hist<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
 }
 
-// Pass 2: histogram of key bits 20..10 among keys whose top digit is the
-// threshold digit.
-__global__ __launch_bounds__(kThreads) void topk_hist2_kernel(
+// Pass 2: survivors (digit 1 >= b1) compacted in index order into the
+// chunk's list; digit-2 histogram of the candidates (digit 1 == b1).
+__global__ __launch_bounds__(kThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t stride,
-    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nsub,
-    uint32_t* __restrict__ ws) {
+    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
+    void* __restrict__ ws_base) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t lds4[kWavesPerBlock];
+  __shared__ uint2 list_s[kWaves][kSub];
+  __shared__ uint32_t lds[kWaves];
+  __shared__ uint32_t wcount[kWaves];
   __shared__ BinPick pick;
   const int row = blockIdx.y;
-  const int64_t n = row_len(row_lens, row, cap);
+  const int64_t n = clamp_len(row_lens[row], cap);
   const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
   if (n <= k || start >= n) return;
-  const int64_t end = start + kChunk < n ? start + kChunk : n;
-  const RowWs w = row_ws(ws, row, nsub, gridDim.y);
-  load_hist<kBins1>(hist, w.h1);
-  const BinPick p1 = pick_bin<kBins1>(hist, k, lds4, &pick);
-  zero_hist<kBins2>(hist);
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const float* s = scores + row * stride;
-  for (int64_t i = start + threadIdx.x; i < end; i += kThreads) {
-    const uint32_t key = order_key(s[i]);
-    if ((key >> 21) == p1.bin) atomicAdd(&hist[(key >> 10) & 0x7FF], 1u);
+  const int64_t sub = start + static_cast<int64_t>(w) * kSub;
+  float v[kSub / kWave];
+#pragma unroll
+  for (int r = 0; r < kSub / kWave; ++r) {
+    const int64_t i = sub + r * kWave + lane;
+    v[r] = i < n ? s[i] : 0.f;
   }
-  flush_hist<kBins2>(hist, w.h2);
+  const Ws ws = make_ws(ws_base, gridDim.y, nch);
+  load_lds<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
+  const BinPick p1 = pick_bin<kBins1, kThreads>(hist, k, lds, &pick);
+  zero_lds<kBins2, kThreads>(hist);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int r = 0; r < kSub / kWave; ++r) {
+    const int64_t i = sub + r * kWave + lane;
+    const uint32_t key = order_key(v[r]);
+    const uint32_t d1 = digit1(key);
+    const bool keep = i < n && d1 >= p1.bin;
+    const uint64_t mask = __ballot(keep);
+    if (keep) {
+      const uint32_t pos = cnt + static_cast<uint32_t>(__popcll(mask & lt));
+      list_s[w][pos] = make_uint2(static_cast<uint32_t>(i), key);
+      if (d1 == p1.bin) atomicAdd(&hist[digit2(key)], 1u);
+    }
+    cnt += static_cast<uint32_t>(__popcll(mask));
+  }
+  if (lane == 0) wcount[w] = cnt;
+  __syncthreads();
+  uint32_t total = 0, off[kWaves];
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    off[i] = total;
+    total += wcount[i];
+  }
+  uint32_t* counts = ws.counts + static_cast<int64_t>(row) * nch;
+  if (threadIdx.x == 0) counts[blockIdx.x] = total;
+  if (total <= kListCap) {
+    uint2* dst = ws.lists +
+                 (static_cast<int64_t>(row) * nch + blockIdx.x) * kListCap;
+    for (uint32_t e = threadIdx.x; e < total; e += kThreads) {
+      int ww = 0;
+#pragma unroll
+      for (int i = 1; i < kWaves; ++i) ww += e >= off[i];
+      dst[e] = list_s[ww][e - off[ww]];
+    }
+  }
+  flush_hist<kBins2, kThreads>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
 }
 
-// Pass 3: histogram of the low 10 key bits among keys matching the first
-// 22 bits of the threshold.
-__global__ __launch_bounds__(kThreads) void topk_hist3_kernel(
-    const float* __restrict__ scores, int64_t stride,
-    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nsub,
-    uint32_t* __restrict__ ws) {
-  __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t lds4[kWavesPerBlock];
-  __shared__ BinPick pick;
-  const int row = blockIdx.y;
-  const int64_t n = row_len(row_lens, row, cap);
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
-  if (n <= k || start >= n) return;
-  const int64_t end = start + kChunk < n ? start + kChunk : n;
-  const RowWs w = row_ws(ws, row, nsub, gridDim.y);
-  load_hist<kBins1>(hist, w.h1);
-  const BinPick p1 = pick_bin<kBins1>(hist, k, lds4, &pick);
-  load_hist<kBins2>(hist, w.h2);
-  const BinPick p2 = pick_bin<kBins2>(hist, k - p1.above, lds4, &pick);
-  const uint32_t prefix = (p1.bin << 11) | p2.bin;
-  zero_hist<kBins3>(hist);
-  const float* s = scores + row * stride;
-  for (int64_t i = start + threadIdx.x; i < end; i += kThreads) {
-    const uint32_t key = order_key(s[i]);
-    if ((key >> 10) == prefix) atomicAdd(&hist[key & 0x3FF], 1u);
-  }
-  flush_hist<kBins3>(hist, w.h3);
-}
-
-// Pass 4: per 1024-element wave slice, the number of keys above T and equal
-// to T.
-__global__ __launch_bounds__(kThreads) void topk_count_kernel(
-    const float* __restrict__ scores, int64_t stride,
-    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nsub,
-    uint32_t* __restrict__ ws) {
-  __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t lds4[kWavesPerBlock];
-  __shared__ BinPick pick;
-  const int row = blockIdx.y;
-  const int64_t n = row_len(row_lens, row, cap);
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
-  if (n <= k || start >= n) return;
-  const RowWs w = row_ws(ws, row, nsub, gridDim.y);
-  const Threshold th = find_threshold(w, k, hist, lds4, &pick);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int sub = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t s0 = static_cast<int64_t>(sub) * kSub;
-  const int64_t s1 = s0 + kSub < n ? s0 + kSub : n;
-  const float* s = scores + row * stride;
-  uint32_t gt = 0, eq = 0;
-  for (int64_t i = s0 + lane; i < s1; i += kWave) {
-    const uint32_t key = order_key(s[i]);
-    gt += key > th.key;
-    eq += key == th.key;
-  }
-  gt = wave_sum_u32(gt);
-  eq = wave_sum_u32(eq);
-  if (lane == 0 && s0 < n) {
-    w.counts[2 * sub] = gt;
-    w.counts[2 * sub + 1] = eq;
+// Survivors of one chunk, 64 per round, in index order: from the chunk's
+// list, or recomputed from the raw scores when the list overflowed. Calls
+// f(index, key) for every survivor held by this lane.
+template <typename F>
+TSD_DEVICE void for_survivors(const Ws& ws, const float* s, int row, int nch,
+                              int c, uint32_t cnt, int64_t n, uint32_t b1,
+                              int lane, F&& f) {
+  if (cnt <= kListCap) {
+    const uint2* list =
+        ws.lists + (static_cast<int64_t>(row) * nch + c) * kListCap;
+    for (uint32_t e = lane; e < cnt; e += kWave) {
+      const uint2 en = list[e];
+      f(static_cast<int64_t>(en.x), en.y);
+    }
+  } else {
+    const int64_t i0 = static_cast<int64_t>(c) * kChunk;
+    const int64_t i1 = i0 + kChunk < n ? i0 + kChunk : n;
+    for (int64_t i = i0 + lane; i < i1; i += kWave) {
+      const uint32_t key = order_key(s[i]);
+      if (digit1(key) >= b1) f(i, key);
+    }
   }
 }
 
-// Pass 5: ordered compaction into idx (and the fast path for n <= k).
-__global__ __launch_bounds__(kThreads) void topk_write_kernel(
+// Pass 3: exact threshold and ordered output, one workgroup per row.
+__global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
-    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nsub,
-    const uint32_t* __restrict__ ws_in, int32_t* __restrict__ idx,
+    const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
+    void* __restrict__ ws_base, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
+  __shared__ uint32_t cnt_s[kMaxChunks];
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t lds4[kWavesPerBlock];
+  __shared__ uint32_t bits[kSegWords];
+  __shared__ uint32_t lds[kRT / kWave + 1];  // scan partials + running total
+  __shared__ uint32_t misc_s[2];
   __shared__ BinPick pick;
-  const int row = blockIdx.y;
-  const int64_t n = row_len(row_lens, row, cap);
-  const int lane = threadIdx.x & (kWave - 1);
-  const int sub = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid >> 6;
+  constexpr int kWavesR = kRT / kWave;
+  const int64_t n = clamp_len(row_lens[row], cap);
   int32_t* out = idx + static_cast<int64_t>(row) * k;
-  const int64_t m = n < k ? n : k;
-  if (blockIdx.x == 0) {
-    for (int64_t j = m + threadIdx.x; j < k; j += kThreads) out[j] = -1;
-    if (threadIdx.x == 0 && count) count[row] = static_cast<int32_t>(m);
-  }
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
-  if (start >= n) return;
-  const int64_t s0 = static_cast<int64_t>(sub) * kSub;
-  const int64_t s1 = s0 + kSub < n ? s0 + kSub : n;
   if (n <= k) {
-    for (int64_t i = s0 + lane; i < s1; i += kWave)
-      out[i] = static_cast<int32_t>(i);
+    for (int64_t j = tid; j < k; j += kRT)
+      out[j] = j < n ? static_cast<int32_t>(j) : -1;
+    if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
     return;
   }
-  uint32_t* ws = const_cast<uint32_t*>(ws_in);
-  const RowWs w = row_ws(ws, row, nsub, gridDim.y);
-  const Threshold th = find_threshold(w, k, hist, lds4, &pick);
-  if (s0 >= n) return;
-  // counts of the slices before this one
-  uint32_t gt_before = 0, eq_before = 0;
-  for (int j = lane; j < sub; j += kWave) {
-    gt_before += w.counts[2 * j];
-    eq_before += w.counts[2 * j + 1];
-  }
-  gt_before = wave_sum_u32(gt_before);
-  eq_before = wave_sum_u32(eq_before);
-  uint32_t tie_rank = eq_before;
-  uint32_t pos = gt_before + (eq_before < th.need ? eq_before : th.need);
+  const Ws ws = make_ws(ws_base, gridDim.x, nch);
+  const int nc = static_cast<int>((n + kChunk - 1) / kChunk);
   const float* s = scores + row * stride;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t base = s0; base < s1; base += kWave) {
-    const int64_t i = base + lane;
-    const uint32_t key = i < s1 ? order_key(s[i]) : 0u;
-    const bool in = i < s1;
-    const bool is_eq = in && key == th.key;
-    const uint64_t eq_mask = __ballot(is_eq);
-    const uint32_t my_tie =
-        tie_rank + static_cast<uint32_t>(__popcll(eq_mask & lt_mask));
-    const bool take = in && (key > th.key || (is_eq && my_tie < th.need));
-    const uint64_t take_mask = __ballot(take);
-    const uint32_t my_pos =
-        pos + static_cast<uint32_t>(__popcll(take_mask & lt_mask));
-    if (take && my_pos < static_cast<uint32_t>(k))
-      out[my_pos] = static_cast<int32_t>(i);
-    tie_rank += static_cast<uint32_t>(__popcll(eq_mask));
-    pos += static_cast<uint32_t>(__popcll(take_mask));
+  for (int c = tid; c < nc; c += kRT)
+    cnt_s[c] = ws.counts[static_cast<int64_t>(row) * nch + c];
+
+  load_lds<kBins1, kRT>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
+  const BinPick p1 = pick_bin<kBins1, kRT>(hist, k, lds, &pick);
+  load_lds<kBins2, kRT>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
+  const BinPick p2 = pick_bin<kBins2, kRT>(hist, k - p1.above, lds, &pick);
+  const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
+  const uint32_t need2 = k - p1.above - p2.above;
+
+  // digit 3 of the survivors that match the first 22 bits of T
+  zero_lds<kBins3, kRT>(hist);
+  for (int c = wave; c < nc; c += kWavesR)
+    for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
+                  [&](int64_t, uint32_t key) {
+                    if (prefix12(key) == pre)
+                      atomicAdd(&hist[key & (kBins3 - 1)], 1u);
+                  });
+  __syncthreads();
+  const BinPick p3 = pick_bin<kBins3, kRT>(hist, need2, lds, &pick);
+  const uint32_t T = (pre << kB3) | p3.bin;
+  const uint32_t need = need2 - p3.above;   // ties at T to keep
+  const uint32_t ties = hist[p3.bin];       // ties at T in the row
+  __syncthreads();
+
+  // With more ties than needed, the kept ties are those with index <= the
+  // index of the need-th tie, found segment by segment.
+  int64_t tie_cut = n;
+  if (ties > need) {
+    if (tid == 0) misc_s[0] = 0u;
+    uint32_t seen = 0;
+    for (int64_t seg = 0; seg < n && tie_cut == n; seg += kSegBits) {
+      zero_lds<kSegWords, kRT>(bits);
+      const int c0 = static_cast<int>(seg / kChunk);
+      const int c1 = static_cast<int>((seg + kSegBits) / kChunk) < nc
+                         ? static_cast<int>((seg + kSegBits) / kChunk)
+                         : nc;
+      for (int c = c0 + wave; c < c1; c += kWavesR)
+        for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
+                      [&](int64_t i, uint32_t key) {
+                        if (key == T) {
+                          const int64_t r = i - seg;
+                          atomicOr(&bits[r >> 5], 1u << (r & 31));
+                        }
+                      });
+      __syncthreads();
+      constexpr int wpt = kSegWords / kRT;
+      uint32_t pc = 0;
+#pragma unroll
+      for (int j = 0; j < wpt; ++j) pc += __popc(bits[tid * wpt + j]);
+      const uint32_t before = seen + block_exclusive_scan<kRT>(pc, lds);
+      if (before < need && need <= before + pc) {
+        uint32_t acc = before;
+        for (int j = 0; j < wpt; ++j) {
+          uint32_t word = bits[tid * wpt + j];
+          const uint32_t p = __popc(word);
+          if (acc + p >= need) {
+            for (uint32_t r = need - acc; r > 1; --r) word &= word - 1;
+            misc_s[1] = static_cast<uint32_t>(
+                (tid * wpt + j) * 32 + __ffs(word) - 1);
+            misc_s[0] = 1u;
+            break;
+          }
+          acc += p;
+        }
+      }
+      if (tid == kRT - 1) lds[kWavesR] = before + pc;  // ties so far
+      __syncthreads();
+      if (misc_s[0]) tie_cut = seg + misc_s[1];
+      seen = lds[kWavesR];
+      __syncthreads();
+    }
   }
+
+  // mark kept survivors segment by segment and write them in index order
+  uint32_t written = 0;
+  for (int64_t seg = 0; seg < n; seg += kSegBits) {
+    zero_lds<kSegWords, kRT>(bits);
+    const int c0 = static_cast<int>(seg / kChunk);
+    const int c1 = static_cast<int>((seg + kSegBits) / kChunk) < nc
+                       ? static_cast<int>((seg + kSegBits) / kChunk)
+                       : nc;
+    for (int c = c0 + wave; c < c1; c += kWavesR)
+      for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
+                    [&](int64_t i, uint32_t key) {
+                      if (key > T || (key == T && i <= tie_cut)) {
+                        const int64_t r = i - seg;
+                        atomicOr(&bits[r >> 5], 1u << (r & 31));
+                      }
+                    });
+    __syncthreads();
+    constexpr int wpt = kSegWords / kRT;
+    uint32_t wd[wpt], pc = 0;
+#pragma unroll
+    for (int j = 0; j < wpt; ++j) {
+      wd[j] = bits[tid * wpt + j];
+      pc += __popc(wd[j]);
+    }
+    uint32_t pos = written + block_exclusive_scan<kRT>(pc, lds);
+#pragma unroll
+    for (int j = 0; j < wpt; ++j) {
+      uint32_t word = wd[j];
+      while (word) {
+        const int b = __ffs(word) - 1;
+        word &= word - 1;
+        if (pos < static_cast<uint32_t>(k))
+          out[pos] = static_cast<int32_t>(seg + (tid * wpt + j) * 32 + b);
+        ++pos;
+      }
+    }
+    if (tid == kRT - 1) lds[kWavesR] = pos;
+    __syncthreads();
+    written = lds[kWavesR];
+    __syncthreads();
+  }
+  if (tid == 0 && count) count[row] = k;
 }
 
-int nsub_for(int max_len) { return (max_len + kSub - 1) / kSub; }
+int nch_for(int max_len) { return max_len > 0 ? (max_len + kChunk - 1) / kChunk : 1; }
 
 }  // namespace
 
 size_t topk_workspace(int rows, int max_len, int k) {
   (void)k;
-  const int nsub = nsub_for(max_len);
-  return static_cast<size_t>(rows) *
-         (kHistWords + 2 * static_cast<size_t>(nsub)) * sizeof(uint32_t);
+  return static_cast<size_t>(ws_words(rows, nch_for(max_len))) * sizeof(uint32_t);
+}
+
+int topk_max_len() { return kChunk * kMaxChunks; }
+
+hipError_t launch_topk_clear(void* ws, int rows, hipStream_t s) {
+  const int64_t words = hist_words(rows);
+  hipLaunchKernelGGL(topk_clear_kernel,
+                     dim3(static_cast<uint32_t>((words + kThreads - 1) / kThreads)),
+                     dim3(kThreads), 0, s, static_cast<uint32_t*>(ws), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_hist1(const float* scores, int64_t stride, int rows,
+                             const int32_t* row_lens, int max_len, int k,
+                             void* ws, hipStream_t s) {
+  const int nch = nch_for(max_len);
+  const int64_t cap = max_len < stride ? max_len : stride;
+  dim3 grid(static_cast<uint32_t>(nch), static_cast<uint32_t>(rows));
+  hipLaunchKernelGGL(topk_hist1_kernel, grid, dim3(kThreads), 0, s, scores,
+                     stride, row_lens, cap, k, nch, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
+                              const int32_t* row_lens, int max_len, int k,
+                              int32_t* idx, int32_t* count, void* ws,
+                              hipStream_t s) {
+  const int nch = nch_for(max_len);
+  const int64_t cap = max_len < stride ? max_len : stride;
+  dim3 grid(static_cast<uint32_t>(nch), static_cast<uint32_t>(rows));
+  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kThreads), 0, s, scores,
+                     stride, row_lens, cap, k, nch, ws);
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<uint32_t>(rows)),
+                     dim3(kRT), 0, s, scores, stride, row_lens, cap, k, nch,
+                     ws, idx, count);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        const int32_t* row_lens, int max_len, int k,
-                       int32_t* idx, int32_t* count, void* ws_v,
-                       hipStream_t s) {
+                       int32_t* idx, int32_t* count, void* ws, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int nsub = nsub_for(max_len);
-  const int64_t cap = max_len < stride ? max_len : stride;
-  uint32_t* ws = static_cast<uint32_t*>(ws_v);
-  const int64_t words = static_cast<int64_t>(rows) * kHistWords;
-  const int64_t cblocks = (words + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(topk_clear_kernel, dim3(static_cast<uint32_t>(cblocks)),
-                     dim3(kThreads), 0, s, ws, words);
-  const int chunks = max_len > 0 ? (max_len + kChunk - 1) / kChunk : 1;
-  dim3 grid(static_cast<uint32_t>(chunks), static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(topk_hist1_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nsub, ws);
-  hipLaunchKernelGGL(topk_hist2_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nsub, ws);
-  hipLaunchKernelGGL(topk_hist3_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nsub, ws);
-  hipLaunchKernelGGL(topk_count_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nsub, ws);
-  hipLaunchKernelGGL(topk_write_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nsub, ws, idx, count);
-  return hipGetLastError();
+  hipError_t e = launch_topk_clear(ws, rows, s);
+  if (e != hipSuccess) return e;
+  e = launch_topk_hist1(scores, stride, rows, row_lens, max_len, k, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_topk_finish(scores, stride, rows, row_lens, max_len, k, idx,
+                            count, ws, s);
 }
 
 }  // namespace tsd

@@ -65,7 +65,7 @@ int validate_topk(const float* scores, int64_t stride, int rows,
   if (rows < 0 || max_len < 0 || stride < 1 || stride < max_len)
     return TSD_E_SHAPE;
   if (k < 1 || k > TSD_MAX_TOPK) return TSD_E_K;
-  if (rows > 65535) return TSD_E_UNSUPPORTED;
+  if (rows > 65535 || max_len > tsd::topk_max_len()) return TSD_E_UNSUPPORTED;
   if (rows == 0) return TSD_OK;
   if (!scores || !row_lens || !idx) return TSD_E_NULL;
   if (!ws || ws_bytes < tsd::topk_workspace(rows, max_len, k))
@@ -124,6 +124,39 @@ int sparse_index_score(const tsd_score_args* a, hipStream_t stream) {
   if (a->mode == TSD_SCORE_DS_LABEL)
     return launch_status(tsd::launch_ds_scan(*a, stream));
   return launch_status(tsd::launch_qsa_scan(*a, stream));
+}
+
+int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
+                      int32_t* count, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  int rc = validate_score(a);
+  if (rc) return rc;
+  const int64_t rows64 = a->mode == TSD_SCORE_DS_LABEL
+                             ? static_cast<int64_t>(a->B) * a->H_kv
+                             : static_cast<int64_t>(a->B) * a->rows_per_req;
+  int64_t max_len = a->score_stride;
+  if (a->pt_stride * TSD_PAGE_SIZE < max_len) max_len = a->pt_stride * TSD_PAGE_SIZE;
+  if (rows64 > 65535 || max_len > tsd::topk_max_len()) return TSD_E_UNSUPPORTED;
+  const int rows = static_cast<int>(rows64);
+  rc = validate_topk(a->scores, a->score_stride, rows, a->row_lens_out,
+                     static_cast<int>(max_len), k, idx, ws, ws_bytes);
+  if (rc) return rc;
+  if (a->B == 0) return TSD_OK;
+  hipError_t e = tsd::launch_topk_clear(ws, rows, stream);
+  if (e != hipSuccess) return launch_status(e);
+  if (a->mode == TSD_SCORE_QSA_INDEX) {
+    e = tsd::launch_qsa_scan(*a, stream, static_cast<uint32_t*>(ws), k);
+  } else {
+    e = tsd::launch_ds_scan(*a, stream);
+    if (e == hipSuccess)
+      e = tsd::launch_topk_hist1(a->scores, a->score_stride, rows,
+                                 a->row_lens_out, static_cast<int>(max_len), k,
+                                 ws, stream);
+  }
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(tsd::launch_topk_finish(
+      a->scores, a->score_stride, rows, a->row_lens_out,
+      static_cast<int>(max_len), k, idx, count, ws, stream));
 }
 
 size_t topk_select_workspace_bytes(int rows, int max_len, int k) {

@@ -13,8 +13,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (lse_merge, sparse_gqa_decode, sparse_index_score, topk_select,
-               topk_select_workspace_bytes)
+from . import (lse_merge, sparse_gqa_decode, sparse_index_score,
+               sparse_index_topk, topk_select, topk_select_workspace_bytes)
 
 
 class StepBuffers:
@@ -63,6 +63,21 @@ def score(layer, bufs, stream=None):
                            row_lens_out=bufs.row_lens, stream=stream)
 
 
+def score_select(layer, bufs, stream=None):
+    """sparse_index_topk: the scores and the selection in one call."""
+    kw = dict(q_pos=layer.get("q_pos"), rows_per_req=layer.get("rows_per_req", 1),
+              stream=stream)
+    if layer["mode"] == "ds":
+        kw.update(q=layer["q"], channel_idx=layer["channel_idx"],
+                  label_pool=layer["label_pool"])
+    else:
+        kw.update(index_q=layer["index_q"], index_w=layer["index_w"],
+                  index_k_pool=layer.get("index_k_pool", layer.get("index_k")))
+    sparse_index_topk(layer["mode"], bufs.scores, layer["page_table"],
+                      layer["seq_lens"], layer["num_pages"], layer["top_k"],
+                      bufs.idx, bufs.count, bufs.ws, bufs.row_lens, **kw)
+
+
 def select(layer, bufs, stream=None):
     topk_select(bufs.scores, bufs.row_lens, layer["top_k"], bufs.max_len,
                 bufs.idx, bufs.count, bufs.ws, stream=stream)
@@ -82,24 +97,30 @@ def merge(layer, bufs, stream=None):
     lse_merge(bufs.o_part, bufs.lse_part, bufs.out, bufs.out_lse, stream=stream)
 
 
-def decode_step(layer, bufs, stream=None):
-    """All four calls, asynchronously on ``stream`` (default: current)."""
-    score(layer, bufs, stream)
-    select(layer, bufs, stream)
+def decode_step(layer, bufs, stream=None, fused=False):
+    """All four calls, asynchronously on ``stream`` (default: current);
+    ``fused`` replaces the first two with sparse_index_topk."""
+    if fused:
+        score_select(layer, bufs, stream)
+    else:
+        score(layer, bufs, stream)
+        select(layer, bufs, stream)
     attend(layer, bufs, stream)
     merge(layer, bufs, stream)
 
 
 class Plan:
-    """The four C calls of one layer with their arguments marshalled once.
+    """The C calls of one layer's step with their arguments marshalled once.
 
-    ``run(stream)`` issues sparse_index_score, topk_select, sparse_gqa_decode
-    and lse_merge straight through the C ABI on ``stream`` (a torch stream),
-    so repeated steps pay only the foreign-call cost. Per-call hooks
-    (``before``/``after``, called with the call's name) let a caller bracket
-    individual calls with events on the same stream."""
+    ``run(stream)`` issues sparse_index_score + topk_select (or, with
+    ``fused``, sparse_index_topk), then sparse_gqa_decode and lse_merge,
+    straight through the C ABI on ``stream`` (a torch stream), so repeated
+    steps pay only the foreign-call cost. Per-call hooks (``before`` /
+    ``after``, called with the call's name) let a caller bracket individual
+    calls with events on the same stream."""
 
-    def __init__(self, layer, bufs):
+    def __init__(self, layer, bufs, fused=False):
+        self.fused = fused
         import ctypes
 
         from . import (ABI_VERSION, PAGE_SIZE, AttnArgs, ScoreArgs,
@@ -159,18 +180,29 @@ class Plan:
         self._score_ref = ctypes.byref(self.score_args)
         self._attn_ref = ctypes.byref(self.attn_args)
 
-    def run(self, stream=None, before=None, after=None):
+    def calls(self, stream=None):
+        """(name, launch) pairs of this plan's C calls on ``stream``."""
         import ctypes
-
-        from . import TsdError
         s = stream if stream is not None else torch.cuda.current_stream()
         h = ctypes.c_void_p(s.cuda_stream)
         lib = self._lib
-        calls = (("sparse_index_score", lambda: lib.sparse_index_score(self._score_ref, h)),
-                 ("topk_select", lambda: lib.topk_select(*self.topk_args, h)),
-                 ("sparse_gqa_decode", lambda: lib.sparse_gqa_decode(self._attn_ref, h)),
-                 ("lse_merge", lambda: lib.lse_merge(*self.merge_args, h)))
-        for name, fn in calls:
+        if self.fused:
+            first = (("sparse_index_topk",
+                      lambda: lib.sparse_index_topk(
+                          self._score_ref, self.topk_args[5], self.topk_args[6],
+                          self.topk_args[7], self.topk_args[8],
+                          self.topk_args[9], h)),)
+        else:
+            first = (("sparse_index_score",
+                      lambda: lib.sparse_index_score(self._score_ref, h)),
+                     ("topk_select", lambda: lib.topk_select(*self.topk_args, h)))
+        return first + (
+            ("sparse_gqa_decode", lambda: lib.sparse_gqa_decode(self._attn_ref, h)),
+            ("lse_merge", lambda: lib.lse_merge(*self.merge_args, h)))
+
+    def run(self, stream=None, before=None, after=None):
+        from . import TsdError
+        for name, fn in self.calls(stream):
             if before:
                 before(name)
             rc = fn()
