@@ -73,6 +73,54 @@ def cpu_baseline(layer, seconds):
                       f"steps/s"}
 
 
+FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X
+
+
+def prefill_indexer(dev, passes, warmup):
+    """Chunked-prefill indexer: 2,048 causal query rows x 16 heads x 128 FP8
+    dims against 1,048,576 index keys (the tiled MFMA kernel), then per-row
+    top-2048 over the 2,048 x 1M scores, each timed over back-to-back passes
+    with HIP events."""
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd.step as step
+    cfg = tsd_synth.config("qsa_prefill_r2048_l1048576_k2048")
+    layer = tsd_synth.make(cfg, dev)
+    bufs = step.StepBuffers(layer)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n  # ms
+
+    ms_score = timed(lambda: step.score(layer, bufs), passes)
+    ms_topk = timed(lambda: step.select(layer, bufs), passes)
+    ms_fused = timed(lambda: step.score_select(layer, bufs), passes)
+    rows_n = (layer["q_pos"].to(torch.int64) + 1).clamp(max=cfg.L)
+    flops = 2.0 * cfg.H_i * cfg.D_i * float(rows_n.sum())
+    tflops = flops / (ms_score * 1e-3) / 1e12
+    del bufs, layer
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "rows": cfg.prefill_rows, "keys": cfg.L,
+            "index_heads": cfg.H_i, "top_k": cfg.top_k,
+            "flops_per_pass": flops, "score_ms": ms_score,
+            "topk_ms": ms_topk, "score_topk_fused_ms": ms_fused,
+            "roofline": {"bound": "mfma", "kernel": "sparse_index_score",
+                         "achieved": tflops, "peak": FP8_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": tflops / FP8_MFMA_PEAK_TFLOPS}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,6 +131,9 @@ def main():
                     help="layer replicas (0: enough for >= 1 GB between reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the chunked-prefill indexer measurement")
+    ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the step instead of eager "
                          "launches")
@@ -209,6 +260,10 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
+    if not args.no_prefill:
+        del plans, plans_sep, table, fused_plans, bufs, layers
+        torch.cuda.empty_cache()
+        line["prefill_indexer"] = prefill_indexer(dev, args.prefill_passes, 2)
     print(json.dumps(line), flush=True)
 
 

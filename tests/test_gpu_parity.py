@@ -312,3 +312,71 @@ def test_fused_score_select_matches_separate_calls(name, over):
         assert torch.equal(x, y)
     assert torch.equal(torch.nan_to_num(a.scores, nan=-7.0),
                        torch.nan_to_num(b.scores, nan=-7.0))
+
+
+def _prefill_case(lens, R, seed, stale_tail=False):
+    cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=200, chunks=4,
+                           seed=seed, stale_tail=stale_tail)
+    wl = tsd_synth.make(cfg, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    B = len(lens)
+    wl["index_q"] = tsd_synth.fp8_codes(
+        torch.randn((B * R, 16, 128), generator=g, device=DEV))
+    wl["index_w"] = torch.rand((B * R, 16), generator=g, device=DEV)
+    # positions spread over each request, including 0 and the last token
+    qp = []
+    for b, n in enumerate(lens):
+        p = torch.linspace(0, max(n - 1, 0), R).round().to(torch.int32)
+        qp.append(p)
+    wl["q_pos"] = torch.cat(qp).to(DEV)
+    wl["rows_per_req"] = R
+    return wl
+
+
+@pytest.mark.parametrize("lens,R", [((20000,), 130), ((5000, 70000), 64),
+                                    ((16384 + 77, 300), 65)])
+def test_prefill_kernel_matches_decode_scan_bitwise(lens, R):
+    """Rows of a request >= 64 take the tiled prefill kernel; the same rows
+    scored one at a time take the decode scan. Scores must be identical."""
+    import top_sparse_decode_amd as tsd
+    wl = _prefill_case(lens, R, seed=150)
+    B = len(lens)
+    stride = wl["page_table"].shape[1] * 64
+    tiled = torch.full((B * R, stride), float("nan"), device=DEV)
+    rl = torch.empty(B * R, dtype=torch.int32, device=DEV)
+    tsd.sparse_index_score("qsa", tiled, wl["page_table"], wl["seq_lens"],
+                           wl["num_pages"], index_q=wl["index_q"],
+                           index_w=wl["index_w"], index_k_pool=wl["index_k"],
+                           q_pos=wl["q_pos"], rows_per_req=R, row_lens_out=rl)
+    single = torch.full_like(tiled, float("nan"))
+    for b in range(B):
+        for r in range(R):
+            i = b * R + r
+            tsd.sparse_index_score(
+                "qsa", single[i:i + 1], wl["page_table"][b:b + 1],
+                wl["seq_lens"][b:b + 1], wl["num_pages"],
+                index_q=wl["index_q"][i:i + 1], index_w=wl["index_w"][i:i + 1],
+                index_k_pool=wl["index_k"], q_pos=wl["q_pos"][i:i + 1])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(tiled, nan=-3.0),
+                       torch.nan_to_num(single, nan=-3.0))
+    expect = torch.minimum(wl["q_pos"].long() + 1,
+                           wl["seq_lens"].long().repeat_interleave(R))
+    assert torch.equal(rl.long(), expect)
+
+
+def test_prefill_kernel_against_oracle():
+    wl = _prefill_case((3000, 1300), 70, seed=151, stale_tail=True)
+    step = _step()
+    bufs = step.StepBuffers(wl)
+    bufs.scores.fill_(float("nan"))
+    step.score_select(wl, bufs)
+    torch.cuda.synchronize()
+    h = tsd_synth.to_host(wl)
+    rl = oracle_row_lens(h)
+    np.testing.assert_array_equal(bufs.row_lens.cpu().numpy(), rl)
+    gs = bufs.scores.cpu().numpy()
+    check_scores(gs, oracle_scores(h), rl, score_tol("qsa"))
+    check_topk_identical(gs, rl, 200, bufs.idx.cpu().numpy(),
+                         bufs.count.cpu().numpy())

@@ -36,6 +36,12 @@ DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC]
 
 
+# Per-source extra flags. The index scans assume NaN-free scores (a NaN
+# score is outside the top-k contract), which lets max(0, x) compile to one
+# v_max_f32 instead of a NaN-quieting max followed by the max.
+EXTRA_FLAGS = {"score_qsa.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) +
                   glob.glob(os.path.join(CSRC, "*.cpp")))
@@ -43,7 +49,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + DEVICE_FLAGS + ["-c", src, "-o", obj]
+    cmd = ([hipcc()] + DEVICE_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), [])
+           + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stderr}")

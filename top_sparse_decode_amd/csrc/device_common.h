@@ -78,6 +78,25 @@ TSD_DEVICE uint32_t wave_inclusive_scan(uint32_t v, int lane) {
   return v;
 }
 
+// Reduce-scatter of four 16x16 MFMA tiles over the 4 lane groups of a wave:
+// lane l = 16*g + j holds part[i] = its partial for key j of tile i; the
+// result in lane l is sum over the 4 groups of part[g] at key j, i.e. the
+// total for key 16*g + j. Done with the gfx950 lane-swap instructions:
+// permlane32_swap(a, b) gives ([a_lo, b_lo], [a_hi, b_hi]) over the two
+// 32-lane halves, permlane16_swap the same over 16-lane rows.
+TSD_DEVICE float reduce_scatter4(const float part[4]) {
+  const auto r02 = __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+  const auto r13 = __builtin_amdgcn_permlane32_swap(
+      __float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+  // lower half: tiles 0 and 1 over groups {g, g+2}; upper half: tiles 2, 3
+  const float u = __uint_as_float(r02[0]) + __uint_as_float(r02[1]);
+  const float v = __uint_as_float(r13[0]) + __uint_as_float(r13[1]);
+  const auto r = __builtin_amdgcn_permlane16_swap(
+      __float_as_uint(u), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Clamp a device-side length to [0, cap].
 TSD_DEVICE int64_t clamp_len(int64_t n, int64_t cap) {
   return n < 0 ? 0 : (n > cap ? cap : n);

@@ -25,6 +25,8 @@ namespace tsd {
 namespace {
 
 constexpr int kWavesPerBlock = 4;
+// Requests with at least this many query rows use the tiled prefill kernel.
+constexpr int kPrefillMinRows = 64;
 constexpr int kPagesPerWave = 4;
 constexpr int kDi = 128;
 
@@ -140,20 +142,9 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
         part[i] = w[0] * fmaxf(d[0], 0.f) + w[1] * fmaxf(d[1], 0.f) +
                   w[2] * fmaxf(d[2], 0.f) + w[3] * fmaxf(d[3], 0.f);
       }
-      // Reduce-scatter over the 4 lane groups g = lane / 16: lane (g, j)
-      // ends with sum_g' part[g](g', j) = score of key 16*g + j of the page.
-      const int g = kb;
-      const bool upper = g >= 2;
-      const float x_send = upper ? part[0] : part[2];
-      const float y_send = upper ? part[1] : part[3];
-      const float x_recv = __shfl_xor(x_send, 32, kWave);
-      const float y_recv = __shfl_xor(y_send, 32, kWave);
-      const float u = (upper ? part[2] : part[0]) + x_recv;
-      const float v = (upper ? part[3] : part[1]) + y_recv;
-      const bool odd = g & 1;
-      const float s_send = odd ? u : v;
-      const float s_recv = __shfl_xor(s_send, 16, kWave);
-      const float sc = valid[pp] ? (odd ? v : u) + s_recv : -__builtin_inff();
+      // reduce-scatter over the 4 lane groups: lane l gets key l of the page
+      const float red = reduce_scatter4(part);
+      const float sc = valid[pp] ? red : -__builtin_inff();
 
       const int64_t t = (page0 + pp) * kPage + lane;
       if (t < n) {
@@ -175,12 +166,223 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Chunked-prefill indexer: many causal query rows of one request against the
+// request's index keys -- a dense FP8 contraction (rows x 16 heads) x keys x
+// 128 dims with the weighted-ReLU head reduction as epilogue.
+//
+// A workgroup of 8 waves owns 64 consecutive query rows of one request (8 per
+// wave, their index heads held as MFMA A operands in registers) and a span of
+// 16,384 keys. The span is walked in blocks of 256 keys (4 pages) that the
+// workgroup gathers once into LDS; every wave then takes each 16-key tile of
+// the block as a B operand and issues one MFMA per row, so each key byte read
+// from memory feeds 64 rows. The per-row epilogue and the cross-lane
+// reduce-scatter are the decode scan's, in the same order, so both kernels
+// produce bit-identical scores. Keys past a row's causal limit are computed
+// but never stored.
+constexpr int kPfWaves = 16;
+constexpr int kPfRowsPerWave = 4;
+constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // rows per workgroup
+constexpr int kPfBlockKeys = 256;                   // keys per LDS block
+constexpr int kPfSpanBlocks = 64;                   // blocks per workgroup
+constexpr int kPfSpan = kPfBlockKeys * kPfSpanBlocks;
+constexpr int kPfPitch = kDi + 16;                  // LDS bytes per key
+
+TSD_DEVICE v8i lds_row_slice(const uint8_t* row, int kb) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * kb);
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * kb);
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// Gathers the 256 keys of block `key0` (4 pages) into registers: thread tid
+// holds 16-byte vectors tid, tid + 512, ... of the block; keys at or past the
+// workgroup's longest row, or on an invalid page, read as zeros.
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfVecs = kPfBlockKeys * 8;  // 16-byte vectors per block
+constexpr int kPfVecsPerThread = (kPfVecs + kPfThreads - 1) / kPfThreads;
+struct PfStage {
+  uint4 x[kPfVecsPerThread];
+};
+
+TSD_DEVICE void pf_load(PfStage& st, const uint8_t* __restrict__ index_k,
+                        const int32_t* __restrict__ pt, int64_t num_pages,
+                        int64_t key0, int64_t n_wg, int tid) {
+#pragma unroll
+  for (int it = 0; it < kPfVecsPerThread; ++it) {
+    const int v = tid + it * kPfThreads;
+    const int64_t t = key0 + (v >> 3);
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (v < kPfVecs && t < n_wg) {
+      const int32_t page = pt[t / kPage];
+      if (page >= 0 && page < num_pages)
+        x = *reinterpret_cast<const uint4*>(
+            index_k + (static_cast<int64_t>(page) * kPage + t % kPage) * kDi +
+            16 * (v & 7));
+    }
+    st.x[it] = x;
+  }
+}
+
+TSD_DEVICE void pf_store(const PfStage& st, uint8_t* keys_s, int tid) {
+#pragma unroll
+  for (int it = 0; it < kPfVecsPerThread; ++it) {
+    const int v = tid + it * kPfThreads;
+    if (v < kPfVecs)
+      *reinterpret_cast<uint4*>(keys_s + (v >> 3) * kPfPitch + 16 * (v & 7)) =
+          st.x[it];
+  }
+}
+
+__global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
+    const uint8_t* __restrict__ index_q, const float* __restrict__ index_w,
+    const uint8_t* __restrict__ index_k, const int32_t* __restrict__ page_table,
+    int64_t pt_stride, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_pos, int64_t num_pages, int rows_per_req,
+    int groups_per_req, int H_i, float* __restrict__ scores,
+    int64_t score_stride, int32_t* __restrict__ row_lens_out) {
+  // two key blocks: the next one is gathered while the current one is used
+  __shared__ __align__(16) uint8_t keys_s[2][kPfBlockKeys * kPfPitch];
+  __shared__ int page_ok_s[2][kPfBlockKeys / kPage];
+  __shared__ int64_t nmax_s[kPfWaves];
+  // head weights of the workgroup's rows, 4 consecutive heads per 16 bytes
+  __shared__ __align__(16) float w_s[kPfRows][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.y / groups_per_req;
+  const int grp_in_req = blockIdx.y - b * groups_per_req;
+  const int row0 = grp_in_req * kPfRows;  // first row of the group within b
+  const int64_t span0 = static_cast<int64_t>(blockIdx.x) * kPfSpan;
+  const int64_t len = clamp_len(clamp_len(seq_lens[b], pt_stride * kPage),
+                                score_stride);
+  const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
+  const int col = lane & 15, kb = lane >> 4;
+
+  // this wave's rows: A operands and key counts; weights go to LDS
+  v8i qa[kPfRowsPerWave];
+  int32_t nr[kPfRowsPerWave];  // key count of each row (n <= 2^31 - 1)
+  int64_t nmax = 0;
+#pragma unroll
+  for (int i = 0; i < kPfRowsPerWave; ++i) {
+    const int rr = row0 + wave * kPfRowsPerWave + i;  // row within request
+    const bool ok = rr < rows_per_req;
+    const int64_t row = static_cast<int64_t>(b) * rows_per_req + rr;
+    int64_t n = 0;
+    if (ok) {
+      n = len;
+      if (q_pos) {
+        const int64_t p1 = static_cast<int64_t>(q_pos[row]) + 1;
+        n = p1 < n ? (p1 < 0 ? 0 : p1) : n;
+      }
+      if (blockIdx.x == 0 && lane == 0 && row_lens_out)
+        row_lens_out[row] = static_cast<int32_t>(n);
+    }
+    // n is the same in every lane; keep it scalar so row tests are uniform
+    nr[i] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n));
+    nmax = n > nmax ? n : nmax;
+    qa[i] = (ok && col < H_i)
+                ? load_row_slice(index_q + (row * H_i + col) * kDi, kb)
+                : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (lane < 16)
+      w_s[wave * kPfRowsPerWave + i][lane] =
+          (ok && lane < H_i) ? index_w[row * H_i + lane] : 0.f;
+  }
+  if (lane == 0) nmax_s[wave] = nmax;
+  __syncthreads();
+  int64_t n_wg = 0;
+#pragma unroll
+  for (int i = 0; i < kPfWaves; ++i) n_wg = nmax_s[i] > n_wg ? nmax_s[i] : n_wg;
+  int nblk = 0;  // blocks of this span below the longest row
+  while (nblk < kPfSpanBlocks &&
+         span0 + static_cast<int64_t>(nblk) * kPfBlockKeys < n_wg)
+    ++nblk;
+  if (nblk == 0) return;  // uniform over the workgroup
+
+  PfStage st;
+  pf_load(st, index_k, pt, num_pages, span0, n_wg, tid);
+  pf_store(st, keys_s[0], tid);
+  if (tid < kPfBlockKeys / kPage) {
+    const int64_t t = span0 + tid * kPage;
+    const int32_t page = t < len ? pt[t / kPage] : 0;
+    page_ok_s[0][tid] = page >= 0 && page < num_pages;
+  }
+  __syncthreads();
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int cur = blk & 1;
+    const int64_t key0 = span0 + static_cast<int64_t>(blk) * kPfBlockKeys;
+    const bool more = blk + 1 < nblk;
+    if (more)  // next block's loads stay in flight during this block's math
+      pf_load(st, index_k, pt, num_pages, key0 + kPfBlockKeys, n_wg, tid);
+    const uint8_t* ks = keys_s[cur];
+#pragma unroll 1
+    for (int g4 = 0; g4 < kPfBlockKeys / 64; ++g4) {
+      const int64_t t = key0 + 64 * g4 + lane;
+      v8i kt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kt[i] = lds_row_slice(ks + (64 * g4 + 16 * i + col) * kPfPitch, kb);
+      // as in the decode scan, a key on a page outside [0, num_pages)
+      // scores -inf (the 64-key group is exactly one page)
+      const bool page_ok = page_ok_s[cur][g4] != 0;
+      // Per row: the four tiles' MFMAs go out back to back into separate
+      // accumulators (a scheduling barrier keeps the reduction behind them),
+      // so one MFMA latency is exposed per row instead of one per tile. Every
+      // row computes every tile; causality is enforced by the store guard.
+#pragma unroll
+      for (int i = 0; i < kPfRowsPerWave; ++i) {
+        const float4 wv = *reinterpret_cast<const float4*>(
+            &w_s[wave * kPfRowsPerWave + i][4 * kb]);
+        v4f d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = mfma_fp8(qa[i], kt[j]);
+        __builtin_amdgcn_sched_barrier(0);
+        float part[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          part[j] = wv.x * fmaxf(d[j][0], 0.f) + wv.y * fmaxf(d[j][1], 0.f) +
+                    wv.z * fmaxf(d[j][2], 0.f) + wv.w * fmaxf(d[j][3], 0.f);
+        const float red = reduce_scatter4(part);
+        const float sc = page_ok ? red : -__builtin_inff();
+        if (t < nr[i]) {
+          const int64_t row = static_cast<int64_t>(b) * rows_per_req + row0 +
+                              wave * kPfRowsPerWave + i;
+          scores[row * score_stride + t] = sc;
+        }
+      }
+    }
+    if (more) {
+      pf_store(st, keys_s[cur ^ 1], tid);
+      if (tid < kPfBlockKeys / kPage) {
+        const int64_t t = key0 + kPfBlockKeys + tid * kPage;
+        const int32_t page = t < len ? pt[t / kPage] : 0;
+        page_ok_s[cur ^ 1][tid] = page >= 0 && page < num_pages;
+      }
+    }
+    __syncthreads();  // next block landed; this one is no longer read
+  }
+}
+
 }  // namespace
 
 hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                            uint32_t* hist1, int hist_k) {
   const int rows = a.B * a.rows_per_req;
   if (rows == 0) return hipSuccess;
+  if (!hist1 && a.rows_per_req >= kPrefillMinRows) {
+    const int64_t keys = a.pt_stride * kPage < a.score_stride
+                             ? a.pt_stride * kPage : a.score_stride;
+    const int groups = (a.rows_per_req + kPfRows - 1) / kPfRows;
+    dim3 grid(static_cast<uint32_t>((keys + kPfSpan - 1) / kPfSpan),
+              static_cast<uint32_t>(a.B * groups));
+    hipLaunchKernelGGL(qsa_prefill_kernel, grid, dim3(kPfWaves * kWave), 0, s,
+                       a.index_q, a.index_w, a.index_k_pool, a.page_table,
+                       a.pt_stride, a.seq_lens, a.q_pos, a.num_pages,
+                       a.rows_per_req, groups, a.H_i, a.scores, a.score_stride,
+                       a.row_lens_out);
+    return hipGetLastError();
+  }
   int64_t waves_per_row = (a.pt_stride + kPagesPerWave - 1) / kPagesPerWave;
   if (hist1)  // whole workgroups per row
     waves_per_row = (waves_per_row + kWavesPerBlock - 1) / kWavesPerBlock *

@@ -156,39 +156,45 @@ __global__ __launch_bounds__(kThreads) void topk_clear_kernel(
   if (i < words) ws[i] = 0u;
 }
 
-// Pass 1: histogram of digit 1.
+// Pass 1: histogram of digit 1; a workgroup covers `cpw` consecutive chunks.
 __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
-    void* __restrict__ ws_base) {
+    int cpw, void* __restrict__ ws_base) {
   __shared__ uint32_t hist[kBins1];
   const int row = blockIdx.y;
   const int64_t n = clamp_len(row_lens[row], cap);
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
+  const int64_t start = static_cast<int64_t>(blockIdx.x) * cpw * kChunk;
   if (n <= k || start >= n) return;
   const float* s = scores + row * stride;
-  float v[kPerThread];
-#pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t i = start + threadIdx.x + j * kThreads;
-    v[j] = i < n ? s[i] : 0.f;
-  }
   zero_lds<kBins1, kThreads>(hist);
+  for (int c = 0; c < cpw; ++c) {
+    const int64_t c0 = start + static_cast<int64_t>(c) * kChunk;
+    if (c0 >= n) break;
+    float v[kPerThread];
 #pragma unroll
-  for (int j = 0; j < kPerThread; ++j) {
-    const int64_t i = start + threadIdx.x + j * kThreads;
-    if (i < n) atomicAdd(&hist[digit1(order_key(v[j]))], 1u);
+    for (int j = 0; j < kPerThread; ++j) {
+      const int64_t i = c0 + threadIdx.x + j * kThreads;
+      v[j] = i < n ? s[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+      const int64_t i = c0 + threadIdx.x + j * kThreads;
+      if (i < n) atomicAdd(&hist[digit1(order_key(v[j]))], 1u);
+    }
   }
   const Ws ws = make_ws(ws_base, gridDim.y, nch);
   flush_hist<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
 }
 
-// Pass 2: survivors (digit 1 >= b1) compacted in index order into the
-// chunk's list; digit-2 histogram of the candidates (digit 1 == b1).
+// Pass 2: survivors (digit 1 >= b1) compacted in index order into each
+// chunk's list; digit-2 histogram of the candidates (digit 1 == b1). A
+// workgroup covers `cpw` consecutive chunks of one row, so the row's digit-1
+// threshold is resolved once per workgroup.
 __global__ __launch_bounds__(kThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
-    void* __restrict__ ws_base) {
+    int cpw, void* __restrict__ ws_base) {
   __shared__ uint32_t hist[kBins1];
   __shared__ uint2 list_s[kWaves][kSub];
   __shared__ uint32_t lds[kWaves];
@@ -196,56 +202,62 @@ __global__ __launch_bounds__(kThreads) void topk_filter_kernel(
   __shared__ BinPick pick;
   const int row = blockIdx.y;
   const int64_t n = clamp_len(row_lens[row], cap);
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * kChunk;
+  const int64_t start = static_cast<int64_t>(blockIdx.x) * cpw * kChunk;
   if (n <= k || start >= n) return;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
   const float* s = scores + row * stride;
-  const int64_t sub = start + static_cast<int64_t>(w) * kSub;
-  float v[kSub / kWave];
-#pragma unroll
-  for (int r = 0; r < kSub / kWave; ++r) {
-    const int64_t i = sub + r * kWave + lane;
-    v[r] = i < n ? s[i] : 0.f;
-  }
   const Ws ws = make_ws(ws_base, gridDim.y, nch);
   load_lds<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
   const BinPick p1 = pick_bin<kBins1, kThreads>(hist, k, lds, &pick);
   zero_lds<kBins2, kThreads>(hist);
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int r = 0; r < kSub / kWave; ++r) {
-    const int64_t i = sub + r * kWave + lane;
-    const uint32_t key = order_key(v[r]);
-    const uint32_t d1 = digit1(key);
-    const bool keep = i < n && d1 >= p1.bin;
-    const uint64_t mask = __ballot(keep);
-    if (keep) {
-      const uint32_t pos = cnt + static_cast<uint32_t>(__popcll(mask & lt));
-      list_s[w][pos] = make_uint2(static_cast<uint32_t>(i), key);
-      if (d1 == p1.bin) atomicAdd(&hist[digit2(key)], 1u);
-    }
-    cnt += static_cast<uint32_t>(__popcll(mask));
-  }
-  if (lane == 0) wcount[w] = cnt;
-  __syncthreads();
-  uint32_t total = 0, off[kWaves];
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    off[i] = total;
-    total += wcount[i];
-  }
   uint32_t* counts = ws.counts + static_cast<int64_t>(row) * nch;
-  if (threadIdx.x == 0) counts[blockIdx.x] = total;
-  if (total <= kListCap) {
-    uint2* dst = ws.lists +
-                 (static_cast<int64_t>(row) * nch + blockIdx.x) * kListCap;
-    for (uint32_t e = threadIdx.x; e < total; e += kThreads) {
-      int ww = 0;
+  for (int cc = 0; cc < cpw; ++cc) {
+    const int64_t c0 = start + static_cast<int64_t>(cc) * kChunk;
+    if (c0 >= n) break;  // uniform
+    const int chunk = static_cast<int>(c0 / kChunk);
+    const int64_t sub = c0 + static_cast<int64_t>(w) * kSub;
+    float v[kSub / kWave];
 #pragma unroll
-      for (int i = 1; i < kWaves; ++i) ww += e >= off[i];
-      dst[e] = list_s[ww][e - off[ww]];
+    for (int r = 0; r < kSub / kWave; ++r) {
+      const int64_t i = sub + r * kWave + lane;
+      v[r] = i < n ? s[i] : 0.f;
     }
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int r = 0; r < kSub / kWave; ++r) {
+      const int64_t i = sub + r * kWave + lane;
+      const uint32_t key = order_key(v[r]);
+      const uint32_t d1 = digit1(key);
+      const bool keep = i < n && d1 >= p1.bin;
+      const uint64_t mask = __ballot(keep);
+      if (keep) {
+        const uint32_t pos = cnt + static_cast<uint32_t>(__popcll(mask & lt));
+        list_s[w][pos] = make_uint2(static_cast<uint32_t>(i), key);
+        if (d1 == p1.bin) atomicAdd(&hist[digit2(key)], 1u);
+      }
+      cnt += static_cast<uint32_t>(__popcll(mask));
+    }
+    if (lane == 0) wcount[w] = cnt;
+    __syncthreads();
+    uint32_t total = 0, off[kWaves];
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+      off[i] = total;
+      total += wcount[i];
+    }
+    if (threadIdx.x == 0) counts[chunk] = total;
+    if (total <= kListCap) {
+      uint2* dst =
+          ws.lists + (static_cast<int64_t>(row) * nch + chunk) * kListCap;
+      for (uint32_t e = threadIdx.x; e < total; e += kThreads) {
+        int ww = 0;
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) ww += e >= off[i];
+        dst[e] = list_s[ww][e - off[ww]];
+      }
+    }
+    __syncthreads();  // list_s and wcount are reused by the next chunk
   }
   flush_hist<kBins2, kThreads>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
 }
@@ -438,14 +450,25 @@ hipError_t launch_topk_clear(void* ws, int rows, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Chunks per pass-1/2 workgroup: one, unless the launch would exceed about
+// 2,048 workgroups, in which case a workgroup takes consecutive chunks.
+int chunks_per_wg(int nch, int rows) {
+  const int64_t total = static_cast<int64_t>(nch) * rows;
+  int cpw = 1;
+  while (total / cpw > 2048 && cpw < nch) cpw *= 2;
+  return cpw;
+}
+
 hipError_t launch_topk_hist1(const float* scores, int64_t stride, int rows,
                              const int32_t* row_lens, int max_len, int k,
                              void* ws, hipStream_t s) {
   const int nch = nch_for(max_len);
+  const int cpw = chunks_per_wg(nch, rows);
   const int64_t cap = max_len < stride ? max_len : stride;
-  dim3 grid(static_cast<uint32_t>(nch), static_cast<uint32_t>(rows));
+  dim3 grid(static_cast<uint32_t>((nch + cpw - 1) / cpw),
+            static_cast<uint32_t>(rows));
   hipLaunchKernelGGL(topk_hist1_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nch, ws);
+                     stride, row_lens, cap, k, nch, cpw, ws);
   return hipGetLastError();
 }
 
@@ -454,10 +477,12 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s) {
   const int nch = nch_for(max_len);
+  const int cpw = chunks_per_wg(nch, rows);
   const int64_t cap = max_len < stride ? max_len : stride;
-  dim3 grid(static_cast<uint32_t>(nch), static_cast<uint32_t>(rows));
+  dim3 grid(static_cast<uint32_t>((nch + cpw - 1) / cpw),
+            static_cast<uint32_t>(rows));
   hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nch, ws);
+                     stride, row_lens, cap, k, nch, cpw, ws);
   hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<uint32_t>(rows)),
                      dim3(kRT), 0, s, scores, stride, row_lens, cap, k, nch,
                      ws, idx, count);

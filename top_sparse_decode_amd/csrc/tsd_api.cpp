@@ -53,6 +53,7 @@ int validate_score(const tsd_score_args* a) {
       return TSD_E_UNSUPPORTED;
     const int64_t rows = static_cast<int64_t>(a->B) * a->rows_per_req;
     if (rows > kMaxGrid) return TSD_E_UNSUPPORTED;
+    if (a->pt_stride * TSD_PAGE_SIZE > kMaxGrid) return TSD_E_UNSUPPORTED;
     const int64_t waves = rows * ((a->pt_stride + 3) / 4);
     if (waves / 4 + 1 > kMaxGrid) return TSD_E_UNSUPPORTED;
   }
@@ -144,8 +145,14 @@ int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
   if (a->B == 0) return TSD_OK;
   hipError_t e = tsd::launch_topk_clear(ws, rows, stream);
   if (e != hipSuccess) return launch_status(e);
-  if (a->mode == TSD_SCORE_QSA_INDEX) {
+  if (a->mode == TSD_SCORE_QSA_INDEX && a->rows_per_req < 64) {
     e = tsd::launch_qsa_scan(*a, stream, static_cast<uint32_t*>(ws), k);
+  } else if (a->mode == TSD_SCORE_QSA_INDEX) {  // prefill rows: tiled kernel
+    e = tsd::launch_qsa_scan(*a, stream);
+    if (e == hipSuccess)
+      e = tsd::launch_topk_hist1(a->scores, a->score_stride, rows,
+                                 a->row_lens_out, static_cast<int>(max_len), k,
+                                 ws, stream);
   } else {
     e = tsd::launch_ds_scan(*a, stream);
     if (e == hipSuccess)
