@@ -137,6 +137,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time HIP-graph replays of the step instead of eager "
                          "launches")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB "
+                         "once (a plain copy kernel of known size, to scale "
+                         "the HBM byte counters of a profiler run)")
     ap.add_argument("--unfused", action="store_true",
                     help="time sparse_index_score + topk_select instead of "
                          "sparse_index_topk")
@@ -155,6 +159,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = tsd_synth.config(args.workload)
     index_b, gather_b = model_bytes(cfg)
     R = args.replicas or max(1, math.ceil(1e9 / index_b))

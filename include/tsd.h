@@ -178,8 +178,10 @@ int sparse_index_score(const tsd_score_args *a, hipStream_t stream);
  *   idx      [rows, k] int32             count    [rows] int32 or NULL
  *   max_len  host-side bound on every row length (sizes the launch)
  *   ws       device workspace of at least topk_select_workspace_bytes()
- *            bytes, caller-owned; its contents need no initialisation and
- *            are scratch after the call (one workspace per concurrent call)
+ *            bytes, 16-byte aligned, caller-owned; its contents need no
+ *            initialisation and are scratch after the call (one workspace
+ *            per concurrent call); TSD_E_WORKSPACE if NULL, too small or
+ *            misaligned
  * 1 <= k <= 4096; 0 <= rows <= 65535; stride >= max_len >= 0;
  * max_len <= 16,777,216.
  * ------------------------------------------------------------------------ */

@@ -130,6 +130,7 @@ def test_topk_rejections():
     assert _topk(rows=-1) == E["SHAPE"]
     assert _topk(ws_bytes=16) == E["WORKSPACE"]
     assert _topk(ws=None) == E["WORKSPACE"]
+    assert _topk(ws=ctypes.c_void_p(0x10008)) == E["WORKSPACE"]  # misaligned
     assert _topk(scores=None) == E["NULL"]
     assert _topk(rows=70000) == E["UNSUPPORTED"]
     assert _topk(max_len=(1 << 24) + 1, stride=(1 << 24) + 1) == E["UNSUPPORTED"]
@@ -137,10 +138,11 @@ def test_topk_rejections():
 
 
 def _ws_words(rows, max_len):
-    # 4096- and 1024-bin histograms per row, one counter per 4096-element
-    # chunk, padding to 8 bytes, then a 512-entry list of 8-byte pairs per chunk
+    # 4096- and 1024-bin histograms per row, an 8-byte digit-1 record per
+    # row, one counter per 4096-element chunk, padding to 8 bytes, then a
+    # 512-entry list of 8-byte pairs per chunk
     nch = max(1, -(-max_len // 4096))
-    off = rows * 5120 + rows * nch
+    off = rows * 5120 + rows * 2 + rows * nch
     off += off & 1
     return off + 2 * rows * nch * 512
 

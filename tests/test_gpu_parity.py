@@ -190,6 +190,25 @@ def test_topk_large_rows_with_ties(n, k, levels):
     np.testing.assert_array_equal(gidx, ridx)
 
 
+def test_topk_ties_at_threshold_and_one_overflowing_chunk():
+    # row 0: a few ties planted at the k-th largest value of a normal row,
+    # more than are kept (every chunk list fits); row 1: one 4,096-element
+    # chunk holds 700 of the largest values (its list overflows and is read
+    # raw); row 2: 6,000 survivors spread evenly (a large fits-all case)
+    rng = np.random.default_rng(17)
+    n, k = 262144, 2048
+    s = rng.normal(size=(3, n)).astype(np.float32)
+    t = np.sort(s[0])[::-1][k - 1]
+    s[0, rng.choice(n, size=40, replace=False)] = t
+    s[1, 5 * 4096:5 * 4096 + 700] = 10.0 + rng.random(700).astype(np.float32)
+    s[2] = np.where(rng.random(n) < 6000 / n, 5.0, s[2]).astype(np.float32)
+    lens = [n, n, n]
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+
+
 def test_topk_row_lens_clamped_to_max_len():
     rng = np.random.default_rng(9)
     s = rng.normal(size=(2, 5000)).astype(np.float32)

@@ -68,13 +68,17 @@ TSD_DEVICE uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
-TSD_DEVICE uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+// Inclusive prefix sum across the 64 lanes of a wave, on DPP lane moves:
+// shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted past the
+// row start read 0), then lane 15 of rows 0 and 2 is added into rows 1 and
+// 3 (row_bcast:15) and lane 31 into rows 2 and 3 (row_bcast:31).
+TSD_DEVICE uint32_t wave_inclusive_scan(uint32_t v) {
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xf, 0xf, true));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xf, 0xf, true));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xf, 0xf, true));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xf, 0xf, true));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xa, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xc, 0xf, false));
   return v;
 }
 

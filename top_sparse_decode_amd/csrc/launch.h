@@ -8,10 +8,11 @@
 
 namespace tsd {
 
-// hist1 (optional): first-digit top-k histograms [rows][4096] to accumulate
-// the scores into (the top-k workspace base); rows with n <= hist_k skip it.
+// topk_ws (optional): a cleared top-k workspace for rows = B * rows_per_req;
+// the scan then also builds each row's digit-1 histograms (rows with
+// n <= hist_k skip them).
 hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
-                           uint32_t* hist1 = nullptr, int hist_k = 0);
+                           void* topk_ws = nullptr, int hist_k = 0);
 hipError_t launch_ds_scan(const tsd_score_args& a, hipStream_t s);
 
 size_t topk_workspace(int rows, int max_len, int k);

@@ -19,7 +19,7 @@
 // stores 256 contiguous bytes of scores.
 #include "device_common.h"
 #include "launch.h"
-#include "topk_digits.h"
+#include "topk_common.h"
 
 namespace tsd {
 namespace {
@@ -51,9 +51,10 @@ TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
 }
 
 // HIST: also accumulate the first top-k radix digit of every written score
-// into hist1[row][4096] (LDS-privatised per workgroup, flushed with integer
-// atomics). The launch then gives each row a multiple of 4 waves so that a
-// workgroup never spans two rows, and no wave leaves before the barriers.
+// into the top-k workspace's digit-1 histograms (LDS-privatised per
+// workgroup, flushed with integer atomics). The launch
+// gives each row a multiple of 4 waves so that a workgroup never spans two
+// rows, and no wave leaves before the barriers.
 template <bool HIST>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     const uint8_t* __restrict__ index_q, const float* __restrict__ index_w,
@@ -62,8 +63,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     const int32_t* __restrict__ q_pos, int64_t num_pages, int rows,
     int rows_per_req, int H_i, int waves_per_row, float* __restrict__ scores,
     int64_t score_stride, int32_t* __restrict__ row_lens_out,
-    uint32_t* __restrict__ hist1, int hist_k) {
-  __shared__ uint32_t hist_s[HIST ? kTopkBins1 : 1];
+    void* __restrict__ topk_base, int hist_k) {
+  __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   const int row = wave / waves_per_row;
@@ -157,11 +158,9 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
   if constexpr (HIST) {
     __syncthreads();
     if (do_hist) {  // uniform: the workgroup lies in one row
-      uint32_t* g = hist1 + static_cast<int64_t>(row) * kTopkBins1;
-      for (int i = threadIdx.x; i < kTopkBins1; i += kWavesPerBlock * kWave) {
-        const uint32_t c = hist_s[i];
-        if (c) atomicAdd(g + i, c);
-      }
+      const TopkWs ws = topk_ws(topk_base, rows, 0);
+      topk_flush_h1<kWavesPerBlock * kWave>(
+          hist_s, ws.h1 + static_cast<int64_t>(row) * kTopkBins1);
     }
   }
 }
@@ -367,10 +366,10 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
 }  // namespace
 
 hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
-                           uint32_t* hist1, int hist_k) {
+                           void* topk_ws, int hist_k) {
   const int rows = a.B * a.rows_per_req;
   if (rows == 0) return hipSuccess;
-  if (!hist1 && a.rows_per_req >= kPrefillMinRows) {
+  if (!topk_ws && a.rows_per_req >= kPrefillMinRows) {
     const int64_t keys = a.pt_stride * kPage < a.score_stride
                              ? a.pt_stride * kPage : a.score_stride;
     const int groups = (a.rows_per_req + kPfRows - 1) / kPfRows;
@@ -384,18 +383,18 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
     return hipGetLastError();
   }
   int64_t waves_per_row = (a.pt_stride + kPagesPerWave - 1) / kPagesPerWave;
-  if (hist1)  // whole workgroups per row
+  if (topk_ws)  // whole workgroups per row
     waves_per_row = (waves_per_row + kWavesPerBlock - 1) / kWavesPerBlock *
                     kWavesPerBlock;
   const int64_t waves = waves_per_row * rows;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  auto kern = hist1 ? qsa_scan_kernel<true> : qsa_scan_kernel<false>;
+  auto kern = topk_ws ? qsa_scan_kernel<true> : qsa_scan_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)),
                      dim3(kWavesPerBlock * kWave), 0, s, a.index_q, a.index_w,
                      a.index_k_pool, a.page_table, a.pt_stride, a.seq_lens,
                      a.q_pos, a.num_pages, rows, a.rows_per_req, a.H_i,
                      static_cast<int>(waves_per_row), a.scores,
-                     a.score_stride, a.row_lens_out, hist1, hist_k);
+                     a.score_stride, a.row_lens_out, topk_ws, hist_k);
   return hipGetLastError();
 }
 

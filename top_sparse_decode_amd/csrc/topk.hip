@@ -5,33 +5,38 @@
 // Scores map to order-preserving 32-bit keys (-0 folded onto +0). The k-th
 // largest key T is found by an MSD radix select over digits of 12, 10 and
 // 10 bits; all counts are integer atomics, so the result is deterministic.
-//   pass 1 (per 4096-element chunk): histogram of digit 1 -> H1[row].
-//   pass 2 (per chunk): with the threshold digit b1 known from H1, every key
-//          whose digit 1 is >= b1 (above it: certainly kept; equal: a
-//          candidate) is compacted in index order into the chunk's list of
-//          (index, key) pairs, and the candidates' digit 2 is histogrammed
-//          -> H2[row]. Typically 1-3% of a row survives.
-//   pass 3 (one workgroup per row): digit 3 of the list keys matching
-//          (b1, b2) is histogrammed in LDS, giving T and the number of ties
-//          at T to keep. The kept entries are then marked in an LDS bitmap
-//          over the row's indices (2^19 indices per segment) and a popcount
-//          scan of the bitmap writes them out in ascending order.
+//   pass 1 (per 4096-element chunk, or inside the index scan): histogram of
+//          digit 1 -> H1[row].
+//   pass 2 (4 chunks per workgroup pass): the threshold digit b1 (the bin
+//          holding the k-th largest) is resolved from H1; every key whose
+//          digit 1 is >= b1 (above it:
+//          certainly kept; equal: a candidate) is compacted in index order
+//          into the chunk's list of (index, key) pairs, and the candidates'
+//          digit 2 is histogrammed -> H2[row]. Typically 1-3% of a row
+//          survives.
+//   pass 3 (one workgroup per row): the chunk lists, concatenated in chunk
+//          order, are the row's survivors in ascending index order. Digit 3
+//          of those matching (b1, b2) gives T and the number of ties at T to
+//          keep; the kept entries are placed by ballots and one exchange of
+//          per-wave totals. When a list overflowed or the survivors exceed
+//          what the workgroup holds in registers, the survivors are instead
+//          marked in an LDS bitmap over the row's indices (2^19 indices per
+//          segment) and written out by a popcount scan.
 // A chunk whose survivors overflow its list is read raw by pass 3 (the same
 // entries, recomputed from the scores), so the result never depends on the
 // list capacity. Rows with n <= k keep every index.
 #include "device_common.h"
 #include "launch.h"
-#include "topk_digits.h"
+#include "topk_common.h"
 
 namespace tsd {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunk = 4096;           // elements per pass-1/2 workgroup
-constexpr int kSub = kChunk / kWaves;  // elements per wave
+constexpr int kChunk = kTopkChunk;     // elements per pass-1/2 workgroup
 constexpr int kPerThread = kChunk / kThreads;
-constexpr int kListCap = 512;          // entries kept per chunk list
+constexpr int kListCap = kTopkListCap;  // entries kept per chunk list
 constexpr int kB1 = kTopkB1, kB2 = kTopkB2, kB3 = kTopkB3;
 constexpr int kBins1 = kTopkBins1, kBins2 = kTopkBins2, kBins3 = kTopkBins3;
 constexpr int kShift1 = 32 - kB1, kShift2 = kB3;
@@ -39,6 +44,8 @@ constexpr int kRT = 1024;              // pass-3 threads
 constexpr int kSegBits = 1 << 19;      // indices per bitmap segment
 constexpr int kSegWords = kSegBits / 32;
 constexpr int kMaxChunks = 4096;       // max_len <= 2^24
+constexpr int kStage = 8192;           // survivors the pass-3 fast path holds
+constexpr int kPerLane = kStage / kRT; // survivors per lane on that path
 
 TSD_DEVICE uint32_t digit1(uint32_t key) { return topk_digit1(key); }
 TSD_DEVICE uint32_t digit2(uint32_t key) {
@@ -46,94 +53,7 @@ TSD_DEVICE uint32_t digit2(uint32_t key) {
 }
 TSD_DEVICE uint32_t prefix12(uint32_t key) { return key >> kShift2; }
 
-struct Ws {
-  uint32_t* h1;      // [rows][kBins1]
-  uint32_t* h2;      // [rows][kBins2]
-  uint32_t* counts;  // [rows][nch]  survivors of each chunk
-  uint2* lists;      // [rows][nch][kListCap]  (index, key)
-};
-
-__host__ __device__ inline int64_t hist_words(int rows) {
-  return static_cast<int64_t>(rows) * (kBins1 + kBins2);
-}
-
-__host__ __device__ inline int64_t list_offset_words(int rows, int nch) {
-  const int64_t off = hist_words(rows) + static_cast<int64_t>(rows) * nch;
-  return (off + 1) & ~static_cast<int64_t>(1);  // 8-byte alignment
-}
-
-__host__ __device__ inline Ws make_ws(void* base, int rows, int nch) {
-  uint32_t* w = static_cast<uint32_t*>(base);
-  Ws ws;
-  ws.h1 = w;
-  ws.h2 = w + static_cast<int64_t>(rows) * kBins1;
-  ws.counts = w + hist_words(rows);
-  ws.lists = reinterpret_cast<uint2*>(w + list_offset_words(rows, nch));
-  return ws;
-}
-
-__host__ __device__ inline int64_t ws_words(int rows, int nch) {
-  return list_offset_words(rows, nch) +
-         2 * static_cast<int64_t>(rows) * nch * kListCap;
-}
-
-// Block-wide exclusive scan of one value per thread.
-template <int NT>
-TSD_DEVICE uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_scan(v, lane);
-  if (lane == kWave - 1) lds[w] = inc;
-  __syncthreads();
-  uint32_t before = 0;
-  for (int i = 0; i < w; ++i) before += lds[i];
-  __syncthreads();
-  return before + inc - v;
-}
-
-struct BinPick {
-  uint32_t bin;
-  uint32_t above;  // elements in bins strictly above `bin`
-};
-
-// The bin holding the target-th largest element of an LDS histogram:
-// above(bin) < target <= above(bin) + hist[bin]. Threads own runs of bins
-// from the top down; a block scan of the run totals locates the run. If the
-// histogram holds fewer than `target` elements the result is bin 0 with
-// everything above it (the callers' bounds checks keep that harmless).
-template <int NB, int NT>
-TSD_DEVICE BinPick pick_bin(const uint32_t* hist, uint32_t target,
-                            uint32_t* lds, BinPick* result) {
-  constexpr int per = NB / NT;
-  const int t = threadIdx.x;
-  const int top = NB - t * per;  // this thread owns bins [top - per, top)
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 1; i <= per; ++i) s += hist[top - i];
-  if (t == 0) *result = BinPick{0u, 0u};
-  const uint32_t before = block_exclusive_scan<NT>(s, lds);
-  if (before < target && target <= before + s) {
-    uint32_t acc = before;
-#pragma unroll
-    for (int i = 1; i <= per; ++i) {
-      const uint32_t h = hist[top - i];
-      if (acc + h >= target) {
-        *result = BinPick{static_cast<uint32_t>(top - i), acc};
-        break;
-      }
-      acc += h;
-    }
-  }
-  __syncthreads();
-  const BinPick r = *result;
-  __syncthreads();
-  return r;
-}
-
-template <int NB, int NT>
-TSD_DEVICE void load_lds(uint32_t* lds, const uint32_t* g) {
-  for (int i = threadIdx.x; i < NB; i += NT) lds[i] = g[i];
-  __syncthreads();
-}
+using Ws = TopkWs;
 
 template <int NB, int NT>
 TSD_DEVICE void zero_lds(uint32_t* lds) {
@@ -161,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
     int cpw, void* __restrict__ ws_base) {
-  __shared__ uint32_t hist[kBins1];
+  __shared__ __align__(16) uint32_t hist[kBins1];
   const int row = blockIdx.y;
   const int64_t n = clamp_len(row_lens[row], cap);
   const int64_t start = static_cast<int64_t>(blockIdx.x) * cpw * kChunk;
@@ -183,83 +103,117 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
       if (i < n) atomicAdd(&hist[digit1(order_key(v[j]))], 1u);
     }
   }
-  const Ws ws = make_ws(ws_base, gridDim.y, nch);
-  flush_hist<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
+  const Ws ws = topk_ws(ws_base, gridDim.y, nch);
+  __syncthreads();
+  topk_flush_h1<kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
 }
 
 // Pass 2: survivors (digit 1 >= b1) compacted in index order into each
-// chunk's list; digit-2 histogram of the candidates (digit 1 == b1). A
-// workgroup covers `cpw` consecutive chunks of one row, so the row's digit-1
-// threshold is resolved once per workgroup.
-__global__ __launch_bounds__(kThreads) void topk_filter_kernel(
+// chunk's list; digit-2 histogram of the candidates (digit 1 == b1).
+// A workgroup of 16 waves takes 4 consecutive chunks per pass (4 waves per
+// chunk, 1,024 elements per wave) and `passes` consecutive passes. It
+// resolves b1 itself from the row's H1 (one uint4 run of 4 bins per thread,
+// read while its first scores are in flight); the row's first workgroup
+// records (b1, above) for pass 3. Survivors are counted by ballots, the
+// per-wave counts exchanged once, and each survivor stored straight to its
+// slot in the chunk's list.
+constexpr int kFT = 1024;                        // filter threads
+constexpr int kFW = kFT / kWave;                 // 16 waves
+constexpr int kFChunks = 4;                      // chunks per pass
+constexpr int kFWavesPerChunk = kFW / kFChunks;  // 4
+constexpr int kFSub = kChunk / kFWavesPerChunk;  // elements per wave
+constexpr int kFPer = kFSub / kWave;             // elements per lane
+
+__global__ __launch_bounds__(kFT) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
-    int cpw, void* __restrict__ ws_base) {
-  __shared__ uint32_t hist[kBins1];
-  __shared__ uint2 list_s[kWaves][kSub];
-  __shared__ uint32_t lds[kWaves];
-  __shared__ uint32_t wcount[kWaves];
+    int passes, void* __restrict__ ws_base) {
+  __shared__ uint32_t hist[kBins2];
+  __shared__ uint32_t wcount[kFW];
+  __shared__ uint32_t lds[kFW];
   __shared__ BinPick pick;
   const int row = blockIdx.y;
   const int64_t n = clamp_len(row_lens[row], cap);
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * cpw * kChunk;
+  constexpr int64_t kSpan = static_cast<int64_t>(kFChunks) * kChunk;
+  const int64_t start = static_cast<int64_t>(blockIdx.x) * passes * kSpan;
   if (n <= k || start >= n) return;
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
+  const int q = w / kFWavesPerChunk, wq = w % kFWavesPerChunk;
   const float* s = scores + row * stride;
-  const Ws ws = make_ws(ws_base, gridDim.y, nch);
-  load_lds<kBins1, kThreads>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
-  const BinPick p1 = pick_bin<kBins1, kThreads>(hist, k, lds, &pick);
-  zero_lds<kBins2, kThreads>(hist);
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  uint32_t* counts = ws.counts + static_cast<int64_t>(row) * nch;
-  for (int cc = 0; cc < cpw; ++cc) {
-    const int64_t c0 = start + static_cast<int64_t>(cc) * kChunk;
-    if (c0 >= n) break;  // uniform
-    const int chunk = static_cast<int>(c0 / kChunk);
-    const int64_t sub = c0 + static_cast<int64_t>(w) * kSub;
-    float v[kSub / kWave];
+  const Ws ws = topk_ws(ws_base, gridDim.y, nch);
+  float v[kFPer];
+  auto load_pass = [&](int64_t p0) {
+    const int64_t sub = p0 + static_cast<int64_t>(q) * kChunk +
+                        static_cast<int64_t>(wq) * kFSub;
 #pragma unroll
-    for (int r = 0; r < kSub / kWave; ++r) {
+    for (int r = 0; r < kFPer; ++r) {
       const int64_t i = sub + r * kWave + lane;
       v[r] = i < n ? s[i] : 0.f;
     }
+  };
+  load_pass(start);
+  // b1 from the row's H1: thread t holds bins [4096 - 4(t+1), 4096 - 4t)
+  constexpr int per1 = kBins1 / kFT;
+  static_assert(per1 == 4, "one uint4 run per thread");
+  const uint4 x = *reinterpret_cast<const uint4*>(
+      ws.h1 + static_cast<int64_t>(row) * kBins1 + (kBins1 - (tid + 1) * per1));
+  const uint32_t h[per1] = {x.w, x.z, x.y, x.x};  // from the top down
+  for (int i = tid; i < kBins2; i += kFT) hist[i] = 0u;  // ordered by the pick
+  const BinPick p1 =
+      pick_bin_runs<kBins1, kFT>(h, static_cast<uint32_t>(k), lds, &pick);
+  if (blockIdx.x == 0 && tid == 0) ws.sel[row] = make_uint2(p1.bin, p1.above);
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  uint32_t* counts = ws.counts + static_cast<int64_t>(row) * nch;
+  for (int ps = 0; ps < passes; ++ps) {
+    const int64_t p0 = start + static_cast<int64_t>(ps) * kSpan;
+    if (p0 >= n) break;  // uniform
+    const int64_t c0 = p0 + static_cast<int64_t>(q) * kChunk;
+    const int64_t sub = c0 + static_cast<int64_t>(wq) * kFSub;
+    uint32_t key[kFPer];
+    uint64_t mask[kFPer];
     uint32_t cnt = 0;
 #pragma unroll
-    for (int r = 0; r < kSub / kWave; ++r) {
+    for (int r = 0; r < kFPer; ++r) {
       const int64_t i = sub + r * kWave + lane;
-      const uint32_t key = order_key(v[r]);
-      const uint32_t d1 = digit1(key);
+      key[r] = order_key(v[r]);
+      const uint32_t d1 = digit1(key[r]);
       const bool keep = i < n && d1 >= p1.bin;
-      const uint64_t mask = __ballot(keep);
-      if (keep) {
-        const uint32_t pos = cnt + static_cast<uint32_t>(__popcll(mask & lt));
-        list_s[w][pos] = make_uint2(static_cast<uint32_t>(i), key);
-        if (d1 == p1.bin) atomicAdd(&hist[digit2(key)], 1u);
-      }
-      cnt += static_cast<uint32_t>(__popcll(mask));
+      mask[r] = __ballot(keep);
+      cnt += static_cast<uint32_t>(__popcll(mask[r]));
+      if (keep && d1 == p1.bin) atomicAdd(&hist[digit2(key[r])], 1u);
     }
+    if (ps + 1 < passes && p0 + kSpan < n) load_pass(p0 + kSpan);
     if (lane == 0) wcount[w] = cnt;
     __syncthreads();
-    uint32_t total = 0, off[kWaves];
+    uint32_t off = 0, total = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-      off[i] = total;
-      total += wcount[i];
+    for (int j = 0; j < kFWavesPerChunk; ++j) {
+      const uint32_t c = wcount[q * kFWavesPerChunk + j];
+      off += j < wq ? c : 0u;
+      total += c;
     }
-    if (threadIdx.x == 0) counts[chunk] = total;
-    if (total <= kListCap) {
-      uint2* dst =
-          ws.lists + (static_cast<int64_t>(row) * nch + chunk) * kListCap;
-      for (uint32_t e = threadIdx.x; e < total; e += kThreads) {
-        int ww = 0;
+    if (c0 < n) {  // uniform per wave; the chunk holds elements
+      const int chunk = static_cast<int>(c0 / kChunk);
+      if (wq == 0 && lane == 0) counts[chunk] = total;
+      if (total <= static_cast<uint32_t>(kListCap)) {
+        uint2* dst =
+            ws.lists + (static_cast<int64_t>(row) * nch + chunk) * kListCap;
+        uint32_t pos = off;
 #pragma unroll
-        for (int i = 1; i < kWaves; ++i) ww += e >= off[i];
-        dst[e] = list_s[ww][e - off[ww]];
+        for (int r = 0; r < kFPer; ++r) {
+          if ((mask[r] >> lane) & 1ull) {
+            const uint32_t pidx =
+                pos + static_cast<uint32_t>(__popcll(mask[r] & lt));
+            dst[pidx] = make_uint2(static_cast<uint32_t>(sub + r * kWave + lane),
+                                   key[r]);
+          }
+          pos += static_cast<uint32_t>(__popcll(mask[r]));
+        }
       }
     }
-    __syncthreads();  // list_s and wcount are reused by the next chunk
+    __syncthreads();  // wcount is reused by the next pass
   }
-  flush_hist<kBins2, kThreads>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
+  flush_hist<kBins2, kFT>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
 }
 
 // Survivors of one chunk, 64 per round, in index order: from the chunk's
@@ -287,13 +241,23 @@ TSD_DEVICE void for_survivors(const Ws& ws, const float* s, int row, int nch,
 }
 
 // Pass 3: exact threshold and ordered output, one workgroup per row.
+//
+// The chunk counts, b1 and H2 are read in one round trip; a block scan turns
+// the counts into each chunk's offset in the row's survivor sequence.
+// Fast path (no list overflowed, at most kStage survivors): every survivor
+// is loaded once into registers, wave-contiguously, while digit 3 is
+// histogrammed; after T is known one wave-total exchange gives each wave its
+// output base (kept = key > T, plus the first `need` ties in index order)
+// and ballots place the kept entries. Otherwise the survivors are re-read
+// per pass and ordered through an LDS bitmap over the row's indices.
 __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
     void* __restrict__ ws_base, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
-  __shared__ uint32_t cnt_s[kMaxChunks];
-  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t off_s[kMaxChunks + 1];  // survivors before chunk c
+  __shared__ __align__(16) uint32_t hist[kBins3];
+  __shared__ __align__(16) uint32_t hist2[kBins2];
   __shared__ uint32_t bits[kSegWords];
   __shared__ uint32_t lds[kRT / kWave + 1];  // scan partials + running total
   __shared__ uint32_t misc_s[2];
@@ -310,24 +274,121 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
     return;
   }
-  const Ws ws = make_ws(ws_base, gridDim.x, nch);
+  const Ws ws = topk_ws(ws_base, gridDim.x, nch);
   const int nc = static_cast<int>((n + kChunk - 1) / kChunk);
   const float* s = scores + row * stride;
-  for (int c = tid; c < nc; c += kRT)
-    cnt_s[c] = ws.counts[static_cast<int64_t>(row) * nch + c];
 
-  load_lds<kBins1, kRT>(hist, ws.h1 + static_cast<int64_t>(row) * kBins1);
-  const BinPick p1 = pick_bin<kBins1, kRT>(hist, k, lds, &pick);
-  load_lds<kBins2, kRT>(hist, ws.h2 + static_cast<int64_t>(row) * kBins2);
-  const BinPick p2 = pick_bin<kBins2, kRT>(hist, k - p1.above, lds, &pick);
+  // counts of this thread's run of chunks, b1 and H2, all loads in flight
+  constexpr int kCpt = kMaxChunks / kRT;
+  uint32_t cnt[kCpt];
+#pragma unroll
+  for (int j = 0; j < kCpt; ++j) {
+    const int c = tid * kCpt + j;
+    cnt[j] = c < nc ? ws.counts[static_cast<int64_t>(row) * nch + c] : 0u;
+  }
+  const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 1
+  const uint32_t* h2 = ws.h2 + static_cast<int64_t>(row) * kBins2;
+  for (int i = tid; i < kBins2; i += kRT) hist2[i] = h2[i];
+  uint32_t run = 0;
+  bool over = false;
+#pragma unroll
+  for (int j = 0; j < kCpt; ++j) {
+    run += cnt[j];
+    over |= cnt[j] > static_cast<uint32_t>(kListCap);
+  }
+  {
+    // the scan's first barrier also publishes hist2
+    uint32_t acc = block_exclusive_scan<kRT>(run, lds);
+#pragma unroll
+    for (int j = 0; j < kCpt; ++j) {
+      const int c = tid * kCpt + j;
+      if (c < nc) off_s[c] = acc;
+      acc += cnt[j];
+    }
+    if (tid == kRT - 1) off_s[nc] = acc;  // every chunk lies in some run
+  }
+  const bool any_over = __syncthreads_or(over);
+  const uint32_t total = off_s[nc];
+  const bool fast = !any_over && total <= static_cast<uint32_t>(kStage);
+
+  // Fast path: every survivor is loaded once, wave-contiguously, and its
+  // loads stay in flight while the digit-2 bin is resolved.
+  const uint32_t E = (total + kRT - 1) / kRT;  // rounds per lane
+  const uint32_t wbase = static_cast<uint32_t>(wave) * E * kWave;
+  uint2 v[kPerLane];
+  if (fast) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const uint32_t e = wbase + j * kWave + lane;
+      v[j] = make_uint2(0u, 0u);
+      if (static_cast<uint32_t>(j) < E && e < total) {
+        int lo = 0, hi = nc - 1;  // largest chunk with off_s[c] <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off_s[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        v[j] = ws.lists[(static_cast<int64_t>(row) * nch + lo) * kListCap +
+                        (e - off_s[lo])];
+      }
+    }
+  }
+  const BinPick p1{sel.x, sel.y};
+  for (int i = tid; i < kBins3; i += kRT) hist[i] = 0u;  // ordered by p2
+  const BinPick p2 = pick_bin<kBins2, kRT>(hist2, k - p1.above, lds, &pick);
   const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
   const uint32_t need2 = k - p1.above - p2.above;
 
-  // digit 3 of the survivors that match the first 22 bits of T
-  zero_lds<kBins3, kRT>(hist);
+  if (fast) {
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const uint32_t e = wbase + j * kWave + lane;
+      if (static_cast<uint32_t>(j) < E && e < total &&
+          prefix12(v[j].y) == pre)
+        atomicAdd(&hist[v[j].y & (kBins3 - 1)], 1u);
+    }
+    __syncthreads();
+    const BinPick p3 = pick_bin<kBins3, kRT>(hist, need2, lds, &pick);
+    const uint32_t T = (pre << kB3) | p3.bin;
+    const uint32_t need = need2 - p3.above;  // ties at T to keep
+    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    uint64_t mg[kPerLane], me[kPerLane];
+    uint32_t gtw = 0, eqw = 0;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const uint32_t e = wbase + j * kWave + lane;
+      const bool ok = static_cast<uint32_t>(j) < E && e < total;
+      mg[j] = __ballot(ok && v[j].y > T);
+      me[j] = __ballot(ok && v[j].y == T);
+      gtw += static_cast<uint32_t>(__popcll(mg[j]));
+      eqw += static_cast<uint32_t>(__popcll(me[j]));
+    }
+    // per-wave totals packed (ties << 16 | above); each is <= kStage
+    if (lane == 0) lds[wave] = (eqw << 16) | gtw;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int i = 0; i < wave; ++i) before += lds[i];
+    uint32_t eqr = before >> 16;  // ties in earlier waves
+    uint32_t pos = (before & 0xffffu) + (eqr < need ? eqr : need);
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const bool is_gt = (mg[j] >> lane) & 1ull;
+      const bool is_eq = (me[j] >> lane) & 1ull;
+      const uint32_t rank = eqr + static_cast<uint32_t>(__popcll(me[j] & lt));
+      const bool kept = is_gt || (is_eq && rank < need);
+      const uint64_t mk = __ballot(kept);
+      const uint32_t p = pos + static_cast<uint32_t>(__popcll(mk & lt));
+      if (kept && p < static_cast<uint32_t>(k)) out[p] = static_cast<int32_t>(v[j].x);
+      pos += static_cast<uint32_t>(__popcll(mk));
+      eqr += static_cast<uint32_t>(__popcll(me[j]));
+    }
+    if (tid == 0 && count) count[row] = k;
+    return;
+  }
+
+  // ---- general path: survivors re-read per pass, ordered by a bitmap ----
   for (int c = wave; c < nc; c += kWavesR)
-    for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
-                  [&](int64_t, uint32_t key) {
+    for_survivors(ws, s, row, nch, c, off_s[c + 1] - off_s[c], n, p1.bin,
+                  lane, [&](int64_t, uint32_t key) {
                     if (prefix12(key) == pre)
                       atomicAdd(&hist[key & (kBins3 - 1)], 1u);
                   });
@@ -351,8 +412,8 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
                          ? static_cast<int>((seg + kSegBits) / kChunk)
                          : nc;
       for (int c = c0 + wave; c < c1; c += kWavesR)
-        for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
-                      [&](int64_t i, uint32_t key) {
+        for_survivors(ws, s, row, nch, c, off_s[c + 1] - off_s[c], n, p1.bin,
+                      lane, [&](int64_t i, uint32_t key) {
                         if (key == T) {
                           const int64_t r = i - seg;
                           atomicOr(&bits[r >> 5], 1u << (r & 31));
@@ -396,8 +457,8 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
                        ? static_cast<int>((seg + kSegBits) / kChunk)
                        : nc;
     for (int c = c0 + wave; c < c1; c += kWavesR)
-      for_survivors(ws, s, row, nch, c, cnt_s[c], n, p1.bin, lane,
-                    [&](int64_t i, uint32_t key) {
+      for_survivors(ws, s, row, nch, c, off_s[c + 1] - off_s[c], n, p1.bin,
+                    lane, [&](int64_t i, uint32_t key) {
                       if (key > T || (key == T && i <= tie_cut)) {
                         const int64_t r = i - seg;
                         atomicOr(&bits[r >> 5], 1u << (r & 31));
@@ -437,13 +498,13 @@ int nch_for(int max_len) { return max_len > 0 ? (max_len + kChunk - 1) / kChunk 
 
 size_t topk_workspace(int rows, int max_len, int k) {
   (void)k;
-  return static_cast<size_t>(ws_words(rows, nch_for(max_len))) * sizeof(uint32_t);
+  return static_cast<size_t>(topk_ws_words(rows, nch_for(max_len))) * sizeof(uint32_t);
 }
 
 int topk_max_len() { return kChunk * kMaxChunks; }
 
 hipError_t launch_topk_clear(void* ws, int rows, hipStream_t s) {
-  const int64_t words = hist_words(rows);
+  const int64_t words = topk_clear_words(rows);
   hipLaunchKernelGGL(topk_clear_kernel,
                      dim3(static_cast<uint32_t>((words + kThreads - 1) / kThreads)),
                      dim3(kThreads), 0, s, static_cast<uint32_t*>(ws), words);
@@ -472,17 +533,27 @@ hipError_t launch_topk_hist1(const float* scores, int64_t stride, int rows,
   return hipGetLastError();
 }
 
+// Filter passes per workgroup: one, unless the launch would exceed about
+// 1,024 workgroups, in which case a workgroup takes consecutive passes.
+int filter_passes(int nch, int rows) {
+  const int64_t per_row = (nch + kFChunks - 1) / kFChunks;
+  int passes = 1;
+  while (per_row * rows / passes > 1024 && passes < per_row) passes *= 2;
+  return passes;
+}
+
 hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               const int32_t* row_lens, int max_len, int k,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s) {
   const int nch = nch_for(max_len);
-  const int cpw = chunks_per_wg(nch, rows);
+  const int passes = filter_passes(nch, rows);
   const int64_t cap = max_len < stride ? max_len : stride;
-  dim3 grid(static_cast<uint32_t>((nch + cpw - 1) / cpw),
+  const int64_t per_row = (nch + kFChunks - 1) / kFChunks;
+  dim3 grid(static_cast<uint32_t>((per_row + passes - 1) / passes),
             static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kThreads), 0, s, scores,
-                     stride, row_lens, cap, k, nch, cpw, ws);
+  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kFT), 0, s, scores,
+                     stride, row_lens, cap, k, nch, passes, ws);
   hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<uint32_t>(rows)),
                      dim3(kRT), 0, s, scores, stride, row_lens, cap, k, nch,
                      ws, idx, count);

@@ -69,7 +69,8 @@ int validate_topk(const float* scores, int64_t stride, int rows,
   if (rows > 65535 || max_len > tsd::topk_max_len()) return TSD_E_UNSUPPORTED;
   if (rows == 0) return TSD_OK;
   if (!scores || !row_lens || !idx) return TSD_E_NULL;
-  if (!ws || ws_bytes < tsd::topk_workspace(rows, max_len, k))
+  if (!ws || ws_bytes < tsd::topk_workspace(rows, max_len, k) ||
+      (reinterpret_cast<uintptr_t>(ws) & 15u) != 0)
     return TSD_E_WORKSPACE;
   return TSD_OK;
 }
@@ -146,7 +147,7 @@ int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
   hipError_t e = tsd::launch_topk_clear(ws, rows, stream);
   if (e != hipSuccess) return launch_status(e);
   if (a->mode == TSD_SCORE_QSA_INDEX && a->rows_per_req < 64) {
-    e = tsd::launch_qsa_scan(*a, stream, static_cast<uint32_t*>(ws), k);
+    e = tsd::launch_qsa_scan(*a, stream, ws, k);
   } else if (a->mode == TSD_SCORE_QSA_INDEX) {  // prefill rows: tiled kernel
     e = tsd::launch_qsa_scan(*a, stream);
     if (e == hipSuccess)
