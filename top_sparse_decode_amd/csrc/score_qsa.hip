@@ -11,8 +11,8 @@
 // single streaming pass over the index-K pages: every byte is read once, the
 // query rows sit in registers for the whole scan.
 //
-// Work split: one wave owns one query row and a run of consecutive 64-token
-// pages; a page is 4 MFMA tiles of 16 keys. The 16x16 f32 result gives lane
+// Work split: one wave owns one query row and a run of up to 32 consecutive
+// 64-token pages; a page is 4 MFMA tiles of 16 keys. The 16x16 f32 result gives lane
 // l the dots of key (l % 16) with heads 4*(l/16) .. 4*(l/16)+3; the weighted
 // ReLU is applied per lane and a 3-shuffle reduce-scatter over the 4 lane
 // groups leaves lane l with the full score of key l of the page, so a page
@@ -27,7 +27,6 @@ namespace {
 constexpr int kWavesPerBlock = 4;
 // Requests with at least this many query rows use the tiled prefill kernel.
 constexpr int kPrefillMinRows = 64;
-constexpr int kPagesPerWave = 4;
 constexpr int kDi = 128;
 
 // 32 bytes of one 128-byte FP8 row in the lane's MFMA operand slot:
@@ -50,12 +49,18 @@ TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
                                                           127, 0, 127);
 }
 
+// One wave owns G consecutive pages of one row. Pages are contracted in
+// pairs with the next pair's loads already in flight (two register sets of
+// 2 pages x 4 tiles), and the wave's scores are staged in LDS and stored in
+// one burst after its last page: stores issued between the loads would
+// share the loads' completion counter and stall every later wait on them.
+//
 // HIST: also accumulate the first top-k radix digit of every written score
 // into the top-k workspace's digit-1 histograms (LDS-privatised per
-// workgroup, flushed with integer atomics). The launch
-// gives each row a multiple of 4 waves so that a workgroup never spans two
-// rows, and no wave leaves before the barriers.
-template <bool HIST>
+// workgroup, flushed with integer atomics). The launch then gives each row
+// a multiple of 4 waves so that a workgroup never spans two rows, and no
+// wave leaves before the barriers.
+template <int G, bool HIST>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     const uint8_t* __restrict__ index_q, const float* __restrict__ index_w,
     const uint8_t* __restrict__ index_k, const int32_t* __restrict__ page_table,
@@ -64,9 +69,11 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     int rows_per_req, int H_i, int waves_per_row, float* __restrict__ scores,
     int64_t score_stride, int32_t* __restrict__ row_lens_out,
     void* __restrict__ topk_base, int hist_k) {
+  static_assert(G % 4 == 0, "pages per wave");
   __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  __shared__ float res_s[kWavesPerBlock][G * kPage];
+  const int lane = threadIdx.x & (kWave - 1), wl = threadIdx.x >> 6;
+  const int wave = blockIdx.x * kWavesPerBlock + wl;
   const int row = wave / waves_per_row;
   const bool row_ok = row < rows;
   const int chunk = wave - row * waves_per_row;
@@ -84,18 +91,23 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     if (chunk == 0 && lane == 0 && row_lens_out)
       row_lens_out[row] = static_cast<int32_t>(n);
   }
-  const int64_t page0 = static_cast<int64_t>(chunk) * kPagesPerWave;
-  const bool active = row_ok && page0 * kPage < n;
+  const int64_t page0 = static_cast<int64_t>(chunk) * G;
+  // live pages of this wave (the last one may be partial)
+  int npg = 0;
+  if (row_ok && page0 * kPage < n) {
+    const int64_t left = (n - page0 * kPage + kPage - 1) / kPage;
+    npg = left < G ? static_cast<int>(left) : G;
+  }
   const bool do_hist = HIST && row_ok && n > hist_k;
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kTopkBins1; i += kWavesPerBlock * kWave)
       hist_s[i] = 0u;
     __syncthreads();
   } else {
-    if (!active) return;
+    if (npg == 0) return;
   }
 
-  if (active) {
+  if (npg > 0) {
     const int col = lane & 15;  // MFMA row (head) for A, column (key) for B
     const int kb = lane >> 4;   // which 32-byte slice of the 128 dims
 
@@ -111,48 +123,68 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
       const int h = 4 * kb + v;
       w[v] = h < H_i ? index_w[static_cast<int64_t>(row) * H_i + h] : 0.f;
     }
-
     const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
-    float* out = scores + static_cast<int64_t>(row) * score_stride;
+    float* res = res_s[wl];
+    // every page id of the wave up front, lane l holding page l: a page-id
+    // load inside the loop would make each wait on it also drain the other
+    // register set's key loads (loads complete in order)
+    const int32_t my_page = lane < npg ? pt[page0 + lane] : -1;
 
-    // All of the wave's pages are requested before any is consumed (32 KB
-    // of loads in flight per wave), then each page is contracted and
-    // reduced.
-    v8i kt[kPagesPerWave][4];
-    bool live[kPagesPerWave], valid[kPagesPerWave];
+    // loads of wave pages j, j+1 (pages past npg or outside the pool load
+    // nothing; a page outside [0, num_pages) scores -inf)
+    auto load2 = [&](int j, v8i (&kt)[2][4], bool (&valid)[2]) {
 #pragma unroll
-    for (int pp = 0; pp < kPagesPerWave; ++pp) {
-      const int64_t p = page0 + pp;
-      live[pp] = p * kPage < n;
-      const int32_t page = live[pp] ? pt[p] : -1;
-      valid[pp] = page >= 0 && page < num_pages;
-      const uint8_t* base =
-          index_k + static_cast<int64_t>(valid[pp] ? page : 0) * kPage * kDi;
+      for (int d = 0; d < 2; ++d) {
+        const bool live = j + d < npg;
+        const int32_t page =
+            live ? __builtin_amdgcn_readlane(my_page, j + d) : -1;
+        valid[d] = page >= 0 && page < num_pages;
+        const uint8_t* base =
+            index_k + static_cast<int64_t>(valid[d] ? page : 0) * kPage * kDi;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        kt[pp][i] = valid[pp] ? load_row_slice(base + (16 * i + col) * kDi, kb)
+        for (int i = 0; i < 4; ++i)
+          kt[d][i] = valid[d] ? load_row_slice(base + (16 * i + col) * kDi, kb)
                               : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int pp = 0; pp < kPagesPerWave; ++pp) {
-      if (!live[pp]) break;
-      float part[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4f d = mfma_fp8(qa, kt[pp][i]);
-        part[i] = w[0] * fmaxf(d[0], 0.f) + w[1] * fmaxf(d[1], 0.f) +
-                  w[2] * fmaxf(d[2], 0.f) + w[3] * fmaxf(d[3], 0.f);
       }
-      // reduce-scatter over the 4 lane groups: lane l gets key l of the page
-      const float red = reduce_scatter4(part);
-      const float sc = valid[pp] ? red : -__builtin_inff();
-
-      const int64_t t = (page0 + pp) * kPage + lane;
-      if (t < n) {
-        out[t] = sc;
-        if (do_hist) atomicAdd(&hist_s[topk_digit1(order_key(sc))], 1u);
+    };
+    auto score2 = [&](int j, const v8i (&kt)[2][4], const bool (&valid)[2]) {
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        if (j + d >= npg) break;  // uniform
+        float part[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const v4f dd = mfma_fp8(qa, kt[d][i]);
+          part[i] = w[0] * fmaxf(dd[0], 0.f) + w[1] * fmaxf(dd[1], 0.f) +
+                    w[2] * fmaxf(dd[2], 0.f) + w[3] * fmaxf(dd[3], 0.f);
+        }
+        // reduce-scatter over the 4 lane groups: lane l gets key l
+        const float red = reduce_scatter4(part);
+        const float sc = valid[d] ? red : -__builtin_inff();
+        res[(j + d) * kPage + lane] = sc;
+        const int64_t t = (page0 + j + d) * kPage + lane;
+        if (do_hist && t < n)
+          atomicAdd(&hist_s[topk_digit1(order_key(sc))], 1u);
       }
+    };
+    v8i ka[2][4], kc[2][4];
+    bool va[2], vc[2];
+    load2(0, ka, va);
+#pragma unroll 1
+    for (int j = 0; j < npg; j += 4) {
+      load2(j + 2, kc, vc);
+      score2(j, ka, va);
+      if (j + 4 < npg) load2(j + 4, ka, va);
+      score2(j + 2, kc, vc);
     }
+    // the wave's scores are contiguous in the row: one burst of stores
+    // (LDS order within the wave makes every lane's staged score visible)
+    __builtin_amdgcn_wave_barrier();
+    float* out = scores + static_cast<int64_t>(row) * score_stride + page0 * kPage;
+    const int64_t cnt64 = n - page0 * kPage;
+    const int cnt = cnt64 < npg * kPage ? static_cast<int>(cnt64) : npg * kPage;
+#pragma unroll 4
+    for (int e = lane; e < cnt; e += kWave) out[e] = res[e];
   }
 
   if constexpr (HIST) {
@@ -382,13 +414,27 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                        a.row_lens_out);
     return hipGetLastError();
   }
-  int64_t waves_per_row = (a.pt_stride + kPagesPerWave - 1) / kPagesPerWave;
+  // pages per wave: the most (up to 32) that still gives >= 1,024 waves
+  const int64_t pages = a.pt_stride * static_cast<int64_t>(rows);
+  int G = 32;
+  while (G > 4 && pages / G < 1024) G /= 2;
+  int64_t waves_per_row = (a.pt_stride + G - 1) / G;
   if (topk_ws)  // whole workgroups per row
     waves_per_row = (waves_per_row + kWavesPerBlock - 1) / kWavesPerBlock *
                     kWavesPerBlock;
   const int64_t waves = waves_per_row * rows;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  auto kern = topk_ws ? qsa_scan_kernel<true> : qsa_scan_kernel<false>;
+  using Kern = void (*)(const uint8_t*, const float*, const uint8_t*,
+                        const int32_t*, int64_t, const int32_t*,
+                        const int32_t*, int64_t, int, int, int, int, float*,
+                        int64_t, int32_t*, void*, int);
+  Kern kern;
+  if (topk_ws)
+    kern = G == 32 ? qsa_scan_kernel<32, true> : G == 16 ? qsa_scan_kernel<16, true>
+         : G == 8 ? qsa_scan_kernel<8, true> : qsa_scan_kernel<4, true>;
+  else
+    kern = G == 32 ? qsa_scan_kernel<32, false> : G == 16 ? qsa_scan_kernel<16, false>
+         : G == 8 ? qsa_scan_kernel<8, false> : qsa_scan_kernel<4, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)),
                      dim3(kWavesPerBlock * kWave), 0, s, a.index_q, a.index_w,
                      a.index_k_pool, a.page_table, a.pt_stride, a.seq_lens,
