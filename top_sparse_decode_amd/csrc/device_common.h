@@ -50,22 +50,40 @@ TSD_DEVICE uint32_t order_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Butterfly over the 64 lanes of a wave: DPP moves within each 16-lane row
+// (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors),
+// then the gfx950 lane swaps across rows (permlane16_swap) and halves
+// (permlane32_swap). Every lane returns the combination of all 64.
+template <typename Op>
+TSD_DEVICE uint32_t wave_butterfly(uint32_t v, Op op) {
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                0, static_cast<int>(v), 0xB1, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                0, static_cast<int>(v), 0x4E, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                0, static_cast<int>(v), 0x141, 0xf, 0xf, false)));
+  v = op(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                0, static_cast<int>(v), 0x140, 0xf, 0xf, false)));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);
+}
+
 TSD_DEVICE float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return __uint_as_float(wave_butterfly(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 
 TSD_DEVICE float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __uint_as_float(wave_butterfly(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 
 TSD_DEVICE uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_butterfly(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave, on DPP lane moves:

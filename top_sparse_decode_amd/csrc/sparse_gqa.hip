@@ -118,10 +118,17 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
   const int G = H_q / H_kv;
   const int h0 = g * G;
   const int srow = H_sel == 1 ? 0 : g;
+  const int32_t* sel = idx + (static_cast<int64_t>(b) * H_sel + srow) * k;
+  // The chunk bounds depend on the selection's length m, which is k for
+  // every row longer than k: the first tile's entries for m = k are loaded
+  // together with the count and kept wherever they match the real bounds.
+  const int64_t lo_s = c * static_cast<int64_t>(k) / C;
+  const int64_t hi_s = (c + 1) * static_cast<int64_t>(k) / C;
+  int32_t t_spec = -1;
+  if (tid < NT && lo_s + tid < hi_s) t_spec = sel[lo_s + tid];
   const int64_t m = clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
   const int64_t lo = c * m / C, hi = (c + 1) * m / C;
   const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
-  const int32_t* sel = idx + (static_cast<int64_t>(b) * H_sel + srow) * k;
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
   const float zscale = softmax_scale * kLog2e;
 
@@ -153,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       int64_t slot = -1;
       float ksc = 0.f, vsc = 0.f;
       if (tid < tn) {
-        const int64_t t = sel[base + tid];
+        const bool spec = base == lo_s && lo_s + tid < hi_s;
+        const int64_t t = spec ? t_spec : sel[base + tid];
         if (t >= 0 && t < n) {
           const int32_t page = pt[t / kPage];
           if (page >= 0 && page < num_pages) {
@@ -168,20 +176,31 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       vs_s[tid] = vsc;
     }
     __syncthreads();
-    // 2. gather K and V rows (16-byte vectors; masked rows become zeros)
+    // 2. gather K and V rows (16-byte vectors; masked rows become zeros):
+    // every load of the tile is issued before the first LDS store
     constexpr int vpr = T::kRowBytes / 16;
+    constexpr int kIt = NT * vpr / kThreads;
+    static_assert(NT * vpr % kThreads == 0, "gather split");
+    uint4 kx[kIt], vx[kIt];
 #pragma unroll
-    for (int i = tid; i < NT * vpr; i += kThreads) {
+    for (int it = 0; it < kIt; ++it) {
+      const int i = tid + it * kThreads;
       const int j = i / vpr, v = i % vpr;
       const int64_t slot = slot_s[j];
-      uint4 kx = make_uint4(0, 0, 0, 0), vx = make_uint4(0, 0, 0, 0);
+      kx[it] = make_uint4(0, 0, 0, 0);
+      vx[it] = make_uint4(0, 0, 0, 0);
       if (slot >= 0) {
         const int64_t off = (slot * H_kv + g) * T::kRowBytes + 16 * v;
-        kx = *reinterpret_cast<const uint4*>(k_pool + off);
-        vx = *reinterpret_cast<const uint4*>(v_pool + off);
+        kx[it] = *reinterpret_cast<const uint4*>(k_pool + off);
+        vx[it] = *reinterpret_cast<const uint4*>(v_pool + off);
       }
-      *reinterpret_cast<uint4*>(k_s + j * T::kPitch + 16 * v) = kx;
-      *reinterpret_cast<uint4*>(v_s + j * T::kPitch + 16 * v) = vx;
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i = tid + it * kThreads;
+      const int j = i / vpr, v = i % vpr;
+      *reinterpret_cast<uint4*>(k_s + j * T::kPitch + 16 * v) = kx[it];
+      *reinterpret_cast<uint4*>(v_s + j * T::kPitch + 16 * v) = vx[it];
     }
     __syncthreads();
     // 3. logits on MFMA: wave owns tokens [16*kBlocks*wave, +16*kBlocks)

@@ -46,6 +46,7 @@ constexpr int kSegWords = kSegBits / 32;
 constexpr int kMaxChunks = 4096;       // max_len <= 2^24
 constexpr int kStage = 8192;           // survivors the pass-3 fast path holds
 constexpr int kPerLane = kStage / kRT; // survivors per lane on that path
+constexpr int kBlindRounds = 16;       // list reads per lane on the blind path
 
 TSD_DEVICE uint32_t digit1(uint32_t key) { return topk_digit1(key); }
 TSD_DEVICE uint32_t digit2(uint32_t key) {
@@ -266,6 +267,34 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid >> 6;
   constexpr int kWavesR = kRT / kWave;
+  const Ws ws = topk_ws(ws_base, gridDim.x, nch);
+  // Blind reads, issued with the row length: wave w takes chunks
+  // [w*R, w*R + R) and reads the first 64*H entries of each chunk's list
+  // and, in lane j, the count of its j-th chunk. Entries past a chunk's
+  // count are ignored; when every live chunk holds at most 64*H survivors
+  // this is the whole survivor sequence, wave-contiguous, after a single
+  // round trip.
+  // Round q of a lane covers chunk wave*R + q/H, entry 64*(q%H) + lane: H = 2
+  // (128 entries per chunk) when a wave has at most 8 chunks, else 1.
+  const int R = (nch + kWavesR - 1) / kWavesR;
+  const int H = R * 2 <= kBlindRounds ? 2 : 1;
+  const bool blind = R * H <= kBlindRounds;
+  uint2 bl[kBlindRounds];
+  uint32_t cntw = 0;
+  if (blind) {
+#pragma unroll
+    for (int q = 0; q < kBlindRounds; ++q) {
+      const int c = wave * R + q / H;
+      bl[q] = make_uint2(0u, 0u);
+      if (q < R * H && c < nch)
+        bl[q] = ws.lists[(static_cast<int64_t>(row) * nch + c) * kListCap +
+                         kWave * (q % H) + lane];
+    }
+    const int c = wave * R + lane;
+    if (lane < R && c < nch) cntw = ws.counts[static_cast<int64_t>(row) * nch + c];
+  }
+  const uint32_t h2v = ws.h2[static_cast<int64_t>(row) * kBins2 + (kBins2 - 1 - tid)];
+  const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 2
   const int64_t n = clamp_len(row_lens[row], cap);
   int32_t* out = idx + static_cast<int64_t>(row) * k;
   if (n <= k) {
@@ -274,9 +303,78 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
     return;
   }
-  const Ws ws = topk_ws(ws_base, gridDim.x, nch);
   const int nc = static_cast<int>((n + kChunk - 1) / kChunk);
   const float* s = scores + row * stride;
+  const BinPick p1{sel.x, sel.y};
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+
+  bool blind_ok = blind;
+  if (blind) {
+    const int c = wave * R + lane;
+    blind_ok = __ballot(lane < R && c < nc &&
+                        cntw > static_cast<uint32_t>(kWave * H)) == 0;
+  }
+  if (__syncthreads_and(blind_ok)) {
+    // ---- blind fast path ----
+    hist[tid] = 0u;  // digit-3 counts; ordered before use by p2's barriers
+    const uint32_t h2r[1] = {h2v};
+    const BinPick p2 = pick_bin_runs<kBins2, kRT>(h2r, k - p1.above, lds, &pick);
+    const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
+    const uint32_t need2 = k - p1.above - p2.above;
+    // per-lane flags of the rounds, one bit per round (ok, above T, at T),
+    // balloted again where a wave-wide view is needed
+    uint32_t okb = 0;
+#pragma unroll
+    for (int q = 0; q < kBlindRounds; ++q) {
+      const int j = q / H;  // the wave's chunk of this round
+      const int c = wave * R + j;
+      const uint32_t cc = static_cast<uint32_t>(
+          __builtin_amdgcn_readlane(static_cast<int>(cntw), j));
+      const bool ok = q < R * H && c < nc &&
+                      static_cast<uint32_t>(kWave * (q % H) + lane) < cc;
+      okb |= static_cast<uint32_t>(ok) << q;
+      if (ok && prefix12(bl[q].y) == pre)
+        atomicAdd(&hist[bl[q].y & (kBins3 - 1)], 1u);
+    }
+    __syncthreads();
+    const BinPick p3 = pick_bin<kBins3, kRT>(hist, need2, lds, &pick);
+    const uint32_t T = (pre << kB3) | p3.bin;
+    const uint32_t need = need2 - p3.above;  // ties at T to keep
+    uint32_t gtb = 0, eqb = 0, gtl = 0, eql = 0;
+#pragma unroll
+    for (int q = 0; q < kBlindRounds; ++q) {
+      const bool ok = (okb >> q) & 1u;
+      const bool gt = ok && bl[q].y > T, eq = ok && bl[q].y == T;
+      gtb |= static_cast<uint32_t>(gt) << q;
+      eqb |= static_cast<uint32_t>(eq) << q;
+      gtl += gt;
+      eql += eq;
+    }
+    const uint32_t gtw = wave_sum_u32(gtl), eqw = wave_sum_u32(eql);
+    // per-wave totals packed (ties << 16 | above); each is < 2^16
+    if (lane == 0) lds[wave] = (eqw << 16) | gtw;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int i = 0; i < kWavesR; ++i) before += i < wave ? lds[i] : 0u;
+    uint32_t eqr = before >> 16;  // ties in earlier waves
+    uint32_t pos = (before & 0xffffu) + (eqr < need ? eqr : need);
+#pragma unroll
+    for (int q = 0; q < kBlindRounds; ++q) {
+      const bool is_gt = (gtb >> q) & 1u;
+      const bool is_eq = (eqb >> q) & 1u;
+      const uint64_t me = __ballot(is_eq);
+      const uint32_t rank = eqr + static_cast<uint32_t>(__popcll(me & lt));
+      const bool kept = is_gt || (is_eq && rank < need);
+      const uint64_t mk = __ballot(kept);
+      const uint32_t p = pos + static_cast<uint32_t>(__popcll(mk & lt));
+      if (kept && p < static_cast<uint32_t>(k)) out[p] = static_cast<int32_t>(bl[q].x);
+      pos += static_cast<uint32_t>(__popcll(mk));
+      eqr += static_cast<uint32_t>(__popcll(me));
+    }
+    if (tid == 0 && count) count[row] = k;
+    return;
+  }
 
   // counts of this thread's run of chunks, b1 and H2, all loads in flight
   constexpr int kCpt = kMaxChunks / kRT;
@@ -286,7 +384,6 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const int c = tid * kCpt + j;
     cnt[j] = c < nc ? ws.counts[static_cast<int64_t>(row) * nch + c] : 0u;
   }
-  const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 1
   const uint32_t* h2 = ws.h2 + static_cast<int64_t>(row) * kBins2;
   for (int i = tid; i < kBins2; i += kRT) hist2[i] = h2[i];
   uint32_t run = 0;
@@ -317,22 +414,28 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   const uint32_t wbase = static_cast<uint32_t>(wave) * E * kWave;
   uint2 v[kPerLane];
   if (fast) {
+    // chunk of each entry: the largest c with off_s[c] <= e, by a
+    // branchless binary search run for all of the lane's entries at once
+    int cl[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) cl[j] = 0;
+    for (int step = 1 << (31 - __clz(nc)); step > 0; step >>= 1) {
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const uint32_t e = wbase + j * kWave + lane;
+        const int c = cl[j] + step;
+        if (c < nc && off_s[c] <= e) cl[j] = c;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
       const uint32_t e = wbase + j * kWave + lane;
       v[j] = make_uint2(0u, 0u);
-      if (static_cast<uint32_t>(j) < E && e < total) {
-        int lo = 0, hi = nc - 1;  // largest chunk with off_s[c] <= e
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (off_s[mid] <= e) lo = mid; else hi = mid - 1;
-        }
-        v[j] = ws.lists[(static_cast<int64_t>(row) * nch + lo) * kListCap +
-                        (e - off_s[lo])];
-      }
+      if (static_cast<uint32_t>(j) < E && e < total)
+        v[j] = ws.lists[(static_cast<int64_t>(row) * nch + cl[j]) * kListCap +
+                        (e - off_s[cl[j]])];
     }
   }
-  const BinPick p1{sel.x, sel.y};
   for (int i = tid; i < kBins3; i += kRT) hist[i] = 0u;  // ordered by p2
   const BinPick p2 = pick_bin<kBins2, kRT>(hist2, k - p1.above, lds, &pick);
   const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
@@ -350,7 +453,6 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const BinPick p3 = pick_bin<kBins3, kRT>(hist, need2, lds, &pick);
     const uint32_t T = (pre << kB3) | p3.bin;
     const uint32_t need = need2 - p3.above;  // ties at T to keep
-    const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
     uint64_t mg[kPerLane], me[kPerLane];
     uint32_t gtw = 0, eqw = 0;
 #pragma unroll
@@ -366,7 +468,8 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     if (lane == 0) lds[wave] = (eqw << 16) | gtw;
     __syncthreads();
     uint32_t before = 0;
-    for (int i = 0; i < wave; ++i) before += lds[i];
+#pragma unroll
+    for (int i = 0; i < kWavesR; ++i) before += i < wave ? lds[i] : 0u;
     uint32_t eqr = before >> 16;  // ties in earlier waves
     uint32_t pos = (before & 0xffffu) + (eqr < need ? eqr : need);
 #pragma unroll
