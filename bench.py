@@ -73,6 +73,33 @@ def cpu_baseline(layer, seconds):
                       f"steps/s"}
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles",
+                              "qsa_decode_b8_l262144_k2048.hbm_traffic.md")
+SCAN_SOURCES = ("score_qsa.hip", "device_common.h", "topk_common.h")
+
+
+def scan_traffic():
+    """HBM bytes per launch of the index scan from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the
+    scan's sources have changed since those counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+    except OSError:
+        return None
+    rec = dict(line.strip().split(": ", 1) for line in text.splitlines()
+               if line.strip().startswith(("scan_traffic_bytes_per_launch:",
+                                           "scan_sources_sha256:")))
+    h = hashlib.sha256()
+    for name in SCAN_SOURCES:
+        with open(os.path.join(ROOT, "top_sparse_decode_amd", "csrc", name),
+                  "rb") as f:
+            h.update(f.read())
+    if rec.get("scan_sources_sha256") != h.hexdigest():
+        return None
+    return int(rec["scan_traffic_bytes_per_launch"])
+
+
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X
 
 
@@ -268,7 +295,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "sparse_index_score",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "bytes_per_launch": index_b, "traffic": None},
+                     "bytes_per_launch": index_b, "traffic": scan_traffic()},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
