@@ -161,8 +161,10 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill indexer measurement")
     ap.add_argument("--prefill-passes", type=int, default=5)
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing HIP-graph replays of the step")
     ap.add_argument("--graph", action="store_true",
-                    help="time HIP-graph replays of the step instead of eager "
+                    help="report HIP-graph replays of the step as the value instead of eager "
                          "launches")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB "
@@ -220,7 +222,8 @@ def main():
 
     # the same step captured once per layer into a HIP graph and replayed
     graphs = []
-    if args.graph:
+    wall_graph = None
+    if not args.no_graph or args.graph:
         for plan in plans:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
@@ -234,7 +237,7 @@ def main():
             graphs[i % R].replay()
         torch.cuda.synchronize()
         wall_graph = time.perf_counter() - t0
-    wall = wall_graph if graphs else wall_eager
+    wall = wall_graph if args.graph else wall_eager
 
     # kernel durations: for each call, K back-to-back launches (rotating the
     # layers) between two HIP events on the launch stream; the average per
@@ -263,6 +266,23 @@ def main():
         torch.cuda.synchronize()
         us[name] = e0.elapsed_time(e1) * 1e3 / K
 
+    # stream-copy bandwidth of the part (1 GiB device copy, read + write)
+    del graphs
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    big2.copy_(big)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        big2.copy_(big)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big, big2
+    torch.cuda.empty_cache()
+
     step_s = wall / K
     scan_s = us["sparse_index_score"] * 1e-6
     achieved = index_b / scan_s / 1e9
@@ -289,9 +309,11 @@ def main():
         "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
         "step_frac_of_hbm": (index_b + gather_b) / step_s / 1e9 / HBM_PEAK_GBPS,
         "kernel_us": us,
-        "launch_mode": "hip_graph" if graphs else "eager",
+        "launch_mode": "hip_graph" if args.graph else "eager",
         "score_select": "separate calls" if args.unfused else "sparse_index_topk",
         "eager_steps_per_s": K / wall_eager,
+        "graph_steps_per_s": K / wall_graph if wall_graph else None,
+        "copy_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": "sparse_index_score",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

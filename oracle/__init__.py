@@ -67,6 +67,8 @@ def _load():
         "tsd_oracle_qsa_score_points": (I, [I, I, I, I, P, P, P, P, L, P, P,
                                             L, I, L, P, P, P]),
         "tsd_oracle_topk": (I, [P, L, I, P, I, P, P]),
+        "tsd_oracle_topk_merge_sharded": (I, [P, L, P, P, I, I, I, I, I, P,
+                                              P]),
         "tsd_oracle_sparse_attention": (I, [I, I, I, I, I, I, I, P, I, P, P, I,
                                             P, P, P, L, P, L, I, P, P, D, P,
                                             P]),
@@ -205,6 +207,32 @@ def topk(scores, row_lens, k):
     _check(_load().tsd_oracle_topk(_ptr(s), stride, rows, _ptr(rl), k,
                                    _ptr(idx), _ptr(cnt)))
     return idx, cnt
+
+
+def topk_merge_sharded(scores, idx, count, k, page_size=64):
+    """Exact global top-k from W page-owner shards: scores f32 [W, rows,
+    stride] (shard-local order), idx int32 [W, rows, kl] (local top-k lists),
+    count int32 [W, rows] -> (global idx int32 [rows, k], count [rows])."""
+    s = _c(scores, np.float32)
+    ix = _c(idx, np.int32)
+    ct = _c(count, np.int32)
+    W, rows, stride = s.shape
+    kl = ix.shape[2]
+    assert ix.shape[:2] == (W, rows) and ct.shape == (W, rows)
+    out = np.empty((rows, k), np.int32)
+    cnt = np.empty(rows, np.int32)
+    _check(_load().tsd_oracle_topk_merge_sharded(
+        _ptr(s), stride, _ptr(ix), _ptr(ct), W, rows, kl, page_size, k,
+        _ptr(out), _ptr(cnt)))
+    return out, cnt
+
+
+def shard_row_order(n, W, page_size=64):
+    """Global tokens of each shard in local order, for a row of n tokens
+    whose logical pages are owned by p % W: a list of W int64 arrays."""
+    t = np.arange(n, dtype=np.int64)
+    owner = (t // page_size) % W
+    return [t[owner == w] for w in range(W)]
 
 
 # ---------------------------------------------------------------- attention

@@ -323,6 +323,43 @@ int tsd_oracle_topk(const float *scores, int64_t stride, int rows,
   return ORC_OK;
 }
 
+int tsd_oracle_topk_merge_sharded(const float *scores, int64_t stride,
+                                  const int32_t *idx, const int32_t *count,
+                                  int W, int rows, int kl, int page_size,
+                                  int k, int32_t *out_idx,
+                                  int32_t *out_count) {
+  if (W < 1 || rows < 0 || kl < 0 || k <= 0 || page_size < 1) return ORC_E_ARG;
+  scored_t *all = (scored_t *)malloc(sizeof(scored_t) * (size_t)(W * kl + 1));
+  if (!all) return ORC_E_ARG;
+  for (int row = 0; row < rows; ++row) {
+    int64_t n = 0;
+    for (int w = 0; w < W; ++w) {
+      const int64_t sr = (int64_t)w * rows + row;
+      int32_t c = count[sr];
+      if (c > kl) c = kl;
+      for (int32_t j = 0; j < c; ++j) {
+        const int32_t u = idx[sr * kl + j];
+        if (u < 0) continue;
+        const float sc = scores[sr * stride + u];
+        if (isnan(sc)) { free(all); return ORC_E_NAN; }
+        all[n].s = sc;
+        all[n].t = (int32_t)(((int64_t)(u / page_size) * W + w) * page_size +
+                             u % page_size);
+        ++n;
+      }
+    }
+    qsort(all, (size_t)n, sizeof(scored_t), by_score_then_index);
+    const int64_t m = n < k ? n : k;
+    int32_t *out = out_idx + (int64_t)row * k;
+    for (int64_t j = 0; j < m; ++j) out[j] = all[j].t;
+    qsort(out, (size_t)m, sizeof(int32_t), by_index);
+    for (int64_t j = m; j < k; ++j) out[j] = -1;
+    if (out_count) out_count[row] = (int32_t)m;
+  }
+  free(all);
+  return ORC_OK;
+}
+
 /* --------------------------------------------------------------- attention */
 
 /* Dequantised element d of token slot, KV head g. */

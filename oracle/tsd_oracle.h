@@ -101,6 +101,23 @@ int tsd_oracle_topk(const float *scores, int64_t stride, int rows,
                     const int32_t *row_lens, int k, int32_t *idx,
                     int32_t *count);
 
+/* Exact global top-k from W page-owner shards ("QSA cache sharding",
+ * Distributed QSA execution: every rank selects over its own pages, the
+ * candidates are exchanged, and one exact top-k with token-id tie-breaking
+ * is formed). Shard w owns the logical pages p with p % W == w of every row;
+ * its local token u is the global token
+ *   t = ((u / page_size) * W + w) * page_size + u % page_size.
+ * Inputs per shard: scores [W][rows][stride] in local order, the local top-k
+ * lists idx [W][rows][kl] (local tokens, -1 padded) and count [W][rows].
+ * Output per row: the m = min(k, sum of counts) candidates ranked highest by
+ * (score descending, global token ascending), as global tokens in ascending
+ * order, -1 padded to k; out_count[row] = m. A NaN score is ORC_E_NAN. */
+int tsd_oracle_topk_merge_sharded(const float *scores, int64_t stride,
+                                  const int32_t *idx, const int32_t *count,
+                                  int W, int rows, int kl, int page_size,
+                                  int k, int32_t *out_idx,
+                                  int32_t *out_count);
+
 /* Chunked sparse GQA attention over selected tokens.
  * For request b, query head h (KV head g = h / (H_q / H_kv)) and chunk c of
  * the row's ascending selection list sel[0 .. m): tokens

@@ -319,6 +319,70 @@ def test_topk_signed_zero_tie_and_empty_rows(orc):
         orc.topk(np.array([[1.0, np.nan]], np.float32), [2], 1)
 
 
+def _sharded_topk(orc, s, n, W, k, page_size=64, kl=None):
+    """Shard a row by page owner p % W, select k locally per shard with the
+    oracle top-k, and merge the candidates with the oracle merge."""
+    kl = k if kl is None else kl
+    orders = orc.shard_row_order(n, W, page_size)
+    L = max(1, max(len(o) for o in orders))
+    S = np.zeros((W, 1, L), np.float32)
+    I = np.zeros((W, 1, kl), np.int32)
+    C = np.zeros((W, 1), np.int32)
+    for w, o in enumerate(orders):
+        S[w, 0, :len(o)] = s[o]
+        I[w], C[w] = orc.topk(S[w], [len(o)], kl)
+    return orc.topk_merge_sharded(S, I, C, k, page_size)
+
+
+def test_sharded_merge_hand_worked(orc):
+    # page size 2, W = 2: shard 0 owns pages 0 and 2 (tokens 0,1,4,5), shard 1
+    # owns page 1 (tokens 2,3); local token u of shard 1 is global u + 2
+    s = np.array([5.0, 1.0, 5.0, 7.0, 1.0, 5.0], np.float32)
+    idx, cnt = _sharded_topk(orc, s, 6, 2, 3, page_size=2)
+    assert list(idx[0]) == [0, 2, 3] and cnt[0] == 3  # 7, then 5s at 0 and 2
+    idx, cnt = _sharded_topk(orc, s, 6, 2, 4, page_size=2)
+    assert list(idx[0]) == [0, 2, 3, 5]
+    # a shard's local token maps back through its page: u = 2 of shard 0 is
+    # token 4 (page 2), u = 1 of shard 1 is token 3
+    S = np.array([[[0, 0, 9, 0]], [[0, 8, 0, 0]]], np.float32)
+    I = np.array([[[2]], [[1]]], np.int32)
+    C = np.array([[1], [1]], np.int32)
+    idx, cnt = orc.topk_merge_sharded(S, I, C, 2, page_size=2)
+    assert list(idx[0]) == [3, 4] and cnt[0] == 2
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 4, 5])
+def test_sharded_merge_equals_unsharded(orc, W):
+    # the global top-k of a row lies in the union of the shards' local
+    # top-ks, with the lowest global token winning ties across shards
+    rng = np.random.default_rng(W)
+    for n, k, levels in [(1000, 50, 20), (5000, 300, 3), (64 * 7 + 5, 100, 4),
+                         (40, 100, 5), (130, 7, 1), (20000, 2048, 1000)]:
+        s = (rng.integers(0, levels, size=n) / levels).astype(np.float32)
+        s[rng.random(n) < 0.05] = -0.0
+        got, gc = _sharded_topk(orc, s, n, W, k)
+        ref, rc = orc.topk(s[None], [n], k)
+        np.testing.assert_array_equal(got, ref)
+        np.testing.assert_array_equal(gc, rc)
+
+
+def test_sharded_merge_short_local_lists(orc):
+    # local lists shorter than k (kl < k) still merge exactly when every
+    # shard keeps at least its share of the global top-k
+    rng = np.random.default_rng(11)
+    n, W, k = 4096, 4, 64
+    s = rng.normal(size=n).astype(np.float32)
+    got, _ = _sharded_topk(orc, s, n, W, k, kl=k)
+    ref, _ = orc.topk(s[None], [n], k)
+    np.testing.assert_array_equal(got, ref)
+    # an empty row and rows shorter than one page per shard
+    got, gc = _sharded_topk(orc, s, 0, W, k)
+    assert (got == -1).all() and gc[0] == 0
+    got, gc = _sharded_topk(orc, s, 70, W, k)
+    ref, rc = orc.topk(s[None, :70], [70], k)
+    np.testing.assert_array_equal(got, ref)
+
+
 # ---------------------------------------------------------------- attention
 def _decoded_kv(wl, key, scale_key):
     x = wl[key]
