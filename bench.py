@@ -148,6 +148,82 @@ def prefill_indexer(dev, passes, warmup):
                          "frac": tflops / FP8_MFMA_PEAK_TFLOPS}}
 
 
+def sharded_select(dev, passes, warmup, W=4):
+    """Page-owner sharded exact top-k, emulated on one GPU: the 1,048,576-
+    token request split over W shards (shard w owns the logical pages
+    p % W == w; at W = 4 each holds 262,144 tokens, one GPU's share), each
+    shard scored and selected by sparse_index_topk, then topk_merge_sharded.
+    Times the whole emulated selection, the merge alone and the unsharded
+    sparse_index_topk, over back-to-back passes with HIP events."""
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config("qsa_decode_b1_l1048576_k2048")
+    wl = tsd_synth.make(cfg, dev)
+    k, B = cfg.top_k, cfg.B
+    views = tsd_synth.shard_views(wl, W)
+    stride = views[0]["page_table"].shape[1] * 64
+    S = torch.empty((W, B, stride), device=dev)
+    lens = torch.empty((W, B), dtype=torch.int32, device=dev)
+    il = torch.empty((W, B, k), dtype=torch.int32, device=dev)
+    cl = torch.empty((W, B), dtype=torch.int32, device=dev)
+    ws = [torch.empty(tsd.topk_select_workspace_bytes(B, stride, k),
+                      dtype=torch.uint8, device=dev) for _ in range(W)]
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    full_stride = wl["page_table"].shape[1] * 64
+    Sf = torch.empty((B, full_stride), device=dev)
+    lf = torch.empty((B,), dtype=torch.int32, device=dev)
+    wsf = torch.empty(tsd.topk_select_workspace_bytes(B, full_stride, k),
+                      dtype=torch.uint8, device=dev)
+    idxf = torch.empty((B, k), dtype=torch.int32, device=dev)
+    cntf = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def shards():
+        for w, v in enumerate(views):
+            tsd.sparse_index_topk("qsa", S[w], v["page_table"], v["seq_lens"],
+                                  wl["num_pages"], k, il[w], cl[w], ws[w],
+                                  lens[w], index_q=wl["index_q"],
+                                  index_w=wl["index_w"],
+                                  index_k_pool=wl["index_k"])
+
+    def merge():
+        tsd.topk_merge_sharded(S, il, cl, k, idx, cnt)
+
+    def unsharded():
+        tsd.sparse_index_topk("qsa", Sf, wl["page_table"], wl["seq_lens"],
+                              wl["num_pages"], k, idxf, cntf, wsf, lf,
+                              index_q=wl["index_q"], index_w=wl["index_w"],
+                              index_k_pool=wl["index_k"])
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n  # us
+
+    us_all = timed(lambda: (shards(), merge()), passes)
+    us_merge = timed(merge, passes)
+    us_full = timed(unsharded, passes)
+    exact = bool(torch.equal(idx, idxf) and torch.equal(cnt, cntf))
+    del wl, S, Sf
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "shards": W, "tokens_per_shard": stride,
+            "top_k": k, "sharded_select_us": us_all, "merge_us": us_merge,
+            "unsharded_select_us": us_full,
+            "merge_candidates_per_row": W * k,
+            "equals_unsharded": exact}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +237,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill indexer measurement")
     ap.add_argument("--prefill-passes", type=int, default=5)
+    ap.add_argument("--no-sharded", action="store_true",
+                    help="skip the page-owner sharded top-k emulation")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing HIP-graph replays of the step")
     ap.add_argument("--graph", action="store_true",
@@ -325,6 +403,8 @@ def main():
         del plans, plans_sep, table, fused_plans, bufs, layers
         torch.cuda.empty_cache()
         line["prefill_indexer"] = prefill_indexer(dev, args.prefill_passes, 2)
+    if not args.no_sharded:
+        line["sharded_topk"] = sharded_select(dev, 200, 20)
     print(json.dumps(line), flush=True)
 
 

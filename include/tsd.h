@@ -210,6 +210,35 @@ int sparse_index_topk(const tsd_score_args *a, int k, int32_t *idx,
                       hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * topk_merge_sharded
+ *
+ * Exact global top-k from W page-owner shards ("QSA cache sharding", sglang
+ * PR #43527, Distributed QSA execution: each rank selects over its own
+ * pages, the candidates are exchanged, and one exact top-k with token-id
+ * tie-breaking is formed). Shard w owns the logical pages p with
+ * p % W == w of every row; its local token u is the global token
+ * ((u / 64) * W + w) * 64 + u % 64. The inputs are each shard's scores in
+ * its local token order and its topk_select output; for each row the call
+ * writes the m = min(k, valid candidates) candidates ranked highest by
+ * (score descending, global token ascending) as global tokens in strictly
+ * ascending order, then -1 padding; count[row] = m. When every shard
+ * selected kl >= k (or all of its tokens), the result equals topk_select on
+ * the unsharded row.
+ *   scores       [W, rows, stride] f32   shard-local scores
+ *   idx_local    [W, rows, kl] int32     shard topk_select outputs
+ *   count_local  [W, rows] int32         their counts (entries j >= count,
+ *                                        and tokens outside [0, stride),
+ *                                        are ignored)
+ *   idx          [rows, k] int32 out     count [rows] int32 out or NULL
+ * 1 <= W <= 16; 1 <= kl, k <= 4096; W * kl <= 16,384; rows <= 65,535;
+ * W * stride <= 2^31 - 1. No workspace; nothing is allocated.
+ * ------------------------------------------------------------------------ */
+int topk_merge_sharded(const float *scores, int64_t stride,
+                       const int32_t *idx_local, const int32_t *count_local,
+                       int W, int rows, int kl, int k, int32_t *idx,
+                       int32_t *count, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * sparse_gqa_decode
  *
  * For request b, query head h, KV head g = h / G (G = H_q / H_kv) and chunk

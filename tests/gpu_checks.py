@@ -137,3 +137,44 @@ def check_merge(o_part, lse_part, out, out_lse, tol=1e-5):
               np.abs(gl[fin] - rl[fin]).max() if fin.any() else 0.0)
     assert err <= tol, f"merge error {err}"
     return err
+
+
+# ------------------------------------------------ page-owner sharded select
+def gpu_topk_stack(S, lens, kl):
+    """topk_select on each shard's [rows, stride] scores (one call per
+    shard) -> idx [W, rows, kl], count [W, rows] on the scores' device."""
+    import torch
+    import top_sparse_decode_amd as tsd
+    W, rows, stride = S.shape
+    idx = torch.full((W, rows, kl), -7, dtype=torch.int32, device=S.device)
+    cnt = torch.full((W, rows), -7, dtype=torch.int32, device=S.device)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(rows, stride, kl),
+                     dtype=torch.uint8, device=S.device)
+    for w in range(W):
+        tsd.topk_select(S[w], lens[w], kl, stride, idx[w], cnt[w], ws)
+    return idx, cnt
+
+
+def sharded_qsa_select(wl, W, k):
+    """Every page-owner shard scores and selects over its own pages of a QSA
+    decode workload; the candidates are merged. Returns (idx [B, k], count
+    [B], shard scores [W, B, stride_w], shard lengths [W, B])."""
+    import torch
+    import top_sparse_decode_amd as tsd
+    import tsd_synth
+    views = tsd_synth.shard_views(wl, W)
+    B = wl["page_table"].shape[0]
+    dev = wl["page_table"].device
+    stride = views[0]["page_table"].shape[1] * 64
+    S = torch.full((W, B, stride), float("nan"), device=dev)
+    lens = torch.empty((W, B), dtype=torch.int32, device=dev)
+    for w, v in enumerate(views):
+        tsd.sparse_index_score("qsa", S[w], v["page_table"], v["seq_lens"],
+                               wl["num_pages"], index_q=wl["index_q"],
+                               index_w=wl["index_w"],
+                               index_k_pool=wl["index_k"], row_lens_out=lens[w])
+    il, cl = gpu_topk_stack(S, lens, k)
+    idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+    tsd.topk_merge_sharded(S, il, cl, k, idx, cnt)
+    return idx, cnt, S, lens

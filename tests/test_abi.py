@@ -154,6 +154,26 @@ def test_topk_workspace_size():
     assert tsd.topk_select_workspace_bytes(0, 100, 5) == 0
 
 
+def test_merge_sharded_rejections():
+    m = LIB.topk_merge_sharded
+    ok = dict(stride=128, W=4, rows=2, kl=16, k=16)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return m(FAKE, a["stride"], FAKE, FAKE, a["W"], a["rows"], a["kl"],
+                 a["k"], FAKE, None, None)
+    assert call(W=0) == E["SHAPE"]
+    assert call(kl=0) == E["SHAPE"]
+    assert call(stride=0) == E["SHAPE"]
+    assert call(k=0) == E["K"]
+    assert call(k=4097) == E["K"]
+    assert call(W=17) == E["UNSUPPORTED"]
+    assert call(W=8, kl=4096) == E["UNSUPPORTED"]  # 32,768 candidates
+    assert call(W=16, stride=1 << 28) == E["UNSUPPORTED"]  # tokens past 2^31
+    assert m(None, 128, FAKE, FAKE, 4, 2, 16, 16, FAKE, None, None) == E["NULL"]
+    assert m(None, 128, None, None, 4, 0, 16, 16, None, None, None) == 0
+
+
 def _attn(**kw):
     a = AttnArgs()
     a.abi_version, a.B, a.H_q, a.H_kv, a.D = 1, 2, 32, 4, 128

@@ -162,6 +162,20 @@ def test_full_qsa_decode_b1_l1048576():
     _check_layer(wl, bufs, full_rows=[0])
 
 
+def test_full_sharded_select_b1_l1048576_w4():
+    """The 1M-token request split over 4 page-owner shards of 262,144 tokens
+    (each one GPU's share): per-shard score and top-k, then the exact merge,
+    equals the unsharded selection bit for bit."""
+    from gpu_checks import sharded_qsa_select
+    wl = tsd_synth.make("qsa_decode_b1_l1048576_k2048", DEV)
+    bufs = _run(wl)
+    idx, cnt, _, lens = sharded_qsa_select(wl, 4, 2048)
+    torch.cuda.synchronize()
+    assert lens[:, 0].tolist() == [262144] * 4
+    assert torch.equal(idx, bufs.idx.view(1, 2048))
+    assert torch.equal(cnt, bufs.count.view(1))
+
+
 def test_full_qsa_prefill_r2048_l1048576():
     """Chunked-prefill indexer pass: 2,048 causal query rows against all
     1,048,576 index keys, then per-row top-k. Rows 0, 1023 and 2047 are

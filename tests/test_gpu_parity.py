@@ -10,7 +10,8 @@ import oracle
 import tsd_synth
 from gpu_checks import (check_attention_on, check_merge, check_scores,
                         check_sets_within_window, check_topk_identical,
-                        oracle_row_lens, oracle_scores, out_tol, score_tol)
+                        gpu_topk_stack, oracle_row_lens, oracle_scores,
+                        out_tol, score_tol, sharded_qsa_select)
 
 pytestmark = pytest.mark.gpu
 
@@ -207,6 +208,81 @@ def test_topk_ties_at_threshold_and_one_overflowing_chunk():
     ridx, rcnt = oracle.topk(s, lens, k)
     np.testing.assert_array_equal(gcnt, rcnt)
     np.testing.assert_array_equal(gidx, ridx)
+
+
+# --------------------------------------------------- sharded top-k merge
+@pytest.mark.parametrize("W", [1, 3, 4, 8])
+def test_merge_sharded_matches_unsharded_topk(W):
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(40 + W)
+    ns = [70000, 4096 * 3 + 17, 64 * W - 5, 0, 2500, 150000]
+    k = 2048
+    rows = len(ns)
+    full = np.full((rows, max(ns)), np.nan, np.float32)
+    for r, n in enumerate(ns):
+        levels = [1000, 7, 50, 1, 3, 100000][r]
+        full[r, :n] = rng.integers(0, levels, size=n) / levels
+        full[r, :n][rng.random(n) < 0.02] = -0.0
+    # shard-local score rows: shard w holds the tokens of pages p % W == w
+    orders = [oracle.shard_row_order(n, W) for n in ns]
+    L = max(1, max(len(o) for ord_ in orders for o in ord_))
+    S = np.full((W, rows, L), np.nan, np.float32)
+    lens = np.zeros((W, rows), np.int32)
+    for r, ord_ in enumerate(orders):
+        for w, o in enumerate(ord_):
+            S[w, r, :len(o)] = full[r, o]
+            lens[w, r] = len(o)
+    Sg = torch.from_numpy(S).to(DEV)
+    lg = torch.from_numpy(lens).to(DEV)
+    il, cl = gpu_topk_stack(Sg, lg, k)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    tsd.topk_merge_sharded(Sg, il, cl, k, idx, cnt)
+    torch.cuda.synchronize()
+    ridx, rcnt = oracle.topk(np.nan_to_num(full, nan=0.0), ns, k)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), rcnt)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    # the oracle merge of the GPU's shard lists agrees as well
+    midx, _ = oracle.topk_merge_sharded(S, il.cpu().numpy(), cl.cpu().numpy(), k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), midx)
+
+
+def test_merge_sharded_short_lists_and_bad_entries():
+    import top_sparse_decode_amd as tsd
+    # hand-made candidate lists: counts below kl, -1 and out-of-range
+    # entries are ignored; k above the number of candidates pads with -1
+    W, rows, stride, kl, k = 2, 1, 128, 4, 6
+    S = torch.zeros((W, rows, stride), device=DEV)
+    S[0, 0, :4] = torch.tensor([1.0, 9.0, 3.0, 9.0])
+    S[1, 0, :4] = torch.tensor([9.0, 2.0, 5.0, 4.0])
+    il = torch.tensor([[[1, 3, 2, 0]], [[0, -1, 500, 3]]], dtype=torch.int32,
+                      device=DEV)
+    cl = torch.tensor([[3], [4]], dtype=torch.int32, device=DEV)
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    tsd.topk_merge_sharded(S, il, cl, k, idx, cnt)
+    torch.cuda.synchronize()
+    # shard 0 local 1, 3, 2 -> global 1, 3, 2; shard 1 local 0, 3 -> 64, 67
+    assert cnt.item() == 5
+    assert idx[0].tolist() == [1, 2, 3, 64, 67, -1]
+    out3 = torch.empty((rows, 3), dtype=torch.int32, device=DEV)
+    tsd.topk_merge_sharded(S, il, cl, 3, out3, cnt)
+    torch.cuda.synchronize()
+    assert out3[0].tolist() == [1, 3, 64]  # 9, 9, 9: lowest global tokens
+
+
+def test_sharded_qsa_pipeline_equals_unsharded():
+    """Each shard scores and selects over its own pages; the merge equals the
+    unsharded sparse_index_topk bit for bit."""
+    cfg = tsd_synth.config(QSA, B=2, lens=(70000, 33333), top_k=2048,
+                           chunks=8, seed=160)
+    wl = tsd_synth.make(cfg, DEV)
+    bufs = _run(wl)
+    idx, cnt, _, lens = sharded_qsa_select(wl, 4, cfg.top_k)
+    torch.cuda.synchronize()
+    assert lens.sum(0).tolist() == list(cfg.lens)
+    assert torch.equal(idx, bufs.idx.view(cfg.B, cfg.top_k))
+    assert torch.equal(cnt, bufs.count.view(cfg.B))
 
 
 def test_topk_row_lens_clamped_to_max_len():

@@ -80,6 +80,9 @@ def _load():
         "sparse_index_topk": (ctypes.c_int, [ctypes.POINTER(ScoreArgs),
                                              ctypes.c_int, _P, _P, _P,
                                              ctypes.c_size_t, _P]),
+        "topk_merge_sharded": (ctypes.c_int, [_P, _I64, _P, _P, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, _P, _P, _P]),
         "sparse_gqa_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _P]),
         "lse_merge": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _P, _P, _P]),
@@ -101,7 +104,7 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("sparse_index_score", "sparse_index_topk",
-           "topk_select_workspace_bytes", "topk_select",
+           "topk_select_workspace_bytes", "topk_select", "topk_merge_sharded",
            "sparse_gqa_decode", "lse_merge", "tsd_strerror", "tsd_abi_version",
            "tsd_sizeof_score_args", "tsd_sizeof_attn_args")
 
@@ -249,6 +252,23 @@ def topk_select(scores, row_lens, k, max_len, idx, count=None, workspace=None,
         _ptr(scores), scores.shape[-1], rows, _ptr(row_lens), int(max_len),
         int(k), _ptr(idx), _ptr(count), _ptr(workspace), ws_bytes,
         _stream(stream)))
+
+
+def topk_merge_sharded(scores, idx_local, count_local, k, idx, count=None,
+                       stream=None):
+    """Exact global top-k from W page-owner shards: ``scores`` [W, rows,
+    stride] (shard-local order), ``idx_local`` [W, rows, kl] and
+    ``count_local`` [W, rows] (each shard's topk_select output) into ``idx``
+    [rows, k] (ascending global tokens, -1 padded) and ``count`` [rows]."""
+    _dev("scores", scores, torch.float32)
+    _dev("idx_local", idx_local, torch.int32)
+    _dev("count_local", count_local, torch.int32)
+    _dev("idx", idx, torch.int32)
+    _dev("count", count, torch.int32)
+    W, rows, stride = scores.shape
+    _check("topk_merge_sharded", _lib.topk_merge_sharded(
+        _ptr(scores), stride, _ptr(idx_local), _ptr(count_local), W, rows,
+        idx_local.shape[2], int(k), _ptr(idx), _ptr(count), _stream(stream)))
 
 
 def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,

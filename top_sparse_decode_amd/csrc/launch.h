@@ -33,6 +33,13 @@ hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        int32_t* idx, int32_t* count, void* ws,
                        hipStream_t s);
 
+int topk_merge_max_candidates();  // W * kl bound of topk_merge_sharded
+hipError_t launch_topk_merge_sharded(const float* scores, int64_t stride,
+                                     const int32_t* idx_local,
+                                     const int32_t* count_local, int W,
+                                     int rows, int kl, int k, int32_t* idx,
+                                     int32_t* count, hipStream_t s);
+
 hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s);
 
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part,

@@ -184,6 +184,23 @@ int topk_select(const float* scores, int64_t stride, int rows,
                                         max_len, k, idx, count, ws, stream));
 }
 
+int topk_merge_sharded(const float* scores, int64_t stride,
+                       const int32_t* idx_local, const int32_t* count_local,
+                       int W, int rows, int kl, int k, int32_t* idx,
+                       int32_t* count, hipStream_t stream) {
+  if (W < 1 || rows < 0 || kl < 1 || stride < 1) return TSD_E_SHAPE;
+  if (k < 1 || k > TSD_MAX_TOPK) return TSD_E_K;
+  if (W > 16 || rows > 65535 || kl > TSD_MAX_TOPK ||
+      static_cast<int64_t>(W) * kl > tsd::topk_merge_max_candidates() ||
+      static_cast<int64_t>(W) * stride > std::numeric_limits<int32_t>::max())
+    return TSD_E_UNSUPPORTED;
+  if (rows == 0) return TSD_OK;
+  if (!scores || !idx_local || !count_local || !idx) return TSD_E_NULL;
+  return launch_status(tsd::launch_topk_merge_sharded(
+      scores, stride, idx_local, count_local, W, rows, kl, k, idx, count,
+      stream));
+}
+
 int sparse_gqa_decode(const tsd_attn_args* a, hipStream_t stream) {
   const int rc = validate_attn(a);
   if (rc) return rc;

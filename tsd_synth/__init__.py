@@ -283,6 +283,31 @@ def make(cfg, device="cpu", layer: int = 0) -> dict:
     return wl
 
 
+def shard_views(wl: dict, W: int):
+    """Page-owner shards of a workload's requests (shard w holds the logical
+    pages p with p % W == w, in order): per shard, its page table
+    [B, ceil(pt_stride / W)] (-1 past its pages) and its token counts [B].
+    The pools are shared; only the views differ."""
+    pt = wl["page_table"]
+    lens = wl["seq_lens"].to(torch.int64).to(pt.device)
+    B, P = pt.shape
+    Pw = -(-P // W)
+    npg = (lens + PAGE_SIZE - 1) // PAGE_SIZE  # logical pages of each row
+    last = npg - 1
+    tail = lens - last * PAGE_SIZE             # tokens on the last page
+    out = []
+    for w in range(W):
+        cols = torch.arange(w, P, W, device=pt.device)
+        ptw = torch.full((B, Pw), -1, dtype=torch.int32, device=pt.device)
+        ptw[:, :len(cols)] = pt[:, cols]
+        owned = torch.clamp((npg - w + W - 1) // W, min=0)
+        lw = owned * PAGE_SIZE
+        owns_last = (npg > 0) & (last % W == w)
+        lw = torch.where(owns_last, lw - PAGE_SIZE + tail, lw)
+        out.append({"page_table": ptw, "seq_lens": lw.to(torch.int32)})
+    return out
+
+
 def to_host(wl: dict) -> dict:
     """Copy a workload to numpy for the CPU oracle: half-precision tensors
     become their uint16 codes, FP8 stays uint8."""
