@@ -49,7 +49,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    if (not os.path.exists(LIB_PATH)
+            or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
@@ -69,6 +70,9 @@ def _load():
         "tsd_oracle_topk": (I, [P, L, I, P, I, P, P]),
         "tsd_oracle_topk_merge_sharded": (I, [P, L, P, P, I, I, I, I, I, P,
                                               P]),
+        "tsd_oracle_encode_fp8e4m3": (ctypes.c_uint8, [D]),
+        "tsd_oracle_kv_append": (I, [I, L, P, L, I, P, P, I, I, I, P, P, I, P,
+                                     P, I, P, P, P, I, P, P, I, P, I]),
         "tsd_oracle_sparse_attention": (I, [I, I, I, I, I, I, I, P, I, P, P, I,
                                             P, P, P, L, P, L, I, P, P, D, P,
                                             P]),
@@ -111,6 +115,11 @@ def _codes(a, enc):
 # ------------------------------------------------------------------ decoders
 def decode_fp8_e4m3(code: int) -> float:
     return _load().tsd_oracle_decode_fp8e4m3(int(code))
+
+
+def encode_fp8_e4m3(x: float) -> int:
+    """Nearest OCP E4M3 code (ties to even, saturating at 448)."""
+    return int(_load().tsd_oracle_encode_fp8e4m3(float(x)))
 
 
 def decode_bf16(bits: int) -> float:
@@ -207,6 +216,51 @@ def topk(scores, row_lens, k):
     _check(_load().tsd_oracle_topk(_ptr(s), stride, rows, _ptr(rl), k,
                                    _ptr(idx), _ptr(cnt)))
     return idx, cnt
+
+
+def kv_append(page_table, num_pages, positions, n_new, max_new, *,
+              k_new=None, v_new=None, new_enc="bf16", k_pool=None,
+              v_pool=None, kv_enc="bf16", k_scale=None, v_scale=None,
+              channel_idx=None, label_pool=None, index_k_new=None,
+              index_enc="bf16", index_k_pool=None, page_size=64):
+    """Cache append on host copies: returns the updated pools as a dict
+    (k_pool, v_pool, k_scale, v_scale, label_pool, index_k_pool; absent
+    ones None). New rows are raw codes of their encodings: k_new/v_new
+    [B, max_new, H_kv, D] 16-bit, index_k_new [B, max_new, 128]."""
+    pt = _c(page_table, np.int32)
+    B, pt_stride = pt.shape
+    pos = _c(positions, np.int32)
+    nn = _c(n_new, np.int32)
+    out = {}
+    H_kv = D = r = 0
+    kn = vn = kp = vp = ks = vs = None
+    if k_pool is not None:
+        kn, vn = _codes(k_new, new_enc).copy(), _codes(v_new, new_enc).copy()
+        H_kv, D = kn.shape[2], kn.shape[3]
+        kp, vp = _codes(k_pool, kv_enc).copy(), _codes(v_pool, kv_enc).copy()
+        if kv_enc == "fp8_e4m3":
+            ks, vs = _c(k_scale, np.float32).copy(), _c(v_scale, np.float32).copy()
+    ci = lp = None
+    if label_pool is not None:
+        kn = _codes(k_new, new_enc).copy() if kn is None else kn
+        H_kv, D = kn.shape[2], kn.shape[3]
+        ci = _c(channel_idx, np.int32)
+        r = ci.shape[1]
+        lp = _codes(label_pool, new_enc).copy()
+    ikn = ikp = None
+    D_i = 0
+    if index_k_pool is not None:
+        ikn = _codes(index_k_new, index_enc).copy()
+        D_i = ikn.shape[2]
+        ikp = _c(index_k_pool, np.uint8).copy()
+    _check(_load().tsd_oracle_kv_append(
+        B, pt_stride, _ptr(pt), int(num_pages), page_size, _ptr(pos),
+        _ptr(nn), int(max_new), H_kv, D, _ptr(kn), _ptr(vn), DTYPE[new_enc],
+        _ptr(kp), _ptr(vp), DTYPE[kv_enc], _ptr(ks), _ptr(vs), _ptr(ci), r,
+        _ptr(lp), _ptr(ikn), DTYPE[index_enc], _ptr(ikp), D_i))
+    out.update(k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs, label_pool=lp,
+               index_k_pool=ikp)
+    return out
 
 
 def topk_merge_sharded(scores, idx, count, k, page_size=64):

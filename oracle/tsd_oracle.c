@@ -360,6 +360,111 @@ int tsd_oracle_topk_merge_sharded(const float *scores, int64_t stride,
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------ cache append */
+
+uint8_t tsd_oracle_encode_fp8e4m3(double x) {
+  const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  const double a = fabs(x);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {  /* every finite non-negative code */
+    const double err = fabs(a - tsd_oracle_decode_fp8e4m3((uint8_t)c));
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a >= 448.0) best = 0x7E;
+  return (uint8_t)(sign | best);
+}
+
+/* f32 value of element i of a 16-bit array, or of an f32 array (dtype 4). */
+static float half_or_f32(const void *base, int dtype, int64_t i) {
+  if (dtype == 4) return ((const float *)base)[i];
+  return (float)decode_elem(base, dtype, i);
+}
+
+int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
+                         int64_t num_pages, int page_size,
+                         const int32_t *positions, const int32_t *n_new,
+                         int max_new, int H_kv, int D, const void *k_new,
+                         const void *v_new, int new_dtype, void *k_pool,
+                         void *v_pool, int kv_dtype, float *k_scale,
+                         float *v_scale, const int32_t *channel_idx, int r,
+                         void *label_pool, const void *index_k_new,
+                         int index_dtype, void *index_k_pool, int D_i) {
+  if (B < 0 || max_new < 0 || page_size < 1) return ORC_E_ARG;
+  const int fp8 = kv_dtype == ORC_FP8E4M3;
+  if (k_pool && (new_dtype != ORC_BF16 && new_dtype != ORC_FP16)) return ORC_E_ARG;
+  if (k_pool && !fp8 && kv_dtype != new_dtype) return ORC_E_ARG;
+  if (k_pool && fp8 && (!k_scale || !v_scale)) return ORC_E_ARG;
+  const int64_t row = (int64_t)H_kv * D;
+  for (int b = 0; b < B; ++b) {
+    int32_t n = n_new[b] < 0 ? 0 : n_new[b];
+    if (n > max_new) n = max_new;
+    const int64_t pos = positions[b];
+    /* page scales of the pages this call starts, from the values it writes */
+    if (k_pool && fp8) {
+      for (int32_t i = 0; i < n; ++i) {
+        const int64_t t = pos + i;
+        if (t < 0 || t >= pt_stride * page_size) continue;
+        const int64_t lp = t / page_size;
+        const int32_t page = page_table[(int64_t)b * pt_stride + lp];
+        if (page < 0 || page >= num_pages) continue;
+        if (lp * page_size < pos) continue;  /* page began before this call */
+        if (t != lp * page_size && i != 0) continue;  /* once per page */
+        float ka = 0.f, va = 0.f;
+        for (int32_t i2 = i; i2 < n && (pos + i2) / page_size == lp; ++i2)
+          for (int64_t e = 0; e < row; ++e) {
+            const int64_t at = ((int64_t)b * max_new + i2) * row + e;
+            const float kv = fabsf(half_or_f32(k_new, new_dtype, at));
+            const float vv = fabsf(half_or_f32(v_new, new_dtype, at));
+            if (kv > ka) ka = kv;
+            if (vv > va) va = vv;
+          }
+        k_scale[page] = ka > 0.f ? ka / 448.0f : 1.0f;
+        v_scale[page] = va > 0.f ? va / 448.0f : 1.0f;
+      }
+    }
+    for (int32_t i = 0; i < n; ++i) {
+      const int64_t t = pos + i;
+      if (t < 0 || t >= pt_stride * page_size) continue;
+      const int32_t page = page_table[(int64_t)b * pt_stride + t / page_size];
+      if (page < 0 || page >= num_pages) continue;
+      const int64_t slot = (int64_t)page * page_size + t % page_size;
+      const int64_t src = ((int64_t)b * max_new + i) * row;
+      if (k_pool) {
+        for (int64_t e = 0; e < row; ++e) {
+          if (fp8) {
+            const float kq = half_or_f32(k_new, new_dtype, src + e) / k_scale[page];
+            const float vq = half_or_f32(v_new, new_dtype, src + e) / v_scale[page];
+            ((uint8_t *)k_pool)[slot * row + e] = tsd_oracle_encode_fp8e4m3(kq);
+            ((uint8_t *)v_pool)[slot * row + e] = tsd_oracle_encode_fp8e4m3(vq);
+          } else {
+            ((uint16_t *)k_pool)[slot * row + e] = ((const uint16_t *)k_new)[src + e];
+            ((uint16_t *)v_pool)[slot * row + e] = ((const uint16_t *)v_new)[src + e];
+          }
+        }
+      }
+      if (label_pool) {
+        for (int g = 0; g < H_kv; ++g)
+          for (int j = 0; j < r; ++j) {
+            const int32_t ch = channel_idx[g * r + j];
+            ((uint16_t *)label_pool)[(slot * H_kv + g) * r + j] =
+                ((const uint16_t *)k_new)[src + (int64_t)g * D + ch];
+          }
+      }
+      if (index_k_pool) {
+        const int64_t isrc = ((int64_t)b * max_new + i) * D_i;
+        for (int d = 0; d < D_i; ++d)
+          ((uint8_t *)index_k_pool)[slot * D_i + d] = tsd_oracle_encode_fp8e4m3(
+              half_or_f32(index_k_new, index_dtype, isrc + d));
+      }
+    }
+  }
+  return ORC_OK;
+}
+
 /* --------------------------------------------------------------- attention */
 
 /* Dequantised element d of token slot, KV head g. */

@@ -101,6 +101,45 @@ int tsd_oracle_topk(const float *scores, int64_t stride, int rows,
                     const int32_t *row_lens, int k, int32_t *idx,
                     int32_t *count);
 
+/* The OCP E4M3 code nearest to x: round to nearest, ties to the code with
+ * an even mantissa, magnitudes beyond 448 saturating to +-448 (the encoding
+ * has no infinity); the sign of x is kept, so -0 and small negatives give
+ * 0x80. x must not be NaN. */
+uint8_t tsd_oracle_encode_fp8e4m3(double x);
+
+/* Cache append ("Support double sparsity", forward_extend: the label cache
+ * is K gathered at the heavy channels and is stored with every new token;
+ * "Context parallelism for QSA attention and the sparse indexer",
+ * Motivation: the indexer stores raw index-K for every token).
+ * For request b the new tokens are positions positions[b] + i for
+ * i < clamp(n_new[b], 0, max_new); a position outside the page table's
+ * reach, or on a page id outside [0, num_pages), is skipped.
+ * Each new token's rows go to slot = page_table[b][t/page_size]*page_size +
+ * t%page_size:
+ *  - K and V (k_new/v_new [B, max_new, H_kv, D] in new_dtype, a 16-bit
+ *    encoding): copied when kv_dtype == new_dtype; for FP8 pools encoded as
+ *    e(v / scale) with the page's f32 scale. A page none of whose tokens
+ *    precede positions[b] starts in this call: its scale becomes
+ *    amax / 448 (1 if amax is 0) over the values this call writes to it
+ *    (all heads and dims, K and V separately) and is stored in
+ *    k_scale/v_scale; any other page keeps its stored scale. The scale and
+ *    the quotient are computed in f32, the code from the f32 quotient.
+ *  - label (if label_pool): label[slot][g][j] = K_new[g][channel_idx[g][j]]
+ *    in new_dtype (bit copy).
+ *  - index-K (if index_k_pool): index_k[slot][d] = e(index_k_new[b][i][d])
+ *    with index_k_new in index_dtype (bf16, fp16, or 4 for f32) rounded to
+ *    f32 first.
+ * Pools not passed (NULL) are left alone. */
+int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
+                         int64_t num_pages, int page_size,
+                         const int32_t *positions, const int32_t *n_new,
+                         int max_new, int H_kv, int D, const void *k_new,
+                         const void *v_new, int new_dtype, void *k_pool,
+                         void *v_pool, int kv_dtype, float *k_scale,
+                         float *v_scale, const int32_t *channel_idx, int r,
+                         void *label_pool, const void *index_k_new,
+                         int index_dtype, void *index_k_pool, int D_i);
+
 /* Exact global top-k from W page-owner shards ("QSA cache sharding",
  * Distributed QSA execution: every rank selects over its own pages, the
  * candidates are exchanged, and one exact top-k with token-id tie-breaking

@@ -383,6 +383,112 @@ def test_sharded_merge_short_local_lists(orc):
     np.testing.assert_array_equal(got, ref)
 
 
+# -------------------------------------------------------------- cache append
+def test_fp8_encode_round_trips_every_code(orc):
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue  # the NaN codes
+        assert orc.encode_fp8_e4m3(orc.decode_fp8_e4m3(c)) == c, c
+
+
+def test_fp8_encode_midpoints_saturation_and_torch(orc):
+    pos = [orc.decode_fp8_e4m3(c) for c in range(0x7F)]
+    for c in range(0x7E):
+        mid = (pos[c] + pos[c + 1]) / 2
+        even = c if c % 2 == 0 else c + 1
+        assert orc.encode_fp8_e4m3(mid) == even
+        assert orc.encode_fp8_e4m3(-mid) == 0x80 | even
+        assert orc.encode_fp8_e4m3(np.nextafter(mid, 1e9)) == c + 1
+    for x, code in [(448.0, 0x7E), (463.9, 0x7E), (1e9, 0x7E), (-600.0, 0xFE),
+                    (0.0, 0x00), (-0.0, 0x80), (-1e-30, 0x80), (2.0 ** -10, 0x00),
+                    (3 * 2.0 ** -10, 0x02)]:
+        assert orc.encode_fp8_e4m3(x) == code, x
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.normal(size=4000) * 40, rng.normal(size=2000) * 1e-2,
+                        rng.uniform(-447, 447, 2000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([orc.encode_fp8_e4m3(float(v)) for v in x], np.uint8)
+    np.testing.assert_array_equal(got, ref)
+
+
+def _bf16_codes(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(
+        torch.int16).numpy().view(np.uint16)
+
+
+def test_append_16bit_rows_label_and_index(orc):
+    # 2 requests, page table with a bad page id and a short capacity
+    rng = np.random.default_rng(4)
+    H, D, r, slots = 2, 8, 3, 6 * 64
+    pt = np.array([[3, 1, -1], [0, 5, 2]], np.int32)
+    kp = rng.integers(0, 65535, (slots, H, D)).astype(np.uint16)
+    vp = rng.integers(0, 65535, (slots, H, D)).astype(np.uint16)
+    lp = rng.integers(0, 65535, (slots, H, r)).astype(np.uint16)
+    ip = rng.integers(0, 255, (slots, 16)).astype(np.uint8)
+    kn = _bf16_codes(rng.normal(size=(2, 5, H, D)))
+    vn = _bf16_codes(rng.normal(size=(2, 5, H, D)))
+    ikn = rng.normal(size=(2, 5, 16)).astype(np.float32) * 30
+    ch = np.array([[0, 5, 7], [2, 3, 6]], np.int32)
+    positions, n_new = [62, 190], [5, 3]
+    got = orc.kv_append(pt, 6, positions, n_new, 5, k_new=kn, v_new=vn,
+                        k_pool=kp, v_pool=vp, channel_idx=ch, label_pool=lp,
+                        index_k_new=ikn, index_enc="f32", index_k_pool=ip)
+    # request 0: positions 62, 63 on page 3; 64, 65, 66 on page 1
+    # request 1: 190, 191 on page 2 (logical page 2); 192 is past capacity
+    writes = {(0, 0): 3 * 64 + 62, (0, 1): 3 * 64 + 63, (0, 2): 64 + 0,
+              (0, 3): 64 + 1, (0, 4): 64 + 2, (1, 0): 2 * 64 + 62,
+              (1, 1): 2 * 64 + 63}
+    ek, ev, el, ei = kp.copy(), vp.copy(), lp.copy(), ip.copy()
+    for (b, i), slot in writes.items():
+        ek[slot], ev[slot] = kn[b, i], vn[b, i]
+        el[slot] = np.take_along_axis(kn[b, i], ch, axis=1)
+        ei[slot] = torch.from_numpy(ikn[b, i]).to(torch.float8_e4m3fn).view(
+            torch.uint8).numpy()
+    np.testing.assert_array_equal(got["k_pool"], ek)
+    np.testing.assert_array_equal(got["v_pool"], ev)
+    np.testing.assert_array_equal(got["label_pool"], el)
+    np.testing.assert_array_equal(got["index_k_pool"], ei)
+    assert got["k_scale"] is None
+
+
+def test_append_fp8_pages_match_the_page_quantizer(orc):
+    # a call that fills a fresh page gives the per-page quantization of the
+    # workload generator (scale = amax/448 in f32, round to nearest even)
+    rng = np.random.default_rng(5)
+    H, D = 2, 16
+    x = (rng.normal(size=(1, 64 + 10, H, D)) * 3).astype(np.float32)
+    x[0, 64:] *= 5
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    kn = xb.view(torch.int16).numpy().view(np.uint16)
+    pt = np.array([[2, 0]], np.int32)
+    kp = np.zeros((3 * 64, H, D), np.uint8)
+    ks = np.full(3, 7.0, np.float32)
+    got = orc.kv_append(pt, 3, [0], [74], 74, k_new=kn, v_new=kn,
+                        k_pool=kp, v_pool=kp.copy(), kv_enc="fp8_e4m3",
+                        k_scale=ks, v_scale=ks.copy())
+    for lp_, page, lo, hi in [(0, 2, 0, 64), (1, 0, 64, 74)]:
+        vals = xb[0, lo:hi].float()
+        pad = torch.zeros((64, H, D))
+        pad[:hi - lo] = vals
+        codes, scale = tsd_synth.quantize_fp8_per_page(pad)
+        assert got["k_scale"][page] == scale[0].item()
+        np.testing.assert_array_equal(got["k_pool"][page * 64:page * 64 + hi - lo],
+                                      codes[:hi - lo].numpy())
+    assert got["k_scale"][1] == 7.0  # untouched page keeps its scale
+    # appending to a started page keeps its scale and saturates above 448*s
+    kn2 = _bf16_codes(np.full((1, 1, H, D), 1e4))
+    got2 = orc.kv_append(pt, 3, [74], [1], 1, k_new=kn2, v_new=kn2,
+                         k_pool=got["k_pool"], v_pool=got["v_pool"],
+                         kv_enc="fp8_e4m3", k_scale=got["k_scale"],
+                         v_scale=got["v_scale"])
+    # token 74 is on logical page 1 = physical page 0, slot 10
+    assert got2["k_scale"][0] == got["k_scale"][0]
+    assert (got2["k_pool"][10] == 0x7E).all()
+    keep = np.ones(3 * 64, bool)
+    keep[10] = False
+    np.testing.assert_array_equal(got2["k_pool"][keep], got["k_pool"][keep])
+
+
 # ---------------------------------------------------------------- attention
 def _decoded_kv(wl, key, scale_key):
     x = wl[key]
