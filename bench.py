@@ -224,6 +224,68 @@ def sharded_select(dev, passes, warmup, W=4):
             "equals_unsharded": exact}
 
 
+def append_bench(dev, passes, warmup):
+    """kv_append at decode shapes, one new token per request, timed per call
+    (pre-marshalled C calls) over back-to-back launches with HIP events: the
+    262,144-token FP8
+    workload (8 requests, 4 KV heads: K, V with per-page scales, index-K),
+    on a page the call starts and mid-page, and the 200-step double-sparsity
+    workload (3 requests, 32 KV heads: FP16 K, V and the 16-channel label)."""
+    import torch
+
+    import top_sparse_decode_amd as tsd
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(passes):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / passes  # us
+
+    out = {}
+    B, H, D, P = 8, 4, 128, 4097  # 4,096 cached pages + the new tokens' page
+    pt = torch.full((B, P), -1, dtype=torch.int32, device=dev)
+    pt[:, P - 1] = torch.arange(B, dtype=torch.int32, device=dev)
+    kp = torch.zeros((B * 64, H, D), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    ks = torch.ones(B, device=dev)
+    vs = torch.ones(B, device=dev)
+    ip = torch.zeros((B * 64, 128), dtype=torch.uint8, device=dev)
+    kn = torch.randn((B, 1, H, D), device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, 1, H, D), device=dev).to(torch.bfloat16)
+    ikn = torch.randn((B, 1, 128), device=dev).to(torch.bfloat16)
+    one = torch.ones(B, dtype=torch.int32, device=dev)
+    for name, p0 in (("qsa_b8_fp8_new_page_us", 4096 * 64),
+                     ("qsa_b8_fp8_mid_page_us", 4096 * 64 + 17)):
+        pos = torch.full((B,), p0, dtype=torch.int32, device=dev)
+        out[name] = timed(tsd.kv_append(
+            pt, B, pos, one, 1, k_new=kn, v_new=vn, k_pool=kp, v_pool=vp,
+            k_scale=ks, v_scale=vs, index_k_new=ikn, index_k_pool=ip,
+            stream=stream, prepare=True))
+    B, H, r, P = 3, 32, 16, 316
+    pt = torch.full((B, P), -1, dtype=torch.int32, device=dev)
+    pt[:, 312] = torch.arange(B, dtype=torch.int32, device=dev)
+    kp = torch.zeros((B * 64, H, D), dtype=torch.float16, device=dev)
+    vp = torch.zeros_like(kp)
+    lp = torch.zeros((B * 64, H, r), dtype=torch.float16, device=dev)
+    ch = torch.stack([torch.randperm(D, device=dev)[:r] for _ in range(H)]).to(torch.int32)
+    kn = torch.randn((B, 1, H, D), device=dev).to(torch.float16)
+    vn = torch.randn((B, 1, H, D), device=dev).to(torch.float16)
+    pos = torch.full((B,), 20000, dtype=torch.int32, device=dev)
+    one = torch.ones(B, dtype=torch.int32, device=dev)
+    out["ds_b3_fp16_label_us"] = timed(tsd.kv_append(
+        pt, B, pos, one, 1, k_new=kn, v_new=vn, k_pool=kp, v_pool=vp,
+        channel_idx=ch, label_pool=lp, stream=stream, prepare=True))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -405,6 +467,7 @@ def main():
         line["prefill_indexer"] = prefill_indexer(dev, args.prefill_passes, 2)
     if not args.no_sharded:
         line["sharded_topk"] = sharded_select(dev, 200, 20)
+    line["kv_append"] = append_bench(dev, 500, 20)
     print(json.dumps(line), flush=True)
 
 

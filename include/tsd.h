@@ -68,7 +68,8 @@ extern "C" {
 enum {
   TSD_BF16 = 1,
   TSD_FP16 = 2,
-  TSD_FP8_E4M3 = 3
+  TSD_FP8_E4M3 = 3,
+  TSD_F32 = 4       /* IEEE binary32 (kv_append's index_k_new only)      */
 };
 
 /* Status codes (negative: rejected on the host, nothing launched). */
@@ -307,16 +308,77 @@ int sparse_gqa_decode(const tsd_attn_args *a, hipStream_t stream);
 int lse_merge(const float *o_part, const float *lse_part, int rows, int C,
               int D, float *out, float *out_lse, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * kv_append
+ *
+ * Stores the rows of newly appended tokens into the paged pools ("Support
+ * double sparsity", forward_extend in the discussion: the label cache is K
+ * gathered at the heavy channels and is written with every new token;
+ * "Context parallelism for QSA attention and the sparse indexer",
+ * Motivation: the indexer stores raw index-K for every token). For request
+ * b the new tokens are the positions positions[b] + i,
+ * i < clamp(n_new[b], 0, max_new); token t goes to
+ * slot = page_table[b][t / 64] * 64 + t % 64. A position at or past
+ * pt_stride * 64, or on a page id outside [0, num_pages), is skipped.
+ *  - K and V (when k_new is not NULL): k_new, v_new [B, max_new, H_kv, D]
+ *    in new_dtype (BF16/FP16). A pool in new_dtype gets a copy. An FP8
+ *    pool gets code(value / scale) with the page's f32 scale: a page none
+ *    of whose tokens precede positions[b] is started by the call and its
+ *    scale becomes amax / 448 (1 for amax 0) over the values the call
+ *    writes to it (all heads and dims; K and V separately), stored in
+ *    k_scale / v_scale; any other page keeps its stored scale, and values
+ *    beyond 448 * scale saturate. Scale and quotient are computed in f32;
+ *    code() rounds to nearest, ties to even.
+ *  - label (when channel_idx is not NULL): label_pool [slots, H_kv, r]
+ *    (new_dtype) gets K_new[g][channel_idx[g][j]] for j < r (a channel
+ *    outside [0, D) stores 0).
+ *  - index-K (when index_k_new is not NULL): index_k_pool [slots, D_i]
+ *    FP8 gets code(index_k_new[b][i][d]) (unit scale), index_k_new
+ *    [B, max_new, D_i] in index_dtype (BF16, FP16 or F32).
+ * D = D_i = 128; 1 <= r <= D; H_kv * D <= 4096; every row and pool
+ * pointer 16-byte aligned (else TSD_E_UNSUPPORTED). A call with no pool to
+ * write launches nothing. Two calls that write the same page of an FP8 pool
+ * must not run concurrently.
+ * ------------------------------------------------------------------------ */
+typedef struct tsd_append_args {
+  int32_t abi_version;        /* TSD_ABI_VERSION                             */
+  int32_t B;
+  int32_t page_size;          /* must be 64                                  */
+  int32_t max_new;            /* host bound on n_new[b] (sizes the launch)   */
+  const int32_t *page_table;  /* [B, pt_stride]                              */
+  int64_t pt_stride;
+  int64_t num_pages;
+  const int32_t *positions;   /* [B] first new position of each request      */
+  const int32_t *n_new;       /* [B] new tokens of each request              */
+  int32_t H_kv, D;
+  int32_t new_dtype;          /* encoding of k_new / v_new / label           */
+  int32_t kv_dtype;           /* pool encoding: new_dtype or TSD_FP8_E4M3    */
+  const void *k_new, *v_new;
+  void *k_pool, *v_pool;
+  float *k_scale, *v_scale;   /* [num_pages], FP8 pools only                 */
+  const int32_t *channel_idx; /* [H_kv, r]                                   */
+  void *label_pool;
+  int32_t r;
+  int32_t index_dtype;
+  const void *index_k_new;
+  void *index_k_pool;
+  int32_t D_i;
+  int32_t reserved0;
+} tsd_append_args;
+
+int kv_append(const tsd_append_args *a, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, host only). */
 const char *tsd_strerror(int status);
 
 /* TSD_ABI_VERSION of the built library. */
 int tsd_abi_version(void);
 
-/* sizeof the two argument structs as compiled into the library, so a
- * binding can check its own layout. */
+/* sizeof the argument structs as compiled into the library, so a binding
+ * can check its own layout. */
 size_t tsd_sizeof_score_args(void);
 size_t tsd_sizeof_attn_args(void);
+size_t tsd_sizeof_append_args(void);
 
 #ifdef __cplusplus
 }

@@ -451,7 +451,9 @@ int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
           for (int j = 0; j < r; ++j) {
             const int32_t ch = channel_idx[g * r + j];
             ((uint16_t *)label_pool)[(slot * H_kv + g) * r + j] =
-                ((const uint16_t *)k_new)[src + (int64_t)g * D + ch];
+                ch >= 0 && ch < D
+                    ? ((const uint16_t *)k_new)[src + (int64_t)g * D + ch]
+                    : 0; /* a channel outside [0, D) stores 0 */
           }
       }
       if (index_k_pool) {

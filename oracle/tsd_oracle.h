@@ -125,7 +125,7 @@ uint8_t tsd_oracle_encode_fp8e4m3(double x);
  *    k_scale/v_scale; any other page keeps its stored scale. The scale and
  *    the quotient are computed in f32, the code from the f32 quotient.
  *  - label (if label_pool): label[slot][g][j] = K_new[g][channel_idx[g][j]]
- *    in new_dtype (bit copy).
+ *    in new_dtype (bit copy); a channel outside [0, D) stores 0.
  *  - index-K (if index_k_pool): index_k[slot][d] = e(index_k_new[b][i][d])
  *    with index_k_new in index_dtype (bf16, fp16, or 4 for f32) rounded to
  *    f32 first.

@@ -39,6 +39,7 @@ def test_abi_version_and_struct_layout():
     assert LIB.tsd_abi_version() == 1
     assert LIB.tsd_sizeof_score_args() == ctypes.sizeof(ScoreArgs)
     assert LIB.tsd_sizeof_attn_args() == ctypes.sizeof(AttnArgs)
+    assert LIB.tsd_sizeof_append_args() == ctypes.sizeof(tsd.AppendArgs)
 
 
 def test_strerror_names_every_code():
@@ -172,6 +173,54 @@ def test_merge_sharded_rejections():
     assert call(W=16, stride=1 << 28) == E["UNSUPPORTED"]  # tokens past 2^31
     assert m(None, 128, FAKE, FAKE, 4, 2, 16, 16, FAKE, None, None) == E["NULL"]
     assert m(None, 128, None, None, 4, 0, 16, 16, None, None, None) == 0
+
+
+def _append(**kw):
+    a = tsd.AppendArgs()
+    a.abi_version, a.B, a.page_size, a.max_new = 1, 2, 64, 4
+    a.page_table, a.pt_stride, a.num_pages = FAKE, 8, 16
+    a.positions, a.n_new = FAKE, FAKE
+    a.H_kv, a.D, a.new_dtype, a.kv_dtype = 4, 128, 1, 3
+    a.k_new, a.v_new, a.k_pool, a.v_pool = FAKE, FAKE, FAKE, FAKE
+    a.k_scale, a.v_scale = FAKE, FAKE
+    a.channel_idx, a.label_pool, a.r = FAKE, FAKE, 16
+    a.index_dtype, a.index_k_new, a.index_k_pool, a.D_i = 4, FAKE, FAKE, 128
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return LIB.kv_append(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(abi_version=3), "ABI"),
+    (dict(page_size=32), "PAGE_SIZE"),
+    (dict(B=-1), "SHAPE"),
+    (dict(max_new=-1), "SHAPE"),
+    (dict(pt_stride=0), "SHAPE"),
+    (dict(new_dtype=3), "DTYPE"),
+    (dict(kv_dtype=2), "DTYPE"),            # fp16 pool for bf16 rows
+    (dict(D=64), "UNSUPPORTED"),
+    (dict(H_kv=64), "UNSUPPORTED"),         # H_kv * D > 4096
+    (dict(v_new=None), "NULL"),
+    (dict(k_scale=None), "NULL"),
+    (dict(label_pool=None), "NULL"),
+    (dict(r=0), "SHAPE"),
+    (dict(r=129), "UNSUPPORTED"),
+    (dict(index_dtype=3), "DTYPE"),
+    (dict(index_k_pool=None), "NULL"),
+    (dict(D_i=64), "UNSUPPORTED"),
+    (dict(k_pool=ctypes.c_void_p(0x10004)), "UNSUPPORTED"),  # misaligned
+    (dict(page_table=None), "NULL"),
+])
+def test_append_rejections(kw, code):
+    assert _append(**kw) == E[code]
+
+
+def test_append_nothing_to_do():
+    assert LIB.kv_append(None, None) == E["NULL"]
+    assert _append(B=0, page_table=None, positions=None, n_new=None) == 0
+    assert _append(max_new=0) == 0
+    # every pool absent: a valid call that stores nothing
+    assert _append(k_new=None, channel_idx=None, index_k_new=None) == 0
 
 
 def _attn(**kw):

@@ -150,6 +150,46 @@ def test_full_ds_llama7b_b3_l20000_200_steps():
     torch.cuda.synchronize()
 
 
+def test_full_ds_llama7b_b3_200_steps_appended_on_gpu():
+    """The 200-step workload with each step's new token stored by kv_append
+    (K, V and its label row) before the step, from rows held aside; the
+    slots start as garbage. Steps 0, 100 and 199 are checked against the
+    oracle and the pools end equal to the generated ones."""
+    import top_sparse_decode_amd as tsd
+    step = _step()
+    wl = tsd_synth.make("ds_llama7b_b3_l20000_s200", DEV)
+    bufs = step.StepBuffers(wl)
+    base = wl["seq_lens"].clone()
+    pt = wl["page_table"]
+    B = base.shape[0]
+    pos = (base.long() - 1)[:, None] + torch.arange(200, device=DEV)[None]
+    slots = (pt.long().gather(1, pos // 64) * 64 + pos % 64)  # [B, 200]
+    keep = {n: wl[n].clone() for n in ("k_pool", "v_pool", "label_pool")}
+    k_rows = wl["k_pool"][slots]                              # [B, 200, H, D]
+    v_rows = wl["v_pool"][slots]
+    for n in keep:
+        wl[n][slots] = torch.randn_like(wl[n][slots])
+    one = torch.ones(B, dtype=torch.int32, device=DEV)
+    for s in range(200):
+        tsd.kv_append(pt, wl["num_pages"], pos[:, s].to(torch.int32), one, 1,
+                      k_new=k_rows[:, s:s + 1].contiguous(),
+                      v_new=v_rows[:, s:s + 1].contiguous(),
+                      k_pool=wl["k_pool"], v_pool=wl["v_pool"],
+                      channel_idx=wl["channel_idx"],
+                      label_pool=wl["label_pool"])
+        wl["seq_lens"] = base + s
+        wl["q"] = wl["step_q"][s].contiguous()
+        bufs.scores.fill_(float("nan"))
+        step.decode_step(wl, bufs)
+        if s in (0, 100, 199):
+            torch.cuda.synchronize()
+            print(f"step {s} len {int(wl['seq_lens'][0])}", flush=True)
+            _check_layer(wl, bufs, full_rows=[0, 95])
+    torch.cuda.synchronize()
+    for n, t in keep.items():
+        assert torch.equal(wl[n], t), n
+
+
 def test_full_qsa_decode_b8_l262144():
     wl = tsd_synth.make("qsa_decode_b8_l262144_k2048", DEV)
     bufs = _run(wl)

@@ -285,6 +285,114 @@ def test_sharded_qsa_pipeline_equals_unsharded():
     assert torch.equal(cnt, bufs.count.view(cfg.B))
 
 
+# ------------------------------------------------------------ cache append
+def _u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_append_fp8_kv_and_index_match_oracle():
+    import top_sparse_decode_amd as tsd
+    g = torch.Generator(device="cpu").manual_seed(70)
+    B, H, D, P, NP, max_new = 3, 4, 128, 6, 40, 150
+    pt = torch.randperm(NP, generator=g)[:B * P].view(B, P).to(torch.int32)
+    pt[2, 4] = NP + 3  # a bad page id: its tokens are skipped
+    positions = torch.tensor([0, 70, 250], dtype=torch.int32)
+    n_new = torch.tensor([150, 1, 140], dtype=torch.int32)  # 250+140 > 6*64
+    codes = torch.randint(0, 0x7E, (NP * 64, H, D), generator=g).to(torch.uint8)
+    codes |= (torch.rand(codes.shape, generator=g) < 0.5).to(torch.uint8) << 7
+    kp, vp = codes.clone(), codes.flip(0).contiguous()
+    ks = torch.rand(NP, generator=g) * 0.05 + 1e-3
+    vs = torch.rand(NP, generator=g) * 0.05 + 1e-3
+    kn = (torch.randn((B, max_new, H, D), generator=g) * 5).to(torch.bfloat16)
+    vn = (torch.randn((B, max_new, H, D), generator=g) * 5).to(torch.bfloat16)
+    ikp = torch.randint(0, 0x7E, (NP * 64, 128), generator=g).to(torch.uint8)
+    ikn = torch.randn((B, max_new, 128), generator=g) * 100
+    ref = oracle.kv_append(pt.numpy(), NP, positions.numpy(), n_new.numpy(),
+                           max_new, k_new=_u16(kn), v_new=_u16(vn),
+                           k_pool=kp.numpy(), v_pool=vp.numpy(),
+                           kv_enc="fp8_e4m3", k_scale=ks.numpy(),
+                           v_scale=vs.numpy(), index_k_new=ikn.numpy(),
+                           index_enc="f32", index_k_pool=ikp.numpy())
+    d = {n: t.to(DEV) for n, t in dict(pt=pt, pos=positions, n=n_new, kp=kp,
+                                       vp=vp, ks=ks, vs=vs, kn=kn, vn=vn,
+                                       ikp=ikp, ikn=ikn).items()}
+    tsd.kv_append(d["pt"], NP, d["pos"], d["n"], max_new, k_new=d["kn"],
+                  v_new=d["vn"], k_pool=d["kp"], v_pool=d["vp"],
+                  k_scale=d["ks"], v_scale=d["vs"], index_k_new=d["ikn"],
+                  index_k_pool=d["ikp"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(d["ks"].cpu().numpy(), ref["k_scale"])
+    np.testing.assert_array_equal(d["vs"].cpu().numpy(), ref["v_scale"])
+    np.testing.assert_array_equal(d["kp"].cpu().numpy(), ref["k_pool"])
+    np.testing.assert_array_equal(d["vp"].cpu().numpy(), ref["v_pool"])
+    np.testing.assert_array_equal(d["ikp"].cpu().numpy(), ref["index_k_pool"])
+    # request 1 appends at 70 onto a page begun at 64: its scale is kept
+    assert d["ks"][pt[1, 1]].item() == ks[pt[1, 1]].item()
+
+
+def test_append_16bit_rows_and_label_match_oracle():
+    import top_sparse_decode_amd as tsd
+    g = torch.Generator(device="cpu").manual_seed(71)
+    B, H, D, P, NP, r, max_new = 2, 8, 128, 5, 12, 16, 70
+    pt = torch.randperm(NP, generator=g)[:B * P].view(B, P).to(torch.int32)
+    pt[0, 2] = -1
+    positions = torch.tensor([100, 5], dtype=torch.int32)
+    n_new = torch.tensor([70, 64], dtype=torch.int32)
+    ch = torch.stack([torch.randperm(D, generator=g)[:r] for _ in range(H)]).to(torch.int32)
+    ch[3, 0], ch[5, 7] = -1, 200  # outside [0, D): stores 0
+    kp = torch.randn((NP * 64, H, D), generator=g).to(torch.float16)
+    vp = torch.randn((NP * 64, H, D), generator=g).to(torch.float16)
+    lp = torch.randn((NP * 64, H, r), generator=g).to(torch.float16)
+    kn = torch.randn((B, max_new, H, D), generator=g).to(torch.float16)
+    vn = torch.randn((B, max_new, H, D), generator=g).to(torch.float16)
+    ref = oracle.kv_append(pt.numpy(), NP, positions.numpy(), n_new.numpy(),
+                           max_new, k_new=_u16(kn), v_new=_u16(vn),
+                           new_enc="fp16", k_pool=_u16(kp), v_pool=_u16(vp),
+                           kv_enc="fp16", channel_idx=ch.numpy(),
+                           label_pool=_u16(lp))
+    d = {n: t.to(DEV) for n, t in dict(pt=pt, pos=positions, n=n_new, kp=kp,
+                                       vp=vp, lp=lp, kn=kn, vn=vn, ch=ch).items()}
+    tsd.kv_append(d["pt"], NP, d["pos"], d["n"], max_new, k_new=d["kn"],
+                  v_new=d["vn"], k_pool=d["kp"], v_pool=d["vp"],
+                  channel_idx=d["ch"], label_pool=d["lp"])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(_u16(d["kp"]), ref["k_pool"])
+    np.testing.assert_array_equal(_u16(d["vp"]), ref["v_pool"])
+    np.testing.assert_array_equal(_u16(d["lp"]), ref["label_pool"])
+
+
+def test_append_index_fp8_encode_every_case():
+    """The gfx950 converter behind kv_append gives the oracle's code for
+    every finite E4M3 value, every midpoint and its neighbours, the
+    subnormal range, signed zeros and out-of-range magnitudes."""
+    import top_sparse_decode_amd as tsd
+    vals = [oracle.decode_fp8_e4m3(c) for c in range(256) if c & 0x7F != 0x7F]
+    pos = [oracle.decode_fp8_e4m3(c) for c in range(0x7F)]
+    for c in range(0x7E):
+        mid = (pos[c] + pos[c + 1]) / 2
+        for m in (mid, np.nextafter(np.float32(mid), np.float32(0)),
+                  np.nextafter(np.float32(mid), np.float32(1e9))):
+            vals += [float(m), -float(m)]
+    vals += [448.0, 463.9, 464.0, 480.0, 1e6, -1e30, 0.0, -0.0, 2.0 ** -12,
+             -2.0 ** -11, 1e-30, 3e38]
+    x = np.array(vals, np.float32)
+    n = -(-len(x) // 128)
+    xs = np.zeros(n * 128, np.float32)
+    xs[:len(x)] = x
+    ikn = torch.from_numpy(xs.reshape(1, n, 128))
+    pt = torch.arange((n + 63) // 64, dtype=torch.int32)[None]
+    ikp = torch.zeros((pt.shape[1] * 64, 128), dtype=torch.uint8)
+    ref = oracle.kv_append(pt.numpy(), pt.shape[1], [0], [n], n,
+                           index_k_new=ikn.numpy(), index_enc="f32",
+                           index_k_pool=ikp.numpy())
+    gi = ikp.to(DEV)
+    tsd.kv_append(pt.to(DEV), pt.shape[1], torch.zeros(1, dtype=torch.int32, device=DEV),
+                  torch.tensor([n], dtype=torch.int32, device=DEV), n,
+                  index_k_new=ikn.to(DEV), index_k_pool=gi)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gi.cpu().numpy(), ref["index_k_pool"])
+
+
 def test_topk_row_lens_clamped_to_max_len():
     rng = np.random.default_rng(9)
     s = rng.normal(size=(2, 5000)).astype(np.float32)

@@ -21,7 +21,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtsd.so")
 
-TSD_BF16, TSD_FP16, TSD_FP8_E4M3 = 1, 2, 3
+TSD_BF16, TSD_FP16, TSD_FP8_E4M3, TSD_F32 = 1, 2, 3, 4
 TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX = 1, 2
 ABI_VERSION = 1
 PAGE_SIZE = 64
@@ -57,6 +57,20 @@ class AttnArgs(ctypes.Structure):
     ]
 
 
+class AppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", _I32), ("B", _I32), ("page_size", _I32),
+        ("max_new", _I32), ("page_table", _P), ("pt_stride", _I64),
+        ("num_pages", _I64), ("positions", _P), ("n_new", _P),
+        ("H_kv", _I32), ("D", _I32), ("new_dtype", _I32), ("kv_dtype", _I32),
+        ("k_new", _P), ("v_new", _P), ("k_pool", _P), ("v_pool", _P),
+        ("k_scale", _P), ("v_scale", _P), ("channel_idx", _P),
+        ("label_pool", _P), ("r", _I32), ("index_dtype", _I32),
+        ("index_k_new", _P), ("index_k_pool", _P), ("D_i", _I32),
+        ("reserved0", _I32),
+    ]
+
+
 class TsdError(RuntimeError):
     def __init__(self, fn, status):
         self.status = status
@@ -84,6 +98,8 @@ def _load():
                                               ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _P, _P, _P]),
         "sparse_gqa_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _P]),
+        "kv_append": (ctypes.c_int, [ctypes.POINTER(AppendArgs), _P]),
+        "tsd_sizeof_append_args": (ctypes.c_size_t, []),
         "lse_merge": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _P, _P, _P]),
         "tsd_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -97,7 +113,8 @@ def _load():
     if lib.tsd_abi_version() != ABI_VERSION:
         raise ImportError("libtsd.so ABI version mismatch")
     if (lib.tsd_sizeof_score_args() != ctypes.sizeof(ScoreArgs)
-            or lib.tsd_sizeof_attn_args() != ctypes.sizeof(AttnArgs)):
+            or lib.tsd_sizeof_attn_args() != ctypes.sizeof(AttnArgs)
+            or lib.tsd_sizeof_append_args() != ctypes.sizeof(AppendArgs)):
         raise ImportError("libtsd.so argument struct layout mismatch")
     return lib
 
@@ -105,8 +122,9 @@ def _load():
 _lib = _load()
 EXPORTS = ("sparse_index_score", "sparse_index_topk",
            "topk_select_workspace_bytes", "topk_select", "topk_merge_sharded",
-           "sparse_gqa_decode", "lse_merge", "tsd_strerror", "tsd_abi_version",
-           "tsd_sizeof_score_args", "tsd_sizeof_attn_args")
+           "sparse_gqa_decode", "lse_merge", "kv_append", "tsd_strerror",
+           "tsd_abi_version", "tsd_sizeof_score_args", "tsd_sizeof_attn_args",
+           "tsd_sizeof_append_args")
 
 
 # ----------------------------------------------------------------- helpers
@@ -304,6 +322,65 @@ def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
     a.o_part, a.lse_part = _ptr(o_part), _ptr(lse_part)
     _check("sparse_gqa_decode", _lib.sparse_gqa_decode(ctypes.byref(a),
                                                        _stream(stream)))
+
+
+def kv_append(page_table, num_pages, positions, n_new, max_new, *,
+              k_new=None, v_new=None, k_pool=None, v_pool=None, k_scale=None,
+              v_scale=None, channel_idx=None, label_pool=None,
+              index_k_new=None, index_k_pool=None, stream=None,
+              prepare=False):
+    """Store new tokens' rows: ``k_new``/``v_new`` [B, max_new, H_kv, 128]
+    (bf16/fp16) into ``k_pool``/``v_pool`` (same encoding, or FP8 with
+    ``k_scale``/``v_scale`` [num_pages]); the label rows K[channel_idx] into
+    ``label_pool``; ``index_k_new`` [B, max_new, 128] (bf16/fp16/f32) into
+    the FP8 ``index_k_pool``. Token positions[b] + i, i < n_new[b].
+    With ``prepare=True`` nothing is launched: the marshalled call is
+    returned as a function of no arguments (it returns the C status)."""
+    _dev("page_table", page_table, torch.int32)
+    _dev("positions", positions, torch.int32)
+    _dev("n_new", n_new, torch.int32)
+    _dev("k_new", k_new, dtypes=_HALF)
+    _dev("v_new", v_new, dtypes=_HALF)
+    _dev("k_pool", k_pool, dtypes=_HALF + _FP8)
+    _dev("v_pool", v_pool, dtypes=_HALF + _FP8)
+    _dev("k_scale", k_scale, torch.float32)
+    _dev("v_scale", v_scale, torch.float32)
+    _dev("channel_idx", channel_idx, torch.int32)
+    _dev("label_pool", label_pool, dtypes=_HALF)
+    _dev("index_k_new", index_k_new, dtypes=_HALF + (torch.float32,))
+    _dev("index_k_pool", index_k_pool, dtypes=_FP8)
+    a = AppendArgs()
+    a.abi_version, a.page_size = ABI_VERSION, PAGE_SIZE
+    a.B, a.max_new = page_table.shape[0], int(max_new)
+    a.page_table, a.pt_stride = _ptr(page_table), page_table.shape[1]
+    a.num_pages = int(num_pages)
+    a.positions, a.n_new = _ptr(positions), _ptr(n_new)
+    src = k_new if k_new is not None else None
+    if src is not None:
+        a.H_kv, a.D = src.shape[2], src.shape[3]
+        a.new_dtype = _half_code(src)
+    if k_pool is not None:
+        a.k_new, a.v_new = _ptr(k_new), _ptr(v_new)
+        a.k_pool, a.v_pool, a.kv_dtype = _ptr(k_pool), _ptr(v_pool), _kv_code(k_pool)
+        a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    if channel_idx is not None:
+        a.k_new = _ptr(k_new)
+        a.channel_idx, a.r = _ptr(channel_idx), channel_idx.shape[1]
+        a.label_pool = _ptr(label_pool)
+    if index_k_new is not None:
+        a.index_k_new, a.index_k_pool = _ptr(index_k_new), _ptr(index_k_pool)
+        a.index_dtype = (TSD_F32 if index_k_new.dtype == torch.float32
+                         else _half_code(index_k_new))
+        a.D_i = index_k_new.shape[2]
+    if prepare:
+        st = _stream(stream)
+        ref = ctypes.byref(a)
+        fn = _lib.kv_append
+        keep = (page_table, positions, n_new, k_new, v_new, k_pool, v_pool,
+                k_scale, v_scale, channel_idx, label_pool, index_k_new,
+                index_k_pool)  # the tensors stay alive with the call
+        return lambda keep=keep: fn(ref, st)
+    _check("kv_append", _lib.kv_append(ctypes.byref(a), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, out_lse=None, stream=None):

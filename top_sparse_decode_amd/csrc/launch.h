@@ -40,6 +40,8 @@ hipError_t launch_topk_merge_sharded(const float* scores, int64_t stride,
                                      int rows, int kl, int k, int32_t* idx,
                                      int32_t* count, hipStream_t s);
 
+hipError_t launch_kv_append(const tsd_append_args& a, hipStream_t s);
+
 hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s);
 
 hipError_t launch_lse_merge(const float* o_part, const float* lse_part,

@@ -201,6 +201,53 @@ int topk_merge_sharded(const float* scores, int64_t stride,
       stream));
 }
 
+static bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int kv_append(const tsd_append_args* a, hipStream_t stream) {
+  if (!a) return TSD_E_NULL;
+  if (a->abi_version != TSD_ABI_VERSION) return TSD_E_ABI;
+  if (a->page_size != TSD_PAGE_SIZE) return TSD_E_PAGE_SIZE;
+  if (a->B < 0 || a->max_new < 0 || a->pt_stride < 1 || a->num_pages < 0)
+    return TSD_E_SHAPE;
+  if (a->B > 65535) return TSD_E_UNSUPPORTED;
+  const bool kv = a->k_new != nullptr, label = a->channel_idx != nullptr,
+             index = a->index_k_new != nullptr;
+  if (kv || label) {
+    if (a->new_dtype != TSD_BF16 && a->new_dtype != TSD_FP16) return TSD_E_DTYPE;
+    if (a->H_kv < 1 || a->D < 1) return TSD_E_SHAPE;
+    if (a->D != TSD_HEAD_DIM || a->H_kv * a->D > 4096) return TSD_E_UNSUPPORTED;
+  }
+  if (kv) {
+    if (a->kv_dtype != a->new_dtype && a->kv_dtype != TSD_FP8_E4M3)
+      return TSD_E_DTYPE;
+    if (!a->v_new || !a->k_pool || !a->v_pool) return TSD_E_NULL;
+    if (a->kv_dtype == TSD_FP8_E4M3 && (!a->k_scale || !a->v_scale))
+      return TSD_E_NULL;
+    if (!aligned16(a->k_new) || !aligned16(a->v_new) ||
+        !aligned16(a->k_pool) || !aligned16(a->v_pool))
+      return TSD_E_UNSUPPORTED;
+  }
+  if (label) {
+    if (!a->k_new || !a->label_pool) return TSD_E_NULL;
+    if (a->r < 1) return TSD_E_SHAPE;
+    if (a->r > a->D) return TSD_E_UNSUPPORTED;
+  }
+  if (index) {
+    if (a->index_dtype != TSD_BF16 && a->index_dtype != TSD_FP16 &&
+        a->index_dtype != TSD_F32)
+      return TSD_E_DTYPE;
+    if (!a->index_k_pool) return TSD_E_NULL;
+    if (a->D_i != TSD_HEAD_DIM) return TSD_E_UNSUPPORTED;
+    if (!aligned16(a->index_k_new) || !aligned16(a->index_k_pool))
+      return TSD_E_UNSUPPORTED;
+  }
+  if (a->B == 0 || a->max_new == 0 || !(kv || label || index)) return TSD_OK;
+  if (!a->page_table || !a->positions || !a->n_new) return TSD_E_NULL;
+  return launch_status(tsd::launch_kv_append(*a, stream));
+}
+
 int sparse_gqa_decode(const tsd_attn_args* a, hipStream_t stream) {
   const int rc = validate_attn(a);
   if (rc) return rc;
@@ -240,5 +287,6 @@ const char* tsd_strerror(int status) {
 int tsd_abi_version(void) { return TSD_ABI_VERSION; }
 size_t tsd_sizeof_score_args(void) { return sizeof(tsd_score_args); }
 size_t tsd_sizeof_attn_args(void) { return sizeof(tsd_attn_args); }
+size_t tsd_sizeof_append_args(void) { return sizeof(tsd_append_args); }
 
 }  // extern "C"
