@@ -259,9 +259,14 @@ int topk_merge_sharded(const float *scores, int64_t stride,
  *   k_scale, v_scale [num_pages] f32 (FP8 only; NULL otherwise)
  *   idx      [B, H_sel, k] int32 ascending, -1 padded   count [B, H_sel]
  *   o_part   [B, H_q, chunks, D] f32     lse_part [B, H_q, chunks] f32
+ * Sparse-decode threshold ("Support double sparsity", Speedup Evaluation:
+ * short contexts decode densely): a request whose length len (clamped to
+ * pt_stride * 64) is at most dense_len attends to every token 0 .. len-1 as
+ * its selection (m = len; idx and count are not read for it). dense_len = 0
+ * turns this off.
  * For a 16-bit cache q must have the cache's encoding; an FP8 cache takes
  * bf16 or fp16 queries. H_q % H_kv == 0, G <= 16, 1 <= chunks <= 64,
- * 1 <= k <= 4096.
+ * 1 <= k <= 4096, dense_len >= 0.
  * ------------------------------------------------------------------------ */
 typedef struct tsd_attn_args {
   int32_t abi_version;           /* TSD_ABI_VERSION                          */
@@ -289,6 +294,8 @@ typedef struct tsd_attn_args {
   float softmax_scale;           /* usually 1/sqrt(D)                        */
   float *o_part;
   float *lse_part;
+  int32_t dense_len;             /* requests with len <= dense_len: dense    */
+  int32_t reserved0;
 } tsd_attn_args;
 
 int sparse_gqa_decode(const tsd_attn_args *a, hipStream_t stream);

@@ -251,6 +251,7 @@ def _attn(**kw):
     (dict(k_scale=None), "NULL"),
     (dict(idx=None), "NULL"),
     (dict(page_size=128), "PAGE_SIZE"),
+    (dict(dense_len=-1), "SHAPE"),
 ])
 def test_attn_rejections(kw, code):
     assert _attn(**kw) == E[code]

@@ -130,6 +130,8 @@ def test_qsa_causal_prefill_rows():
                 steps=0)),
     (DS8B, dict(B=2, lens=(777, 300), r=12, n_outlier=12, top_k=64, chunks=2)),
     ("ds_tiny_b1_l4096", dict(lens=(4096,))),
+    (DS8B, dict(B=2, lens=(2000, 900), top_k=128, chunks=3, channel_type="q")),
+    (DS8B, dict(B=2, lens=(2000, 900), top_k=128, chunks=3, channel_type="qk")),
 ])
 def test_ds_decode_path(name, over):
     cfg = tsd_synth.config(name, seed=111, **over)
@@ -283,6 +285,39 @@ def test_sharded_qsa_pipeline_equals_unsharded():
     assert lens.sum(0).tolist() == list(cfg.lens)
     assert torch.equal(idx, bufs.idx.view(cfg.B, cfg.top_k))
     assert torch.equal(cnt, bufs.count.view(cfg.B))
+
+
+# -------------------------------------------------- sparse-decode threshold
+@pytest.mark.parametrize("name,lens,dense_len", [
+    ("ds_llama31_8b_b3_l60000", (300, 5000, 1000), 1000),
+    (QSA, (700, 9000, 2048, 64), 2048),
+])
+def test_dense_threshold_requests_attend_to_every_token(name, lens, dense_len):
+    """Requests no longer than dense_len attend densely (selection = every
+    token, through the chunked kernel); the others keep their top-k."""
+    cfg = tsd_synth.config(name, B=len(lens), lens=lens, top_k=256, chunks=5,
+                           seed=180)
+    wl = tsd_synth.make(cfg, DEV)
+    wl["dense_len"] = dense_len
+    bufs = _run(wl)
+    h = tsd_synth.to_host(wl)
+    H_sel = bufs.H_sel
+    kmax = max(max(lens), cfg.top_k)
+    idx = np.full((cfg.B, H_sel, kmax), -1, np.int32)
+    cnt = np.zeros((cfg.B, H_sel), np.int32)
+    gidx = bufs.idx.view(cfg.B, H_sel, cfg.top_k).cpu().numpy()
+    gcnt = bufs.count.view(cfg.B, H_sel).cpu().numpy()
+    for b, n in enumerate(lens):
+        if n <= dense_len:
+            idx[b, :, :n] = np.arange(n)
+            cnt[b] = n
+        else:
+            idx[b, :, :cfg.top_k] = gidx[b]
+            cnt[b] = gcnt[b]
+    check_attention_on(h, idx, cnt, cfg.chunks, bufs.o_part.cpu().numpy(),
+                       bufs.lse_part.cpu().numpy(), out_tol(cfg.kv_enc))
+    check_merge(bufs.o_part.cpu().numpy(), bufs.lse_part.cpu().numpy(),
+                bufs.out.cpu().numpy(), bufs.out_lse.cpu().numpy())
 
 
 # ------------------------------------------------------------ cache append

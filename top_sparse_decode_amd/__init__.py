@@ -53,7 +53,7 @@ class AttnArgs(ctypes.Structure):
         ("pt_stride", _I64), ("seq_lens", _P), ("num_pages", _I64),
         ("idx", _P), ("count", _P), ("H_sel", _I32), ("k", _I32),
         ("chunks", _I32), ("softmax_scale", _F32), ("o_part", _P),
-        ("lse_part", _P),
+        ("lse_part", _P), ("dense_len", _I32), ("reserved0", _I32),
     ]
 
 
@@ -291,7 +291,8 @@ def topk_merge_sharded(scores, idx_local, count_local, k, idx, count=None,
 
 def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
                       count, chunks, o_part, lse_part, k_scale=None,
-                      v_scale=None, softmax_scale=None, stream=None):
+                      v_scale=None, softmax_scale=None, dense_len=0,
+                      stream=None):
     """Chunked sparse GQA attention over the selection ``idx`` [B,H_sel,k]
     into ``o_part`` [B,H_q,chunks,128] and ``lse_part`` [B,H_q,chunks]."""
     _dev("q", q, dtypes=_HALF)
@@ -320,6 +321,7 @@ def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
     a.softmax_scale = (1.0 / math.sqrt(a.D) if softmax_scale is None
                        else float(softmax_scale))
     a.o_part, a.lse_part = _ptr(o_part), _ptr(lse_part)
+    a.dense_len = int(dense_len)
     _check("sparse_gqa_decode", _lib.sparse_gqa_decode(ctypes.byref(a),
                                                        _stream(stream)))
 

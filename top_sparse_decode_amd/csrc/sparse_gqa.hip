@@ -6,8 +6,9 @@
 //
 // One workgroup (4 waves) per (request b, KV head g, chunk c) handles the G
 // query heads of the group over the chunk's run of the ascending selection
-// list, one tile of tokens at a time (128 tokens for FP8 rows, 64 for 16-bit
-// rows, so a tile's K and V fit LDS):
+// list (every token 0 .. len-1 for a request at or below the sparse-decode
+// threshold), one tile of tokens at a time (128 tokens for FP8 rows, 64 for
+// 16-bit rows, so a tile's K and V fit LDS):
 //   1. the tile's slots are resolved from the page table; an index outside
 //      [0, len) or a page outside [0, num_pages) is masked and never read;
 //   2. the K and V rows are gathered into LDS with 16-byte loads (a token's
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     const int32_t* __restrict__ seq_lens, int64_t num_pages,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
     int H_sel, int k, int C, float softmax_scale, float* __restrict__ o_part,
-    float* __restrict__ lse_part) {
+    float* __restrict__ lse_part, int dense_len) {
   using T = Tile<ENC>;
   constexpr int NT = T::kTokens;
   constexpr bool fp8 = ENC == TSD_FP8_E4M3;
@@ -122,13 +123,16 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
   // The chunk bounds depend on the selection's length m, which is k for
   // every row longer than k: the first tile's entries for m = k are loaded
   // together with the count and kept wherever they match the real bounds.
+  const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
+  // at or below the sparse-decode threshold the selection is every token
+  const bool dense = n <= dense_len;
   const int64_t lo_s = c * static_cast<int64_t>(k) / C;
   const int64_t hi_s = (c + 1) * static_cast<int64_t>(k) / C;
   int32_t t_spec = -1;
-  if (tid < NT && lo_s + tid < hi_s) t_spec = sel[lo_s + tid];
-  const int64_t m = clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
+  if (!dense && tid < NT && lo_s + tid < hi_s) t_spec = sel[lo_s + tid];
+  const int64_t m =
+      dense ? n : clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
   const int64_t lo = c * m / C, hi = (c + 1) * m / C;
-  const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
   const float zscale = softmax_scale * kLog2e;
 
@@ -160,8 +164,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       int64_t slot = -1;
       float ksc = 0.f, vsc = 0.f;
       if (tid < tn) {
-        const bool spec = base == lo_s && lo_s + tid < hi_s;
-        const int64_t t = spec ? t_spec : sel[base + tid];
+        const bool spec = !dense && base == lo_s && lo_s + tid < hi_s;
+        const int64_t t = dense ? base + tid : (spec ? t_spec : sel[base + tid]);
         if (t >= 0 && t < n) {
           const int32_t page = pt[t / kPage];
           if (page >= 0 && page < num_pages) {
@@ -309,7 +313,7 @@ hipError_t launch_enc(const tsd_attn_args& a, hipStream_t s) {
                      static_cast<const uint8_t*>(a.v_pool), a.k_scale,
                      a.v_scale, a.page_table, a.pt_stride, a.seq_lens,
                      a.num_pages, a.idx, a.count, a.H_sel, a.k, a.chunks,
-                     a.softmax_scale, a.o_part, a.lse_part);
+                     a.softmax_scale, a.o_part, a.lse_part, a.dense_len);
   return hipGetLastError();
 }
 

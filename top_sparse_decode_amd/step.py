@@ -90,7 +90,8 @@ def attend(layer, bufs, stream=None):
                       layer["num_pages"], bufs.idx.view(B, bufs.H_sel, k),
                       bufs.count.view(B, bufs.H_sel), layer["chunks"],
                       bufs.o_part, bufs.lse_part, k_scale=layer.get("k_scale"),
-                      v_scale=layer.get("v_scale"), stream=stream)
+                      v_scale=layer.get("v_scale"),
+                      dense_len=layer.get("dense_len", 0), stream=stream)
 
 
 def merge(layer, bufs, stream=None):

@@ -70,6 +70,7 @@ class Config:
     lens: Optional[tuple] = None
     stale_tail: bool = False     # out-of-range page ids past each request's pages
     spare_pages: int = 0
+    channel_type: str = "k"      # heavy channels by mean |K|, |q| or |q_c K_c|
 
 
 WORKLOADS = {
@@ -198,22 +199,37 @@ def _kv_pool(cfg, tag, slots, device, layer, outliers=None):
 
 
 def heavy_channels(k_pool: torch.Tensor, seq_lens, page_table, r: int,
-                   prefix_len: int):
-    """Offline channel choice standing in for calibration: per KV head, the r
-    channels with the largest mean |K| over the first ``prefix_len`` tokens of
-    every request (ties to the lower channel), listed in ascending order."""
+                   prefix_len: int, channel_type: str = "k", q=None):
+    """Offline channel choice standing in for calibration ("Support double
+    sparsity": heavy channels of type k, q or qk): per KV head, the r
+    channels with the largest mean statistic over the first ``prefix_len``
+    tokens of every request (ties to the lower channel), listed in ascending
+    order. Statistic: |K| (type k); |q| over the group's query heads and the
+    requests (type q, from ``q`` [B, H_q, D]); |q_c K_c| with q summed over
+    the group (type qk)."""
     H_kv, D = k_pool.shape[1], k_pool.shape[2]
-    acc = torch.zeros((H_kv, D), dtype=torch.float64, device=k_pool.device)
+    dev = k_pool.device
+    acc = torch.zeros((H_kv, D), dtype=torch.float64, device=dev)
     cnt = 0
     B = page_table.shape[0]
-    page_table = page_table.to(k_pool.device)
-    t = torch.arange(prefix_len, device=k_pool.device)
-    for b in range(B):
-        n = min(prefix_len, int(seq_lens[b]))
-        tt = t[:n]
-        slots = page_table[b, (tt // PAGE_SIZE)].long() * PAGE_SIZE + tt % PAGE_SIZE
-        acc += k_pool[slots].abs().to(torch.float64).sum(dim=0)
-        cnt += n
+    page_table = page_table.to(dev)
+    if channel_type in ("q", "qk"):
+        G = q.shape[1] // H_kv
+        qg = q.to(dev).to(torch.float64).view(B, H_kv, G, D)
+    if channel_type == "q":
+        acc = qg.abs().sum(dim=(0, 2))
+        cnt = B * G
+    else:
+        t = torch.arange(prefix_len, device=dev)
+        for b in range(B):
+            n = min(prefix_len, int(seq_lens[b]))
+            tt = t[:n]
+            slots = page_table[b, (tt // PAGE_SIZE)].long() * PAGE_SIZE + tt % PAGE_SIZE
+            kk = k_pool[slots].to(torch.float64)
+            if channel_type == "qk":
+                kk = kk * qg[b].sum(dim=1)[None]
+            acc += kk.abs().sum(dim=0)
+            cnt += n
     mean = acc / max(1, cnt)
     ch = torch.empty((H_kv, r), dtype=torch.int32, device=k_pool.device)
     for g in range(H_kv):
@@ -247,7 +263,7 @@ def make(cfg, device="cpu", layer: int = 0) -> dict:
         k_pool, _ = _kv_pool(cfg, "k", slots, device, layer, outliers)
         v_pool, _ = _kv_pool(cfg, "v", slots, device, layer)
         chan = heavy_channels(k_pool, seq_lens.cpu(), pt.cpu(), cfg.r,
-                              cfg.L)
+                              cfg.L, cfg.channel_type, wl["q"])
         chan = chan.to(device)
         label = torch.gather(
             k_pool, 2,
