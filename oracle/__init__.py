@@ -71,6 +71,9 @@ def _load():
         "tsd_oracle_topk_merge_sharded": (I, [P, L, P, P, I, I, I, I, I, P,
                                               P]),
         "tsd_oracle_encode_fp8e4m3": (ctypes.c_uint8, [D]),
+        "tsd_oracle_index_k_compress": (I, [I, I, P, P, L, L, P, P, P, L, L,
+                                            I, I, P]),
+        "tsd_oracle_expand_blocks": (I, [I, P, P, I, I, P, I, P, P]),
         "tsd_oracle_kv_append": (I, [I, L, P, L, I, P, P, I, I, I, P, P, I, P,
                                      P, I, P, P, P, I, P, P, I, P, I]),
         "tsd_oracle_sparse_attention": (I, [I, I, I, I, I, I, I, P, I, P, P, I,
@@ -261,6 +264,35 @@ def kv_append(page_table, num_pages, positions, n_new, max_new, *,
     out.update(k_pool=kp, v_pool=vp, k_scale=ks, v_scale=vs, label_pool=lp,
                index_k_pool=ikp)
     return out
+
+
+def index_k_compress(index_k, page_table, num_pages, seq_lens, from_block,
+                     cpage_table, num_cpages, ck_pool, Bs, page_size=64):
+    """Block-compressed index keys on host copies -> updated ck_pool
+    (uint8 [cslots, D_i])."""
+    ik = _c(index_k, np.uint8)
+    pt = _c(page_table, np.int32)
+    cpt = _c(cpage_table, np.int32)
+    out = _c(ck_pool, np.uint8).copy()
+    B = pt.shape[0]
+    _check(_load().tsd_oracle_index_k_compress(
+        B, Bs, _ptr(ik), _ptr(pt), pt.shape[1], int(num_pages),
+        _ptr(_c(seq_lens, np.int32)), _ptr(_c(from_block, np.int32)),
+        _ptr(cpt), cpt.shape[1], int(num_cpages), page_size, ik.shape[1],
+        _ptr(out)))
+    return out
+
+
+def expand_blocks(sel, count, Bs, row_lens, kt):
+    """Selected blocks [rows, kb] -> (tokens int32 [rows, kt], count)."""
+    sl = _c(sel, np.int32)
+    rows, kb = sl.shape
+    tok = np.empty((rows, kt), np.int32)
+    cnt = np.empty(rows, np.int32)
+    _check(_load().tsd_oracle_expand_blocks(
+        rows, _ptr(sl), _ptr(_c(count, np.int32)), kb, Bs,
+        _ptr(_c(row_lens, np.int32)), kt, _ptr(tok), _ptr(cnt)))
+    return tok, cnt
 
 
 def topk_merge_sharded(scores, idx, count, k, page_size=64):

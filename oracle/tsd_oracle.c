@@ -467,6 +467,69 @@ int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
   return ORC_OK;
 }
 
+/* ------------------------------------------------------ block compression */
+
+int tsd_oracle_index_k_compress(int B, int Bs, const uint8_t *index_k_pool,
+                                const int32_t *page_table, int64_t pt_stride,
+                                int64_t num_pages, const int32_t *seq_lens,
+                                const int32_t *from_block,
+                                const int32_t *cpage_table, int64_t cpt_stride,
+                                int64_t num_cpages, int page_size, int D_i,
+                                uint8_t *ck_pool) {
+  if (B < 0 || Bs < 1 || page_size < 1 || D_i < 1) return ORC_E_ARG;
+  double *acc = (double *)malloc(sizeof(double) * (size_t)D_i);
+  if (!acc) return ORC_E_ARG;
+  for (int b = 0; b < B; ++b) {
+    int64_t n = seq_lens[b] < 0 ? 0 : seq_lens[b];
+    if (n > pt_stride * page_size) n = pt_stride * page_size;
+    const int64_t nblk = (n + Bs - 1) / Bs;
+    for (int64_t j = from_block[b] < 0 ? 0 : from_block[b]; j < nblk; ++j) {
+      if (j >= cpt_stride * page_size) break;
+      const int32_t cpage = cpage_table[(int64_t)b * cpt_stride + j / page_size];
+      if (cpage < 0 || cpage >= num_cpages) continue;
+      const int64_t t0 = j * Bs, t1 = (j + 1) * Bs < n ? (j + 1) * Bs : n;
+      int ok = 1;
+      for (int d = 0; d < D_i; ++d) acc[d] = 0.0;
+      for (int64_t t = t0; t < t1 && ok; ++t) {
+        const int32_t page = page_table[(int64_t)b * pt_stride + t / page_size];
+        if (page < 0 || page >= num_pages) { ok = 0; break; }
+        const int64_t slot = (int64_t)page * page_size + t % page_size;
+        for (int d = 0; d < D_i; ++d)
+          acc[d] += tsd_oracle_decode_fp8e4m3(index_k_pool[slot * D_i + d]);
+      }
+      if (!ok) continue;
+      const int64_t cslot = (int64_t)cpage * page_size + j % page_size;
+      for (int d = 0; d < D_i; ++d) {
+        const float mean = (float)(acc[d] / (double)(t1 - t0));
+        ck_pool[cslot * D_i + d] = tsd_oracle_encode_fp8e4m3(mean);
+      }
+    }
+  }
+  free(acc);
+  return ORC_OK;
+}
+
+int tsd_oracle_expand_blocks(int rows, const int32_t *sel, const int32_t *count,
+                             int kb, int Bs, const int32_t *row_lens, int kt,
+                             int32_t *tok, int32_t *tok_count) {
+  if (rows < 0 || kb < 1 || Bs < 1 || kt < 1) return ORC_E_ARG;
+  for (int row = 0; row < rows; ++row) {
+    const int64_t n = row_lens[row] < 0 ? 0 : row_lens[row];
+    int32_t c = count[row] < 0 ? 0 : count[row];
+    if (c > kb) c = kb;
+    int64_t m = 0;
+    for (int32_t i = 0; i < c; ++i) {
+      const int64_t j = sel[(int64_t)row * kb + i];
+      if (j < 0) continue;
+      for (int64_t t = j * Bs; t < (j + 1) * Bs && t < n && m < kt; ++t)
+        tok[(int64_t)row * kt + m++] = (int32_t)t;
+    }
+    for (int64_t i = m; i < kt; ++i) tok[(int64_t)row * kt + i] = -1;
+    if (tok_count) tok_count[row] = (int32_t)m;
+  }
+  return ORC_OK;
+}
+
 /* --------------------------------------------------------------- attention */
 
 /* Dequantised element d of token slot, KV head g. */

@@ -140,6 +140,35 @@ int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
                          void *label_pool, const void *index_k_new,
                          int index_dtype, void *index_k_pool, int D_i);
 
+/* Block-compressed index keys ("QSA cache sharding": QSA compressed cache
+ * and compressed blocks chosen by top-k; "Context parallelism for QSA
+ * attention and the sparse indexer": block compression of the raw index-K
+ * before scoring). Block j of request b holds its tokens
+ * [j*Bs, min((j+1)*Bs, len_b)); its key is the mean of their decoded FP8
+ * index keys, computed exactly in double, rounded to f32, then encoded to
+ * FP8 (nearest, ties to even, saturating). Blocks
+ * [from_block[b], ceil(len_b / Bs)) are written, into a paged pool of
+ * compressed keys: block j of request b lives at slot
+ * cpage_table[b][j / page_size] * page_size + j % page_size of ck_pool
+ * [cslots][D_i]. Token pages and compressed pages outside their pools are
+ * skipped (a block with a token on a bad page is not written). */
+int tsd_oracle_index_k_compress(int B, int Bs, const uint8_t *index_k_pool,
+                                const int32_t *page_table, int64_t pt_stride,
+                                int64_t num_pages, const int32_t *seq_lens,
+                                const int32_t *from_block,
+                                const int32_t *cpage_table, int64_t cpt_stride,
+                                int64_t num_cpages, int page_size, int D_i,
+                                uint8_t *ck_pool);
+
+/* Expansion of selected blocks to their tokens: for each row, the blocks
+ * sel[row][0 .. count[row]) (ascending) become the tokens
+ * [j*Bs, min((j+1)*Bs, len_row)) in ascending order, written to
+ * tok[row][0 .. m) and padded with -1 up to kt; tok_count[row] = m (at most
+ * kt: blocks past the capacity are dropped). */
+int tsd_oracle_expand_blocks(int rows, const int32_t *sel, const int32_t *count,
+                             int kb, int Bs, const int32_t *row_lens, int kt,
+                             int32_t *tok, int32_t *tok_count);
+
 /* Exact global top-k from W page-owner shards ("QSA cache sharding",
  * Distributed QSA execution: every rank selects over its own pages, the
  * candidates are exchanged, and one exact top-k with token-id tie-breaking

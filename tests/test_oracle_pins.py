@@ -489,6 +489,110 @@ def test_append_fp8_pages_match_the_page_quantizer(orc):
     np.testing.assert_array_equal(got2["k_pool"][keep], got["k_pool"][keep])
 
 
+# ------------------------------------------------------ block compression
+def _fp8_decode_np(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _compress_case(orc, lens, Bs, seed, from_block=None):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    P = max(1, -(-max(lens) // 64))
+    num_pages = B * P + 2
+    pt = rng.permutation(num_pages)[:B * P].reshape(B, P).astype(np.int32)
+    ik = rng.integers(0, 0x7E, size=(num_pages * 64, 128)).astype(np.uint8)
+    ik |= (rng.random(ik.shape) < 0.5).astype(np.uint8) << 7
+    nblk = [-(-n // Bs) for n in lens]
+    CP = max(1, -(-max(nblk) // 64))
+    num_cpages = B * CP + 1
+    cpt = rng.permutation(num_cpages)[:B * CP].reshape(B, CP).astype(np.int32)
+    ck0 = rng.integers(0, 255, size=(num_cpages * 64, 128)).astype(np.uint8)
+    fb = np.zeros(B, np.int32) if from_block is None else np.asarray(from_block, np.int32)
+    ck = orc.index_k_compress(ik, pt, num_pages, lens, fb, cpt, num_cpages,
+                              ck0, Bs)
+    return pt, ik, cpt, ck0, ck, fb, nblk
+
+
+def test_compress_block_size_one_is_the_token_keys(orc):
+    lens = [200, 64, 1]
+    pt, ik, cpt, _, ck, _, _ = _compress_case(orc, lens, 1, 20)
+    for b, n in enumerate(lens):
+        for t in range(n):
+            slot = pt[b, t // 64] * 64 + t % 64
+            cslot = cpt[b, t // 64] * 64 + t % 64
+            if ik[slot].tolist() != ck[cslot].tolist():
+                # -0 and +0 are one value: the mean of -0 is +0
+                assert (_fp8_decode_np(ik[slot]) == _fp8_decode_np(ck[cslot])).all()
+
+
+def test_compress_means_match_numpy(orc):
+    lens, Bs = [1000, 70, 5], 16
+    pt, ik, cpt, ck0, ck, fb, nblk = _compress_case(orc, lens, Bs, 21,
+                                                    from_block=[3, 0, 0])
+    for b, n in enumerate(lens):
+        for j in range(nblk[b]):
+            cslot = cpt[b, j // 64] * 64 + j % 64
+            if j < fb[b]:
+                np.testing.assert_array_equal(ck[cslot], ck0[cslot])
+                continue
+            ts = np.arange(j * Bs, min((j + 1) * Bs, n))
+            slots = pt[b, ts // 64] * 64 + ts % 64
+            mean = _fp8_decode_np(ik[slots]).mean(axis=0).astype(np.float32)
+            ref = torch.from_numpy(mean).to(torch.float8_e4m3fn).view(
+                torch.uint8).numpy()
+            got_v = _fp8_decode_np(ck[cslot])
+            ref_v = _fp8_decode_np(ref)
+            np.testing.assert_array_equal(got_v, ref_v)
+
+
+def test_compress_hand_worked_ties_and_bad_pages(orc):
+    one, two, three, four = (orc.encode_fp8_e4m3(x) for x in (1, 2, 3, 4))
+    ik = np.zeros((2 * 64, 128), np.uint8)
+    ik[0:4, 0] = [one, two, three, four]      # mean 2.5 (exact)
+    ik[0:4, 1] = [one, one, one, two]         # mean 1.25 (exact)
+    ik[4:8, 2] = [one, one, one, orc.encode_fp8_e4m3(1.25)]  # 1.0625: tie -> 1
+    pt = np.array([[0, 7]], np.int32)         # page 7 is outside the pool
+    cpt = np.array([[1]], np.int32)
+    ck0 = np.full((2 * 64, 128), 0x11, np.uint8)
+    ck = orc.index_k_compress(ik, pt, 2, [70], [0], cpt, 2, ck0, 4)
+    assert ck[64, 0] == orc.encode_fp8_e4m3(2.5)
+    assert ck[64, 1] == orc.encode_fp8_e4m3(1.25)
+    assert ck[65, 2] == one
+    # block 16 (tokens 64..67) sits on page 7: not written
+    assert (ck[64 + 16] == 0x11).all()
+
+
+def test_expand_blocks_hand_worked(orc):
+    sel = np.array([[0, 2, 5, -1], [1, 0, 0, 0]], np.int32)
+    tok, cnt = orc.expand_blocks(sel, [3, 1], 4, [22, 3], 12)
+    assert tok[0].tolist() == [0, 1, 2, 3, 8, 9, 10, 11, 20, 21, -1, -1]
+    assert cnt[0] == 10
+    assert tok[1].tolist() == [-1] * 12 and cnt[1] == 0  # block 1 is past len 3
+    tok, cnt = orc.expand_blocks(sel, [3, 1], 4, [22, 8], 6)
+    assert tok[0].tolist() == [0, 1, 2, 3, 8, 9] and cnt[0] == 6
+    assert tok[1].tolist() == [4, 5, 6, 7, -1, -1] and cnt[1] == 4
+
+
+def test_block_pipeline_with_block_size_one_is_the_token_pipeline(orc):
+    # Bs = 1: compress, score the blocks, select, expand == score, select
+    cfg = _ident_cfg(mode="qsa", B=2, L=300, lens=(300, 130), D_i=128, H_i=4,
+                     top_k=40, seed=30)
+    wl = tsd_synth.to_host(tsd_synth.make(cfg))
+    s_tok = orc.qsa_scores(wl["index_q"], wl["index_w"], wl["index_k"],
+                           wl["page_table"], wl["seq_lens"], wl["num_pages"])
+    i_tok, c_tok = orc.topk(s_tok.astype(np.float32), wl["seq_lens"], 40)
+    ck = orc.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                              wl["seq_lens"], [0, 0], wl["page_table"],
+                              wl["num_pages"], np.zeros_like(wl["index_k"]), 1)
+    s_blk = orc.qsa_scores(wl["index_q"], wl["index_w"], ck, wl["page_table"],
+                           wl["seq_lens"], wl["num_pages"])
+    i_blk, c_blk = orc.topk(s_blk.astype(np.float32), wl["seq_lens"], 40)
+    tok, cnt = orc.expand_blocks(i_blk, c_blk, 1, wl["seq_lens"], 40)
+    np.testing.assert_array_equal(tok, i_tok)
+    np.testing.assert_array_equal(cnt, c_tok)
+
+
 # ---------------------------------------------------------------- attention
 def _decoded_kv(wl, key, scale_key):
     x = wl[key]
