@@ -224,6 +224,94 @@ def sharded_select(dev, passes, warmup, W=4):
             "equals_unsharded": exact}
 
 
+def block_select(dev, passes, warmup, Bs=4, kb=512):
+    """Block-compressed QSA selection on the 262,144-token decode workload
+    (8 requests): blocks of Bs tokens get one compressed FP8 index key each;
+    the step scores and selects kb blocks (kb * Bs tokens) and expands them.
+    Times the full compression of every cached block (once per prompt), the
+    per-step compression of each request's last block, the block score+select
+    and the expansion: n back-to-back calls captured in a HIP graph, one
+    replay timed with HIP events (device time, without the per-call host
+    marshalling of the binding)."""
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config("qsa_decode_b8_l262144_k2048")
+    wl = tsd_synth.make(cfg, dev)
+    B = cfg.B
+    lay = tsd_synth.compressed_layout(wl, Bs)
+    nblk = lay["block_lens"]
+    max_blocks = int(nblk.max())
+    last = (nblk - 1).clamp(min=0)
+    stride = lay["cpage_table"].shape[1] * 64
+    S = torch.empty((B, stride), device=dev)
+    rl = torch.empty(B, dtype=torch.int32, device=dev)
+    bidx = torch.empty((B, kb), dtype=torch.int32, device=dev)
+    bcnt = torch.empty(B, dtype=torch.int32, device=dev)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(B, stride, kb),
+                     dtype=torch.uint8, device=dev)
+    tok = torch.empty((B, kb * Bs), dtype=torch.int32, device=dev)
+    tcnt = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def compress_all():
+        tsd.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                             wl["seq_lens"], lay["ck_pool"], lay["cpage_table"],
+                             lay["num_cpages"], Bs, max_blocks)
+
+    def compress_step():
+        tsd.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                             wl["seq_lens"], lay["ck_pool"], lay["cpage_table"],
+                             lay["num_cpages"], Bs, 1, last)
+
+    def select():
+        tsd.sparse_index_topk("qsa", S, lay["cpage_table"], nblk,
+                              lay["num_cpages"], kb, bidx, bcnt, ws, rl,
+                              index_q=wl["index_q"], index_w=wl["index_w"],
+                              index_k_pool=lay["ck_pool"])
+
+    def expand():
+        tsd.expand_blocks(bidx, bcnt, Bs, wl["seq_lens"], tok, tcnt)
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / n  # us
+
+    us_all = timed(compress_all, max(1, passes // 10))
+    us_step = timed(compress_step, passes)
+    us_sel = timed(select, passes)
+    us_exp = timed(expand, passes)
+    us_chain = timed(lambda: (compress_step(), select(), expand()), passes)
+    tokens = float(wl["seq_lens"].to(torch.int64).sum())
+    blocks = float(nblk.to(torch.int64).sum())
+    comp_bytes = tokens * 128 + blocks * 128   # raw keys read, block keys written
+    scan_bytes = blocks * 128                  # compressed keys read per step
+    del wl, lay, S
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "block_size": Bs, "top_k_blocks": kb,
+            "top_k_tokens": kb * Bs, "blocks_per_request": max_blocks,
+            "compress_all_us": us_all,
+            "compress_all_gbps": comp_bytes / (us_all * 1e-6) / 1e9,
+            "compress_step_us": us_step, "block_select_us": us_sel,
+            "block_scan_model_bytes": scan_bytes, "expand_us": us_exp,
+            "block_selection_step_us": us_chain}
+
+
 def append_bench(dev, passes, warmup):
     """kv_append at decode shapes, one new token per request, timed per call
     (pre-marshalled C calls) over back-to-back launches with HIP events: the
@@ -299,6 +387,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill indexer measurement")
     ap.add_argument("--prefill-passes", type=int, default=5)
+    ap.add_argument("--no-blocks", action="store_true",
+                    help="skip the block-compressed selection measurement")
     ap.add_argument("--no-sharded", action="store_true",
                     help="skip the page-owner sharded top-k emulation")
     ap.add_argument("--no-graph", action="store_true",
@@ -468,6 +558,8 @@ def main():
     if not args.no_sharded:
         line["sharded_topk"] = sharded_select(dev, 200, 20)
     line["kv_append"] = append_bench(dev, 500, 20)
+    if not args.no_blocks:
+        line["block_compressed_select"] = block_select(dev, 200, 20)
     print(json.dumps(line), flush=True)
 
 

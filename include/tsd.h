@@ -375,6 +375,58 @@ typedef struct tsd_append_args {
 
 int kv_append(const tsd_append_args *a, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * index_k_compress / expand_blocks
+ *
+ * Block-compressed QSA selection ("QSA cache sharding": the compressed
+ * cache and the top-k over compressed blocks; "Context parallelism for QSA
+ * attention and the sparse indexer": block compression of the raw index-K
+ * before scoring). Block j of request b holds its tokens
+ * [j*Bs, min((j+1)*Bs, len_b)), Bs = block_size in {1, 2, 4, ..., 64}.
+ *
+ * index_k_compress writes the compressed key of blocks
+ * [from_block[b], from_block[b] + max_blocks) that lie below
+ * ceil(len_b / Bs) (from_block NULL: 0): the mean of the block's decoded
+ * FP8 index keys (exact in f64, rounded to f32, encoded to FP8 by round to
+ * nearest even, saturating at 448), stored at slot
+ * cpage_table[b][j / 64] * 64 + j % 64 of ck_pool [cslots, 128]. A block
+ * with a token on a page outside [0, num_pages), or whose compressed page
+ * is outside [0, num_cpages), is not written. The compressed pool is an
+ * index-K pool of its own: sparse_index_score / sparse_index_topk score and
+ * select blocks through cpage_table with seq_lens = ceil(len / Bs).
+ *
+ * expand_blocks turns each row's selected blocks sel [rows, kb] (ascending,
+ * first count[row] entries, negatives ignored) into their tokens in
+ * ascending order: tok [rows, kt] (-1 padded), tok_count [rows] (NULL ok)
+ * = the number written, at most kt. row_lens [rows] are the token lengths.
+ * 1 <= kb, kt <= 4096; rows <= 65,535. index_k_pool and ck_pool must be
+ * 16-byte aligned (else TSD_E_UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+typedef struct tsd_compress_args {
+  int32_t abi_version;          /* TSD_ABI_VERSION                           */
+  int32_t B;
+  int32_t page_size;            /* must be 64                                */
+  int32_t block_size;           /* Bs                                        */
+  const uint8_t *index_k_pool;  /* [slots, 128] FP8                          */
+  const int32_t *page_table;    /* [B, pt_stride]                            */
+  int64_t pt_stride;
+  int64_t num_pages;
+  const int32_t *seq_lens;      /* [B] token lengths                         */
+  const int32_t *from_block;    /* [B] or NULL                               */
+  int32_t max_blocks;           /* host bound on blocks written per request  */
+  int32_t D_i;                  /* 128                                       */
+  uint8_t *ck_pool;             /* [cslots, 128] FP8                         */
+  const int32_t *cpage_table;   /* [B, cpt_stride]                           */
+  int64_t cpt_stride;
+  int64_t num_cpages;
+} tsd_compress_args;
+
+int index_k_compress(const tsd_compress_args *a, hipStream_t stream);
+
+int expand_blocks(const int32_t *sel, const int32_t *count, int rows, int kb,
+                  int block_size, const int32_t *row_lens, int kt,
+                  int32_t *tok, int32_t *tok_count, hipStream_t stream);
+
 /* Human-readable name of a status code (static string, host only). */
 const char *tsd_strerror(int status);
 
@@ -386,6 +438,7 @@ int tsd_abi_version(void);
 size_t tsd_sizeof_score_args(void);
 size_t tsd_sizeof_attn_args(void);
 size_t tsd_sizeof_append_args(void);
+size_t tsd_sizeof_compress_args(void);
 
 #ifdef __cplusplus
 }

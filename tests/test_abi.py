@@ -215,6 +215,36 @@ def test_append_rejections(kw, code):
     assert _append(**kw) == E[code]
 
 
+def test_compress_and_expand_rejections():
+    assert LIB.tsd_sizeof_compress_args() == ctypes.sizeof(tsd.CompressArgs)
+
+    def comp(**kw):
+        a = tsd.CompressArgs()
+        a.abi_version, a.B, a.page_size, a.block_size = 1, 2, 64, 4
+        a.index_k_pool, a.page_table, a.pt_stride, a.num_pages = FAKE, FAKE, 8, 16
+        a.seq_lens, a.from_block, a.max_blocks, a.D_i = FAKE, None, 128, 128
+        a.ck_pool, a.cpage_table, a.cpt_stride, a.num_cpages = FAKE, FAKE, 2, 4
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return LIB.index_k_compress(ctypes.byref(a), None)
+    assert comp(abi_version=0) == E["ABI"]
+    assert comp(page_size=16) == E["PAGE_SIZE"]
+    assert comp(block_size=3) == E["UNSUPPORTED"]
+    assert comp(block_size=128) == E["UNSUPPORTED"]
+    assert comp(D_i=64) == E["UNSUPPORTED"]
+    assert comp(cpt_stride=0) == E["SHAPE"]
+    assert comp(ck_pool=None) == E["NULL"]
+    assert comp(max_blocks=0, ck_pool=None) == 0
+    assert comp(ck_pool=0x10008) == E["UNSUPPORTED"]
+    assert comp(index_k_pool=0x10004) == E["UNSUPPORTED"]
+    x = LIB.expand_blocks
+    assert x(FAKE, FAKE, 2, 0, 4, FAKE, 16, FAKE, None, None) == E["K"]
+    assert x(FAKE, FAKE, 2, 8, 4, FAKE, 4097, FAKE, None, None) == E["K"]
+    assert x(FAKE, FAKE, 2, 8, 5, FAKE, 16, FAKE, None, None) == E["UNSUPPORTED"]
+    assert x(None, FAKE, 2, 8, 4, FAKE, 16, FAKE, None, None) == E["NULL"]
+    assert x(None, None, 0, 8, 4, None, 16, None, None, None) == 0
+
+
 def test_append_nothing_to_do():
     assert LIB.kv_append(None, None) == E["NULL"]
     assert _append(B=0, page_table=None, positions=None, n_new=None) == 0

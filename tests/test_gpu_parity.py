@@ -287,6 +287,153 @@ def test_sharded_qsa_pipeline_equals_unsharded():
     assert torch.equal(cnt, bufs.count.view(cfg.B))
 
 
+# ------------------------------------------- block-compressed QSA select
+@pytest.mark.parametrize("Bs,lens", [(1, (700, 64)), (2, (130, 1)),
+                                     (4, (9000, 1000, 3)), (8, (3000, 511)),
+                                     (16, (5000, 4097)), (32, (10000, 33)),
+                                     (64, (20000, 65))])
+def test_index_k_compress_matches_oracle(Bs, lens):
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, seed=190 + Bs)
+    wl = tsd_synth.make(cfg, DEV)
+    lay = tsd_synth.compressed_layout(wl, Bs)
+    lay["ck_pool"].fill_(0x11)
+    from_block = torch.tensor([i % 2 for i in range(len(lens))],
+                              dtype=torch.int32, device=DEV)
+    max_blocks = int(lay["block_lens"].max())
+    h = tsd_synth.to_host(wl)
+    ref = oracle.index_k_compress(h["index_k"], h["page_table"], h["num_pages"],
+                                  h["seq_lens"], from_block.cpu().numpy(),
+                                  lay["cpage_table"].cpu().numpy(),
+                                  lay["num_cpages"], lay["ck_pool"].cpu().numpy(),
+                                  Bs)
+    tsd.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                         wl["seq_lens"], lay["ck_pool"], lay["cpage_table"],
+                         lay["num_cpages"], Bs, max_blocks, from_block)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay["ck_pool"].cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("Bs", [1, 4, 64])
+def test_index_k_compress_last_block_per_step(Bs):
+    """The per-step update: one block per request, the one holding the last
+    token (max_blocks = 1), over a pool holding other values."""
+    import top_sparse_decode_amd as tsd
+    lens = (4097, 64, 1, 30001)
+    cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, seed=300 + Bs)
+    wl = tsd_synth.make(cfg, DEV)
+    lay = tsd_synth.compressed_layout(wl, Bs)
+    lay["ck_pool"].fill_(0x5a)
+    last = (lay["block_lens"] - 1).clamp(min=0)
+    h = tsd_synth.to_host(wl)
+    ref = oracle.index_k_compress(h["index_k"], h["page_table"], h["num_pages"],
+                                  h["seq_lens"], last.cpu().numpy(),
+                                  lay["cpage_table"].cpu().numpy(),
+                                  lay["num_cpages"], lay["ck_pool"].cpu().numpy(),
+                                  Bs)
+    tsd.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                         wl["seq_lens"], lay["ck_pool"], lay["cpage_table"],
+                         lay["num_cpages"], Bs, 1, last)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(lay["ck_pool"].cpu().numpy(), ref)
+
+
+def test_expand_blocks_matches_oracle():
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(7)
+    rows, kb = 6, 512
+    for Bs in (1, 4, 64):
+        lens = rng.integers(0, 300000, rows).astype(np.int32)
+        lens[0], lens[1] = 0, 5
+        sel = np.full((rows, kb), -1, np.int32)
+        cnt = np.zeros(rows, np.int32)
+        for r in range(rows):
+            nb = -(-int(lens[r]) // Bs)
+            c = min(kb, nb, int(rng.integers(0, kb + 1)))
+            sel[r, :c] = np.sort(rng.choice(max(nb, 1), size=c, replace=False))
+            cnt[r] = c
+        cnt[2] = kb + 5  # clamped to kb
+        for kt in (2048, 4096, 100):
+            ref, rc = oracle.expand_blocks(sel, np.minimum(cnt, kb), Bs, lens, kt)
+            tok = torch.full((rows, kt), -7, dtype=torch.int32, device=DEV)
+            tc = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+            tsd.expand_blocks(torch.from_numpy(sel).to(DEV),
+                              torch.from_numpy(cnt).to(DEV), Bs,
+                              torch.from_numpy(lens).to(DEV), tok, tc)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(tok.cpu().numpy(), ref)
+            np.testing.assert_array_equal(tc.cpu().numpy(), rc)
+
+
+def _block_select(wl, Bs, kb):
+    """Compress every block, score and select blocks with the fused call,
+    expand to tokens. Returns (layout, block scores, block idx, block count,
+    token idx [B, 1, kb*Bs], token count [B, 1])."""
+    import top_sparse_decode_amd as tsd
+    B = wl["B"]
+    lay = tsd_synth.compressed_layout(wl, Bs)
+    tsd.index_k_compress(wl["index_k"], wl["page_table"], wl["num_pages"],
+                         wl["seq_lens"], lay["ck_pool"], lay["cpage_table"],
+                         lay["num_cpages"], Bs, int(lay["block_lens"].max()))
+    stride = lay["cpage_table"].shape[1] * 64
+    scores = torch.full((B, stride), float("nan"), device=DEV)
+    rl = torch.empty(B, dtype=torch.int32, device=DEV)
+    bidx = torch.empty((B, kb), dtype=torch.int32, device=DEV)
+    bcnt = torch.empty(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(B, stride, kb),
+                     dtype=torch.uint8, device=DEV)
+    tsd.sparse_index_topk("qsa", scores, lay["cpage_table"], lay["block_lens"],
+                          lay["num_cpages"], kb, bidx, bcnt, ws, rl,
+                          index_q=wl["index_q"], index_w=wl["index_w"],
+                          index_k_pool=lay["ck_pool"])
+    tok = torch.empty((B, 1, kb * Bs), dtype=torch.int32, device=DEV)
+    tcnt = torch.empty((B, 1), dtype=torch.int32, device=DEV)
+    tsd.expand_blocks(bidx, bcnt, Bs, wl["seq_lens"], tok.view(B, -1),
+                      tcnt.view(B))
+    return lay, scores, rl, bidx, bcnt, tok, tcnt
+
+
+@pytest.mark.parametrize("Bs,lens,kb", [(4, (30000, 3000, 100), 512),
+                                        (16, (65536, 2000), 128)])
+def test_block_compressed_decode_path(Bs, lens, kb):
+    """Compressed keys, block scores, block top-k, expansion and the sparse
+    attention over the expanded tokens, each against the oracle."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=kb * Bs,
+                           chunks=8, seed=200 + Bs)
+    wl = tsd_synth.make(cfg, DEV)
+    lay, scores, rl, bidx, bcnt, tok, tcnt = _block_select(wl, Bs, kb)
+    B, kt = cfg.B, kb * Bs
+    o = torch.empty((B, cfg.H_q, cfg.chunks, 128), device=DEV)
+    lse = torch.empty((B, cfg.H_q, cfg.chunks), device=DEV)
+    tsd.sparse_gqa_decode(wl["q"], wl["k_pool"], wl["v_pool"], wl["page_table"],
+                          wl["seq_lens"], wl["num_pages"], tok, tcnt, cfg.chunks,
+                          o, lse, k_scale=wl["k_scale"], v_scale=wl["v_scale"])
+    torch.cuda.synchronize()
+    h = tsd_synth.to_host(wl)
+    ck = oracle.index_k_compress(h["index_k"], h["page_table"], h["num_pages"],
+                                 h["seq_lens"], np.zeros(B, np.int32),
+                                 lay["cpage_table"].cpu().numpy(),
+                                 lay["num_cpages"],
+                                 np.zeros_like(lay["ck_pool"].cpu().numpy()), Bs)
+    np.testing.assert_array_equal(lay["ck_pool"].cpu().numpy(), ck)
+    blens = lay["block_lens"].cpu().numpy()
+    np.testing.assert_array_equal(rl.cpu().numpy(), blens)
+    ref_s = oracle.qsa_scores(h["index_q"], h["index_w"], ck,
+                              lay["cpage_table"].cpu().numpy(), blens,
+                              lay["num_cpages"],
+                              score_stride=scores.shape[1])
+    gs = scores.cpu().numpy()
+    check_scores(gs, ref_s, blens, score_tol("qsa"))
+    check_topk_identical(gs, blens, kb, bidx.cpu().numpy(), bcnt.cpu().numpy())
+    rtok, rcnt = oracle.expand_blocks(bidx.cpu().numpy(), bcnt.cpu().numpy(), Bs,
+                                      h["seq_lens"], kt)
+    np.testing.assert_array_equal(tok.view(B, kt).cpu().numpy(), rtok)
+    np.testing.assert_array_equal(tcnt.view(B).cpu().numpy(), rcnt)
+    check_attention_on(h, tok.cpu().numpy(), tcnt.cpu().numpy(), cfg.chunks,
+                       o.cpu().numpy(), lse.cpu().numpy(), out_tol(cfg.kv_enc))
+
+
 # -------------------------------------------------- sparse-decode threshold
 @pytest.mark.parametrize("name,lens,dense_len", [
     ("ds_llama31_8b_b3_l60000", (300, 5000, 1000), 1000),

@@ -71,6 +71,17 @@ class AppendArgs(ctypes.Structure):
     ]
 
 
+class CompressArgs(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", _I32), ("B", _I32), ("page_size", _I32),
+        ("block_size", _I32), ("index_k_pool", _P), ("page_table", _P),
+        ("pt_stride", _I64), ("num_pages", _I64), ("seq_lens", _P),
+        ("from_block", _P), ("max_blocks", _I32), ("D_i", _I32),
+        ("ck_pool", _P), ("cpage_table", _P), ("cpt_stride", _I64),
+        ("num_cpages", _I64),
+    ]
+
+
 class TsdError(RuntimeError):
     def __init__(self, fn, status):
         self.status = status
@@ -99,6 +110,11 @@ def _load():
                                               ctypes.c_int, _P, _P, _P]),
         "sparse_gqa_decode": (ctypes.c_int, [ctypes.POINTER(AttnArgs), _P]),
         "kv_append": (ctypes.c_int, [ctypes.POINTER(AppendArgs), _P]),
+        "index_k_compress": (ctypes.c_int, [ctypes.POINTER(CompressArgs), _P]),
+        "expand_blocks": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, _P, ctypes.c_int, _P,
+                                         _P, _P]),
+        "tsd_sizeof_compress_args": (ctypes.c_size_t, []),
         "tsd_sizeof_append_args": (ctypes.c_size_t, []),
         "lse_merge": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, _P, _P, _P]),
@@ -114,7 +130,8 @@ def _load():
         raise ImportError("libtsd.so ABI version mismatch")
     if (lib.tsd_sizeof_score_args() != ctypes.sizeof(ScoreArgs)
             or lib.tsd_sizeof_attn_args() != ctypes.sizeof(AttnArgs)
-            or lib.tsd_sizeof_append_args() != ctypes.sizeof(AppendArgs)):
+            or lib.tsd_sizeof_append_args() != ctypes.sizeof(AppendArgs)
+            or lib.tsd_sizeof_compress_args() != ctypes.sizeof(CompressArgs)):
         raise ImportError("libtsd.so argument struct layout mismatch")
     return lib
 
@@ -122,9 +139,10 @@ def _load():
 _lib = _load()
 EXPORTS = ("sparse_index_score", "sparse_index_topk",
            "topk_select_workspace_bytes", "topk_select", "topk_merge_sharded",
-           "sparse_gqa_decode", "lse_merge", "kv_append", "tsd_strerror",
-           "tsd_abi_version", "tsd_sizeof_score_args", "tsd_sizeof_attn_args",
-           "tsd_sizeof_append_args")
+           "sparse_gqa_decode", "lse_merge", "kv_append", "index_k_compress",
+           "expand_blocks", "tsd_strerror", "tsd_abi_version",
+           "tsd_sizeof_score_args", "tsd_sizeof_attn_args",
+           "tsd_sizeof_append_args", "tsd_sizeof_compress_args")
 
 
 # ----------------------------------------------------------------- helpers
@@ -383,6 +401,47 @@ def kv_append(page_table, num_pages, positions, n_new, max_new, *,
                 index_k_pool)  # the tensors stay alive with the call
         return lambda keep=keep: fn(ref, st)
     _check("kv_append", _lib.kv_append(ctypes.byref(a), _stream(stream)))
+
+
+def index_k_compress(index_k_pool, page_table, num_pages, seq_lens,
+                     ck_pool, cpage_table, num_cpages, block_size,
+                     max_blocks, from_block=None, stream=None):
+    """Compressed index keys of blocks [from_block[b], from_block[b] +
+    max_blocks) below ceil(seq_lens[b] / block_size) into ``ck_pool``."""
+    _dev("index_k_pool", index_k_pool, dtypes=_FP8)
+    _dev("page_table", page_table, torch.int32)
+    _dev("seq_lens", seq_lens, torch.int32)
+    _dev("from_block", from_block, torch.int32)
+    _dev("ck_pool", ck_pool, dtypes=_FP8)
+    _dev("cpage_table", cpage_table, torch.int32)
+    a = CompressArgs()
+    a.abi_version, a.page_size = ABI_VERSION, PAGE_SIZE
+    a.B, a.block_size = page_table.shape[0], int(block_size)
+    a.index_k_pool = _ptr(index_k_pool)
+    a.page_table, a.pt_stride = _ptr(page_table), page_table.shape[1]
+    a.num_pages, a.seq_lens = int(num_pages), _ptr(seq_lens)
+    a.from_block, a.max_blocks = _ptr(from_block), int(max_blocks)
+    a.D_i = index_k_pool.shape[1]
+    a.ck_pool = _ptr(ck_pool)
+    a.cpage_table, a.cpt_stride = _ptr(cpage_table), cpage_table.shape[1]
+    a.num_cpages = int(num_cpages)
+    _check("index_k_compress", _lib.index_k_compress(ctypes.byref(a),
+                                                     _stream(stream)))
+
+
+def expand_blocks(sel, count, block_size, row_lens, tok, tok_count=None,
+                  stream=None):
+    """Selected blocks ``sel`` [rows, kb] (first ``count`` [rows]) -> their
+    tokens ``tok`` [rows, kt] ascending, -1 padded; ``tok_count`` [rows]."""
+    _dev("sel", sel, torch.int32)
+    _dev("count", count, torch.int32)
+    _dev("row_lens", row_lens, torch.int32)
+    _dev("tok", tok, torch.int32)
+    _dev("tok_count", tok_count, torch.int32)
+    rows, kb = sel.shape
+    _check("expand_blocks", _lib.expand_blocks(
+        _ptr(sel), _ptr(count), rows, kb, int(block_size), _ptr(row_lens),
+        tok.shape[1], _ptr(tok), _ptr(tok_count), _stream(stream)))
 
 
 def lse_merge(o_part, lse_part, out, out_lse=None, stream=None):

@@ -41,6 +41,11 @@ hipError_t launch_topk_merge_sharded(const float* scores, int64_t stride,
                                      int32_t* count, hipStream_t s);
 
 hipError_t launch_kv_append(const tsd_append_args& a, hipStream_t s);
+hipError_t launch_index_k_compress(const tsd_compress_args& a, hipStream_t s);
+hipError_t launch_expand_blocks(const int32_t* sel, const int32_t* count,
+                                int rows, int kb, int Bs,
+                                const int32_t* row_lens, int kt, int32_t* tok,
+                                int32_t* tok_count, hipStream_t s);
 
 hipError_t launch_sparse_gqa(const tsd_attn_args& a, hipStream_t s);
 

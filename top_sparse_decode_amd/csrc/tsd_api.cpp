@@ -249,6 +249,39 @@ int kv_append(const tsd_append_args* a, hipStream_t stream) {
   return launch_status(tsd::launch_kv_append(*a, stream));
 }
 
+static bool block_size_ok(int bs) {
+  return bs >= 1 && bs <= TSD_PAGE_SIZE && (bs & (bs - 1)) == 0;
+}
+
+int index_k_compress(const tsd_compress_args* a, hipStream_t stream) {
+  if (!a) return TSD_E_NULL;
+  if (a->abi_version != TSD_ABI_VERSION) return TSD_E_ABI;
+  if (a->page_size != TSD_PAGE_SIZE) return TSD_E_PAGE_SIZE;
+  if (a->B < 0 || a->max_blocks < 0 || a->pt_stride < 1 ||
+      a->cpt_stride < 1 || a->num_pages < 0 || a->num_cpages < 0)
+    return TSD_E_SHAPE;
+  if (!block_size_ok(a->block_size)) return TSD_E_UNSUPPORTED;
+  if (a->D_i != TSD_HEAD_DIM || a->B > 65535) return TSD_E_UNSUPPORTED;
+  if (a->B == 0 || a->max_blocks == 0) return TSD_OK;
+  if (!a->index_k_pool || !a->page_table || !a->seq_lens || !a->ck_pool ||
+      !a->cpage_table)
+    return TSD_E_NULL;
+  if (!aligned16(a->index_k_pool) || !aligned16(a->ck_pool)) return TSD_E_UNSUPPORTED;
+  return launch_status(tsd::launch_index_k_compress(*a, stream));
+}
+
+int expand_blocks(const int32_t* sel, const int32_t* count, int rows, int kb,
+                  int block_size, const int32_t* row_lens, int kt,
+                  int32_t* tok, int32_t* tok_count, hipStream_t stream) {
+  if (rows < 0) return TSD_E_SHAPE;
+  if (kb < 1 || kb > TSD_MAX_TOPK || kt < 1 || kt > TSD_MAX_TOPK) return TSD_E_K;
+  if (!block_size_ok(block_size) || rows > 65535) return TSD_E_UNSUPPORTED;
+  if (rows == 0) return TSD_OK;
+  if (!sel || !count || !row_lens || !tok) return TSD_E_NULL;
+  return launch_status(tsd::launch_expand_blocks(
+      sel, count, rows, kb, block_size, row_lens, kt, tok, tok_count, stream));
+}
+
 int sparse_gqa_decode(const tsd_attn_args* a, hipStream_t stream) {
   const int rc = validate_attn(a);
   if (rc) return rc;
@@ -289,5 +322,6 @@ int tsd_abi_version(void) { return TSD_ABI_VERSION; }
 size_t tsd_sizeof_score_args(void) { return sizeof(tsd_score_args); }
 size_t tsd_sizeof_attn_args(void) { return sizeof(tsd_attn_args); }
 size_t tsd_sizeof_append_args(void) { return sizeof(tsd_append_args); }
+size_t tsd_sizeof_compress_args(void) { return sizeof(tsd_compress_args); }
 
 }  // extern "C"

@@ -299,6 +299,27 @@ def make(cfg, device="cpu", layer: int = 0) -> dict:
     return wl
 
 
+def compressed_layout(wl: dict, block_size: int, seed: int = 0):
+    """A paged pool for the block-compressed index keys of a QSA workload:
+    ceil(ceil(len / Bs) / 64) compressed pages per request, a seeded
+    permutation of physical pages. Returns cpage_table [B, P_c] int32,
+    block counts [B] int32, num_cpages and a zeroed pool [cslots, 128]."""
+    pt = wl["page_table"]
+    dev = pt.device
+    B = pt.shape[0]
+    nblk = (wl["seq_lens"].to(torch.int64).to(dev) + block_size - 1) // block_size
+    cap_blocks = -(-(pt.shape[1] * PAGE_SIZE) // block_size)
+    Pc = max(1, -(-cap_blocks // PAGE_SIZE))
+    num_cpages = B * Pc
+    g = torch.Generator(device="cpu").manual_seed(wl["cfg"].seed * 7919 + seed)
+    cpt = torch.randperm(num_cpages, generator=g).view(B, Pc).to(torch.int32)
+    pool = torch.zeros((num_cpages * PAGE_SIZE, wl["D_i"]), dtype=torch.uint8,
+                       device=dev)
+    return {"cpage_table": cpt.to(dev), "block_lens": nblk.to(torch.int32),
+            "num_cpages": num_cpages, "ck_pool": pool,
+            "block_size": block_size}
+
+
 def shard_views(wl: dict, W: int):
     """Page-owner shards of a workload's requests (shard w holds the logical
     pages p with p % W == w, in order): per shard, its page table
