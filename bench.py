@@ -168,14 +168,14 @@ def sharded_select(dev, passes, warmup, W=4):
     lens = torch.empty((W, B), dtype=torch.int32, device=dev)
     il = torch.empty((W, B, k), dtype=torch.int32, device=dev)
     cl = torch.empty((W, B), dtype=torch.int32, device=dev)
-    ws = [torch.empty(tsd.topk_select_workspace_bytes(B, stride, k),
+    ws = [torch.zeros(tsd.topk_select_workspace_bytes(B, stride, k),
                       dtype=torch.uint8, device=dev) for _ in range(W)]
     idx = torch.empty((B, k), dtype=torch.int32, device=dev)
     cnt = torch.empty((B,), dtype=torch.int32, device=dev)
     full_stride = wl["page_table"].shape[1] * 64
     Sf = torch.empty((B, full_stride), device=dev)
     lf = torch.empty((B,), dtype=torch.int32, device=dev)
-    wsf = torch.empty(tsd.topk_select_workspace_bytes(B, full_stride, k),
+    wsf = torch.zeros(tsd.topk_select_workspace_bytes(B, full_stride, k),
                       dtype=torch.uint8, device=dev)
     idxf = torch.empty((B, k), dtype=torch.int32, device=dev)
     cntf = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -187,7 +187,8 @@ def sharded_select(dev, passes, warmup, W=4):
                                   wl["num_pages"], k, il[w], cl[w], ws[w],
                                   lens[w], index_q=wl["index_q"],
                                   index_w=wl["index_w"],
-                                  index_k_pool=wl["index_k"])
+                                  index_k_pool=wl["index_k"],
+                                  ws_zeroed=True)
 
     def merge():
         tsd.topk_merge_sharded(S, il, cl, k, idx, cnt)
@@ -196,7 +197,7 @@ def sharded_select(dev, passes, warmup, W=4):
         tsd.sparse_index_topk("qsa", Sf, wl["page_table"], wl["seq_lens"],
                               wl["num_pages"], k, idxf, cntf, wsf, lf,
                               index_q=wl["index_q"], index_w=wl["index_w"],
-                              index_k_pool=wl["index_k"])
+                              index_k_pool=wl["index_k"], ws_zeroed=True)
 
     def timed(fn, n):
         for _ in range(warmup):
@@ -249,7 +250,7 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
     rl = torch.empty(B, dtype=torch.int32, device=dev)
     bidx = torch.empty((B, kb), dtype=torch.int32, device=dev)
     bcnt = torch.empty(B, dtype=torch.int32, device=dev)
-    ws = torch.empty(tsd.topk_select_workspace_bytes(B, stride, kb),
+    ws = torch.zeros(tsd.topk_select_workspace_bytes(B, stride, kb),
                      dtype=torch.uint8, device=dev)
     tok = torch.empty((B, kb * Bs), dtype=torch.int32, device=dev)
     tcnt = torch.empty(B, dtype=torch.int32, device=dev)
@@ -268,7 +269,7 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
         tsd.sparse_index_topk("qsa", S, lay["cpage_table"], nblk,
                               lay["num_cpages"], kb, bidx, bcnt, ws, rl,
                               index_q=wl["index_q"], index_w=wl["index_w"],
-                              index_k_pool=lay["ck_pool"])
+                              index_k_pool=lay["ck_pool"], ws_zeroed=True)
 
     def expand():
         tsd.expand_blocks(bidx, bcnt, Bs, wl["seq_lens"], tok, tcnt)

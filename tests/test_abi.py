@@ -94,7 +94,7 @@ def test_score_null_args_and_empty_batch():
 
 
 def test_fused_score_topk_rejections():
-    def call(k=10, row_lens=True, ws_bytes=None, **kw):
+    def call(k=10, row_lens=True, ws_bytes=None, flags=0, **kw):
         a = ScoreArgs()
         a.abi_version, a.mode, a.B, a.page_size = 1, 2, 2, 64
         a.page_table, a.pt_stride, a.seq_lens, a.num_pages = FAKE, 4, FAKE, 8
@@ -107,21 +107,22 @@ def test_fused_score_topk_rejections():
         need = LIB.topk_select_workspace_bytes(2, 256, max(1, k))
         return LIB.sparse_index_topk(ctypes.byref(a), k, FAKE, None, FAKE,
                                      need if ws_bytes is None else ws_bytes,
-                                     None)
+                                     flags, None)
     assert call(row_lens=False) == E["NULL"]
     assert call(k=0) == E["K"]
     assert call(ws_bytes=8) == E["WORKSPACE"]
     assert call(page_size=16) == E["PAGE_SIZE"]
     assert call(B=0, scores=None, page_table=None, seq_lens=None) == 0
+    assert call(flags=2) == E["UNSUPPORTED"]
 
 
-def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, **kw):
+def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, flags=0, **kw):
     need = LIB.topk_select_workspace_bytes(rows, max_len, k)
     args = dict(scores=FAKE, row_lens=FAKE, idx=FAKE, ws=FAKE)
     args.update(kw)
     return LIB.topk_select(args["scores"], stride, rows, args["row_lens"],
                            max_len, k, args["idx"], None, args["ws"],
-                           need if ws_bytes is None else ws_bytes, None)
+                           need if ws_bytes is None else ws_bytes, flags, None)
 
 
 def test_topk_rejections():
@@ -133,6 +134,8 @@ def test_topk_rejections():
     assert _topk(ws=None) == E["WORKSPACE"]
     assert _topk(ws=ctypes.c_void_p(0x10008)) == E["WORKSPACE"]  # misaligned
     assert _topk(scores=None) == E["NULL"]
+    assert _topk(flags=4) == E["UNSUPPORTED"]
+    assert _topk(rows=0, flags=1) == 0
     assert _topk(rows=70000) == E["UNSUPPORTED"]
     assert _topk(max_len=(1 << 24) + 1, stride=(1 << 24) + 1) == E["UNSUPPORTED"]
     assert _topk(rows=0, scores=None, row_lens=None, idx=None, ws=None) == 0

@@ -160,6 +160,80 @@ def _topk_gpu(scores_np, lens, k, max_len=None):
     return idx.cpu().numpy(), cnt.cpu().numpy()
 
 
+def _hist_words(ws, rows):
+    return ws.view(torch.int32)[:rows * 5120].cpu().numpy()
+
+
+def test_topk_reuses_a_zeroed_workspace():
+    """Every call leaves the histogram words zero (a garbage workspace
+    without the flag, then a chain of flagged calls on the same workspace
+    over inputs that take the blind, staged and raw-reread paths, short and
+    empty rows, and fewer rows), each result equal to the oracle's."""
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(77)
+    rows0, stride, k = 6, 70000, 2048
+    ws = torch.full((tsd.topk_select_workspace_bytes(rows0, stride, k),), 0xAB,
+                    dtype=torch.uint8, device=DEV)
+    cases = []
+    s = rng.normal(size=(rows0, stride)).astype(np.float32)
+    cases.append((s, [stride, 60000, 2048, 2047, 0, 30000], False))
+    t = (rng.integers(0, 40, size=(rows0, stride)) / 40).astype(np.float32)
+    cases.append((t, [stride] * rows0, True))          # heavy ties
+    u = rng.normal(size=(rows0, stride)).astype(np.float32)
+    u[1, 4096:8192] += 20.0                             # one overflowing chunk
+    u[2, ::3] = 5.0                                     # many ties at the top
+    cases.append((u, [stride, stride, 50000, 100, 1, 69999], True))
+    v = rng.normal(size=(3, stride)).astype(np.float32)
+    cases.append((v, [65000, 2049, 40000], True))      # fewer rows
+    for sc, lens, zeroed in cases:
+        r = sc.shape[0]
+        idx = torch.full((r, k), -7, dtype=torch.int32, device=DEV)
+        cnt = torch.full((r,), -7, dtype=torch.int32, device=DEV)
+        tsd.topk_select(torch.from_numpy(sc).to(DEV),
+                        torch.tensor(lens, dtype=torch.int32, device=DEV), k,
+                        stride, idx, cnt, ws, ws_zeroed=zeroed)
+        torch.cuda.synchronize()
+        ridx, rcnt = oracle.topk(sc, lens, k)
+        np.testing.assert_array_equal(cnt.cpu().numpy(), rcnt)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        assert not _hist_words(ws, r).any(), "histograms left nonzero"
+
+
+def test_fused_topk_reuses_a_zeroed_workspace():
+    """sparse_index_topk flagged on a zero-filled workspace, several layers
+    in turn: identical to the unflagged call on a fresh workspace."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(QSA, B=3, lens=(70000, 3000, 33333), top_k=2048,
+                           chunks=4, seed=402)
+    B, k = cfg.B, cfg.top_k
+    ws = None
+    for layer in range(3):
+        wl = tsd_synth.make(cfg, DEV, layer=layer)
+        stride = wl["page_table"].shape[1] * 64
+        outs = []
+        for zeroed in (True, False):
+            S = torch.empty((B, stride), device=DEV)
+            rl = torch.empty(B, dtype=torch.int32, device=DEV)
+            idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+            cnt = torch.empty(B, dtype=torch.int32, device=DEV)
+            nbytes = tsd.topk_select_workspace_bytes(B, stride, k)
+            if zeroed and ws is None:
+                ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+            w = ws if zeroed else torch.full((nbytes,), 0x5C, dtype=torch.uint8,
+                                             device=DEV)
+            tsd.sparse_index_topk("qsa", S, wl["page_table"], wl["seq_lens"],
+                                  wl["num_pages"], k, idx, cnt, w, rl,
+                                  index_q=wl["index_q"], index_w=wl["index_w"],
+                                  index_k_pool=wl["index_k"], ws_zeroed=zeroed)
+            torch.cuda.synchronize()
+            outs.append((S.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()))
+            assert not _hist_words(w, B).any()
+        np.testing.assert_array_equal(outs[0][1], outs[1][1])
+        np.testing.assert_array_equal(outs[0][2], outs[1][2])
+        lens = wl["seq_lens"].cpu().numpy()
+        check_topk_identical(outs[0][0], lens, k, outs[0][1], outs[0][2])
+
+
 def test_topk_special_rows_bit_exact():
     rng = np.random.default_rng(5)
     stride, k = 10000, 300

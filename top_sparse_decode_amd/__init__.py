@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_PKG, "libtsd.so")
 
 TSD_BF16, TSD_FP16, TSD_FP8_E4M3, TSD_F32 = 1, 2, 3, 4
 TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX = 1, 2
+TSD_TOPK_WS_ZEROED = 1
 ABI_VERSION = 1
 PAGE_SIZE = 64
 
@@ -101,10 +102,10 @@ def _load():
                                         [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "topk_select": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, ctypes.c_int,
                                        ctypes.c_int, _P, _P, _P,
-                                       ctypes.c_size_t, _P]),
+                                       ctypes.c_size_t, ctypes.c_int, _P]),
         "sparse_index_topk": (ctypes.c_int, [ctypes.POINTER(ScoreArgs),
                                              ctypes.c_int, _P, _P, _P,
-                                             ctypes.c_size_t, _P]),
+                                             ctypes.c_size_t, ctypes.c_int, _P]),
         "topk_merge_sharded": (ctypes.c_int, [_P, _I64, _P, _P, ctypes.c_int,
                                               ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int, _P, _P, _P]),
@@ -252,10 +253,11 @@ def sparse_index_topk(mode, scores, page_table, seq_lens, num_pages, k, idx,
                       count, workspace, row_lens_out, *, q=None,
                       channel_idx=None, label_pool=None, index_q=None,
                       index_w=None, index_k_pool=None, q_pos=None,
-                      rows_per_req=1, stream=None):
+                      rows_per_req=1, ws_zeroed=False, stream=None):
     """sparse_index_score then topk_select on its scores (same results, fewer
-    passes). ``row_lens_out`` is required; ``workspace`` as for topk_select
-    with max_len = min(scores.shape[-1], page_table.shape[1] * 64)."""
+    passes). ``row_lens_out`` is required; ``workspace`` and ``ws_zeroed`` as
+    for topk_select with max_len = min(scores.shape[-1],
+    page_table.shape[1] * 64)."""
     a = _score_args(mode, scores, page_table, seq_lens, num_pages, q,
                     channel_idx, label_pool, index_q, index_w, index_k_pool,
                     q_pos, rows_per_req, row_lens_out)
@@ -265,7 +267,7 @@ def sparse_index_topk(mode, scores, page_table, seq_lens, num_pages, k, idx,
     ws_bytes = workspace.numel() * workspace.element_size()
     _check("sparse_index_topk", _lib.sparse_index_topk(
         ctypes.byref(a), int(k), _ptr(idx), _ptr(count), _ptr(workspace),
-        ws_bytes, _stream(stream)))
+        ws_bytes, TSD_TOPK_WS_ZEROED if ws_zeroed else 0, _stream(stream)))
 
 
 def topk_select_workspace_bytes(rows, max_len, k):
@@ -273,10 +275,13 @@ def topk_select_workspace_bytes(rows, max_len, k):
 
 
 def topk_select(scores, row_lens, k, max_len, idx, count=None, workspace=None,
-                stream=None):
+                ws_zeroed=False, stream=None):
     """Exact top-k per row of ``scores`` [rows, stride] into ``idx`` [rows, k]
     (ascending, -1 padded) and ``count`` [rows]. ``workspace`` is a uint8
-    CUDA tensor of at least topk_select_workspace_bytes(rows, max_len, k)."""
+    CUDA tensor of at least topk_select_workspace_bytes(rows, max_len, k).
+    ``ws_zeroed``: its histogram words are zero already (zero-filled, or last
+    used by a call with at least as many rows), so the clearing launch is
+    skipped; every call leaves them zero."""
     _dev("scores", scores, torch.float32)
     _dev("row_lens", row_lens, torch.int32)
     _dev("idx", idx, torch.int32)
@@ -287,7 +292,7 @@ def topk_select(scores, row_lens, k, max_len, idx, count=None, workspace=None,
     _check("topk_select", _lib.topk_select(
         _ptr(scores), scores.shape[-1], rows, _ptr(row_lens), int(max_len),
         int(k), _ptr(idx), _ptr(count), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        TSD_TOPK_WS_ZEROED if ws_zeroed else 0, _stream(stream)))
 
 
 def topk_merge_sharded(scores, idx_local, count_local, k, idx, count=None,

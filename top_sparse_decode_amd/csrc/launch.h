@@ -30,7 +30,7 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               hipStream_t s);
 hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        const int32_t* row_lens, int max_len, int k,
-                       int32_t* idx, int32_t* count, void* ws,
+                       int32_t* idx, int32_t* count, void* ws, bool zeroed,
                        hipStream_t s);
 
 int topk_merge_max_candidates();  // W * kl bound of topk_merge_sharded

@@ -251,6 +251,17 @@ TSD_DEVICE void for_survivors(const Ws& ws, const float* s, int row, int nch,
 // output base (kept = key > T, plus the first `need` ties in index order)
 // and ballots place the kept entries. Otherwise the survivors are re-read
 // per pass and ordered through an LDS bitmap over the row's indices.
+// Zeroes a row's digit-1 and digit-2 counts once the row's last reader is
+// done with them (every path of the resolve ends here), so the next call on
+// the workspace may skip the clearing launch.
+TSD_DEVICE void clean_row(const Ws& ws, int row) {
+  uint4* h1 = reinterpret_cast<uint4*>(ws.h1 + static_cast<int64_t>(row) * kBins1);
+  uint4* h2 = reinterpret_cast<uint4*>(ws.h2 + static_cast<int64_t>(row) * kBins2);
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = threadIdx.x; i < kBins1 / 4; i += kRT) h1[i] = z;
+  for (int i = threadIdx.x; i < kBins2 / 4; i += kRT) h2[i] = z;
+}
+
 __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
@@ -301,6 +312,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     for (int64_t j = tid; j < k; j += kRT)
       out[j] = j < n ? static_cast<int32_t>(j) : -1;
     if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
+    clean_row(ws, row);
     return;
   }
   const int nc = static_cast<int>((n + kChunk - 1) / kChunk);
@@ -373,6 +385,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
       eqr += static_cast<uint32_t>(__popcll(me));
     }
     if (tid == 0 && count) count[row] = k;
+    clean_row(ws, row);
     return;
   }
 
@@ -485,6 +498,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
       eqr += static_cast<uint32_t>(__popcll(me[j]));
     }
     if (tid == 0 && count) count[row] = k;
+    clean_row(ws, row);
     return;
   }
 
@@ -593,6 +607,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     __syncthreads();
   }
   if (tid == 0 && count) count[row] = k;
+  clean_row(ws, row);
 }
 
 int nch_for(int max_len) { return max_len > 0 ? (max_len + kChunk - 1) / kChunk : 1; }
@@ -665,9 +680,10 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
 
 hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        const int32_t* row_lens, int max_len, int k,
-                       int32_t* idx, int32_t* count, void* ws, hipStream_t s) {
+                       int32_t* idx, int32_t* count, void* ws, bool zeroed,
+                       hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipError_t e = launch_topk_clear(ws, rows, s);
+  hipError_t e = zeroed ? hipSuccess : launch_topk_clear(ws, rows, s);
   if (e != hipSuccess) return e;
   e = launch_topk_hist1(scores, stride, rows, row_lens, max_len, k, ws, s);
   if (e != hipSuccess) return e;

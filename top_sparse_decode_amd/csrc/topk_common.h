@@ -23,7 +23,9 @@ TSD_DEVICE uint32_t topk_digit1(uint32_t key) { return key >> (32 - kTopkB1); }
 //   sel   [rows]        (digit-1 bin, elements above it) as uint2
 //   counts[rows][nch]   survivors of each chunk
 //   lists [rows][nch][512] (index, key) as uint2, 8-byte aligned
-// The first two are cleared at the start of every call.
+// The first two are zero on entry: a call clears them first unless its
+// caller states they are zero already, and every call's last kernel leaves
+// its rows of them zero again.
 struct TopkWs {
   uint32_t* h1;
   uint32_t* h2;

@@ -130,10 +130,11 @@ int sparse_index_score(const tsd_score_args* a, hipStream_t stream) {
 }
 
 int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
-                      int32_t* count, void* ws, size_t ws_bytes,
+                      int32_t* count, void* ws, size_t ws_bytes, int flags,
                       hipStream_t stream) {
   int rc = validate_score(a);
   if (rc) return rc;
+  if (flags & ~TSD_TOPK_WS_ZEROED) return TSD_E_UNSUPPORTED;
   const int64_t rows64 = a->mode == TSD_SCORE_DS_LABEL
                              ? static_cast<int64_t>(a->B) * a->H_kv
                              : static_cast<int64_t>(a->B) * a->rows_per_req;
@@ -145,7 +146,8 @@ int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
                      static_cast<int>(max_len), k, idx, ws, ws_bytes);
   if (rc) return rc;
   if (a->B == 0) return TSD_OK;
-  hipError_t e = tsd::launch_topk_clear(ws, rows, stream);
+  hipError_t e = hipSuccess;
+  if (!(flags & TSD_TOPK_WS_ZEROED)) e = tsd::launch_topk_clear(ws, rows, stream);
   if (e != hipSuccess) return launch_status(e);
   if (a->mode == TSD_SCORE_QSA_INDEX && a->rows_per_req < 64) {
     e = tsd::launch_qsa_scan(*a, stream, ws, k);
@@ -175,14 +177,17 @@ size_t topk_select_workspace_bytes(int rows, int max_len, int k) {
 
 int topk_select(const float* scores, int64_t stride, int rows,
                 const int32_t* row_lens, int max_len, int k, int32_t* idx,
-                int32_t* count, void* ws, size_t ws_bytes,
+                int32_t* count, void* ws, size_t ws_bytes, int flags,
                 hipStream_t stream) {
   const int rc = validate_topk(scores, stride, rows, row_lens, max_len, k,
                                idx, ws, ws_bytes);
   if (rc) return rc;
+  if (flags & ~TSD_TOPK_WS_ZEROED) return TSD_E_UNSUPPORTED;
   if (rows == 0) return TSD_OK;
   return launch_status(tsd::launch_topk(scores, stride, rows, row_lens,
-                                        max_len, k, idx, count, ws, stream));
+                                        max_len, k, idx, count, ws,
+                                        (flags & TSD_TOPK_WS_ZEROED) != 0,
+                                        stream));
 }
 
 int topk_merge_sharded(const float* scores, int64_t stride,

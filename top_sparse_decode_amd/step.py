@@ -36,7 +36,9 @@ class StepBuffers:
         self.row_lens = torch.empty(self.rows, dtype=torch.int32, device=dev)
         self.idx = torch.empty((self.rows, k), dtype=torch.int32, device=dev)
         self.count = torch.empty(self.rows, dtype=torch.int32, device=dev)
-        self.ws = torch.empty(
+        # zero-filled once: every selection leaves its histograms zero, so
+        # the calls below skip the clearing launch
+        self.ws = torch.zeros(
             max(1, topk_select_workspace_bytes(self.rows, self.max_len, k)),
             dtype=torch.uint8, device=dev)
         self.o_part = torch.empty((B, H_q, C, D), dtype=torch.float32, device=dev)
@@ -75,12 +77,13 @@ def score_select(layer, bufs, stream=None):
                   index_k_pool=layer.get("index_k_pool", layer.get("index_k")))
     sparse_index_topk(layer["mode"], bufs.scores, layer["page_table"],
                       layer["seq_lens"], layer["num_pages"], layer["top_k"],
-                      bufs.idx, bufs.count, bufs.ws, bufs.row_lens, **kw)
+                      bufs.idx, bufs.count, bufs.ws, bufs.row_lens,
+                      ws_zeroed=True, **kw)
 
 
 def select(layer, bufs, stream=None):
     topk_select(bufs.scores, bufs.row_lens, layer["top_k"], bufs.max_len,
-                bufs.idx, bufs.count, bufs.ws, stream=stream)
+                bufs.idx, bufs.count, bufs.ws, ws_zeroed=True, stream=stream)
 
 
 def attend(layer, bufs, stream=None):
@@ -125,7 +128,8 @@ class Plan:
         import ctypes
 
         from . import (ABI_VERSION, PAGE_SIZE, AttnArgs, ScoreArgs,
-                       TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX, _half_code,
+                       TSD_SCORE_DS_LABEL, TSD_SCORE_QSA_INDEX,
+                       TSD_TOPK_WS_ZEROED, _half_code,
                        _kv_code, _lib)
         P = ctypes.c_void_p
         p = lambda t: None if t is None else P(t.data_ptr())  # noqa: E731
@@ -157,7 +161,8 @@ class Plan:
         k = layer["top_k"]
         self.topk_args = (p(bufs.scores), bufs.scores.shape[-1], bufs.rows,
                           p(bufs.row_lens), bufs.max_len, k, p(bufs.idx),
-                          p(bufs.count), p(bufs.ws), bufs.ws.numel())
+                          p(bufs.count), p(bufs.ws), bufs.ws.numel(),
+                          TSD_TOPK_WS_ZEROED)
         t = AttnArgs()
         q = layer["q"]
         t.abi_version, t.page_size = ABI_VERSION, PAGE_SIZE
@@ -192,7 +197,7 @@ class Plan:
                       lambda: lib.sparse_index_topk(
                           self._score_ref, self.topk_args[5], self.topk_args[6],
                           self.topk_args[7], self.topk_args[8],
-                          self.topk_args[9], h)),)
+                          self.topk_args[9], self.topk_args[10], h)),)
         else:
             first = (("sparse_index_score",
                       lambda: lib.sparse_index_score(self._score_ref, h)),
