@@ -17,6 +17,8 @@
 // ReLU is applied per lane and a 3-shuffle reduce-scatter over the 4 lane
 // groups leaves lane l with the full score of key l of the page, so a page
 // stores 256 contiguous bytes of scores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -40,6 +42,15 @@ TSD_DEVICE v8i load_row_slice(const uint8_t* row, int kb) {
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
+}
+
+// Weighted ReLU of one lane's 4 heads of an MFMA tile, in a fixed order of
+// rounding (written out with fmaf so that no contraction choice of the
+// compiler changes it): both index kernels call it, so they agree bitwise.
+TSD_DEVICE float weighted_relu4(v4f d, float w0, float w1, float w2, float w3) {
+  const float m0 = fmaxf(d[0], 0.f), m1 = fmaxf(d[1], 0.f);
+  const float m2 = fmaxf(d[2], 0.f), m3 = fmaxf(d[3], 0.f);
+  return fmaf(w3, m3, fmaf(w2, m2, fmaf(w0, m0, w1 * m1)));
 }
 
 TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
@@ -155,8 +166,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const v4f dd = mfma_fp8(qa, kt[d][i]);
-          part[i] = w[0] * fmaxf(dd[0], 0.f) + w[1] * fmaxf(dd[1], 0.f) +
-                    w[2] * fmaxf(dd[2], 0.f) + w[3] * fmaxf(dd[3], 0.f);
+          part[i] = weighted_relu4(dd, w[0], w[1], w[2], w[3]);
         }
         // reduce-scatter over the 4 lane groups: lane l gets key l
         const float red = reduce_scatter4(part);
@@ -202,17 +212,18 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
 // request's index keys -- a dense FP8 contraction (rows x 16 heads) x keys x
 // 128 dims with the weighted-ReLU head reduction as epilogue.
 //
-// A workgroup of 8 waves owns 64 consecutive query rows of one request (8 per
-// wave, their index heads held as MFMA A operands in registers) and a span of
-// 16,384 keys. The span is walked in blocks of 256 keys (4 pages) that the
-// workgroup gathers once into LDS; every wave then takes each 16-key tile of
-// the block as a B operand and issues one MFMA per row, so each key byte read
-// from memory feeds 64 rows. The per-row epilogue and the cross-lane
-// reduce-scatter are the decode scan's, in the same order, so both kernels
-// produce bit-identical scores. Keys past a row's causal limit are computed
-// but never stored.
-constexpr int kPfWaves = 16;
-constexpr int kPfRowsPerWave = 4;
+// A workgroup of 8 waves owns 64 consecutive query rows of one request (8
+// per wave, their index heads held as MFMA A operands and their head weights
+// in registers, 2 waves per SIMD) and a span of 16,384 keys whose page ids it
+// keeps in LDS. The span is walked in blocks of 256 keys (4 pages) that the
+// workgroup gathers once into LDS, the next block's loads in flight during
+// the current one; every wave then takes each 16-key tile of the block as a
+// B operand and issues one MFMA per row, so each key byte read from memory
+// feeds 64 rows. The per-row epilogue (weighted_relu4) and the cross-lane
+// reduce-scatter are the decode scan's, so both kernels produce bit-identical
+// scores. Keys past a row's causal limit are computed but never stored.
+constexpr int kPfWaves = 8;
+constexpr int kPfRowsPerWave = 8;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // rows per workgroup
 constexpr int kPfBlockKeys = 256;                   // keys per LDS block
 constexpr int kPfSpanBlocks = 64;                   // blocks per workgroup
@@ -238,17 +249,21 @@ struct PfStage {
   uint4 x[kPfVecsPerThread];
 };
 
+// Page ids come from the workgroup's LDS copy of its span's page-table
+// entries, so the key loads issue without waiting on earlier memory
+// operations (a page-id load from memory would wait on the vector-memory
+// counter, which also counts every score store still in flight).
 TSD_DEVICE void pf_load(PfStage& st, const uint8_t* __restrict__ index_k,
-                        const int32_t* __restrict__ pt, int64_t num_pages,
-                        int64_t key0, int64_t n_wg, int tid) {
+                        const int32_t* pages_s, int64_t span0, int64_t key0,
+                        int64_t n_wg, int tid) {
 #pragma unroll
   for (int it = 0; it < kPfVecsPerThread; ++it) {
     const int v = tid + it * kPfThreads;
     const int64_t t = key0 + (v >> 3);
     uint4 x = make_uint4(0, 0, 0, 0);
     if (v < kPfVecs && t < n_wg) {
-      const int32_t page = pt[t / kPage];
-      if (page >= 0 && page < num_pages)
+      const int32_t page = pages_s[(t - span0) / kPage];
+      if (page >= 0)
         x = *reinterpret_cast<const uint4*>(
             index_k + (static_cast<int64_t>(page) * kPage + t % kPage) * kDi +
             16 * (v & 7));
@@ -276,10 +291,9 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
     int64_t score_stride, int32_t* __restrict__ row_lens_out) {
   // two key blocks: the next one is gathered while the current one is used
   __shared__ __align__(16) uint8_t keys_s[2][kPfBlockKeys * kPfPitch];
-  __shared__ int page_ok_s[2][kPfBlockKeys / kPage];
-  __shared__ int64_t nmax_s[kPfWaves];
-  // head weights of the workgroup's rows, 4 consecutive heads per 16 bytes
-  __shared__ __align__(16) float w_s[kPfRows][16];
+  // physical page of each page of the span, -1 past the length or invalid
+  __shared__ int32_t pages_s[kPfSpan / kPage];
+  __shared__ int64_t nmax_s[kPfWaves], nmin_s[kPfWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.y / groups_per_req;
   const int grp_in_req = blockIdx.y - b * groups_per_req;
@@ -290,10 +304,12 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
   const int col = lane & 15, kb = lane >> 4;
 
-  // this wave's rows: A operands and key counts; weights go to LDS
+  // this wave's rows: A operands, key counts and, per lane, the weights of
+  // the 4 heads its MFMA output rows hold (4*kb .. 4*kb+3)
   v8i qa[kPfRowsPerWave];
+  float4 wq[kPfRowsPerWave];
   int32_t nr[kPfRowsPerWave];  // key count of each row (n <= 2^31 - 1)
-  int64_t nmax = 0;
+  int64_t nmax = 0, nmin = INT64_MAX;
 #pragma unroll
   for (int i = 0; i < kPfRowsPerWave; ++i) {
     const int rr = row0 + wave * kPfRowsPerWave + i;  // row within request
@@ -312,14 +328,25 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
     // n is the same in every lane; keep it scalar so row tests are uniform
     nr[i] = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(n));
     nmax = n > nmax ? n : nmax;
+    nmin = n < nmin ? n : nmin;
     qa[i] = (ok && col < H_i)
                 ? load_row_slice(index_q + (row * H_i + col) * kDi, kb)
                 : v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    if (lane < 16)
-      w_s[wave * kPfRowsPerWave + i][lane] =
-          (ok && lane < H_i) ? index_w[row * H_i + lane] : 0.f;
+    float w4[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      w4[c] = (ok && 4 * kb + c < H_i) ? index_w[row * H_i + 4 * kb + c] : 0.f;
+    wq[i] = make_float4(w4[0], w4[1], w4[2], w4[3]);
   }
-  if (lane == 0) nmax_s[wave] = nmax;
+  if (lane == 0) {
+    nmax_s[wave] = nmax;
+    nmin_s[wave] = nmin;
+  }
+  for (int i = tid; i < kPfSpan / kPage; i += kPfThreads) {
+    const int64_t t = span0 + static_cast<int64_t>(i) * kPage;
+    int32_t page = t < len ? pt[t / kPage] : -1;
+    pages_s[i] = page >= 0 && page < num_pages ? page : -1;
+  }
   __syncthreads();
   int64_t n_wg = 0;
 #pragma unroll
@@ -329,23 +356,31 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
          span0 + static_cast<int64_t>(nblk) * kPfBlockKeys < n_wg)
     ++nblk;
   if (nblk == 0) return;  // uniform over the workgroup
+  int64_t n_min = nmin_s[0];  // shortest row of the workgroup
+#pragma unroll
+  for (int i = 1; i < kPfWaves; ++i) n_min = nmin_s[i] < n_min ? nmin_s[i] : n_min;
+  int nfull = 0;  // leading blocks below every row's key count
+  while (nfull < nblk &&
+         span0 + static_cast<int64_t>(nfull + 1) * kPfBlockKeys <= n_min)
+    ++nfull;
 
   PfStage st;
-  pf_load(st, index_k, pt, num_pages, span0, n_wg, tid);
+  pf_load(st, index_k, pages_s, span0, span0, n_wg, tid);
   pf_store(st, keys_s[0], tid);
-  if (tid < kPfBlockKeys / kPage) {
-    const int64_t t = span0 + tid * kPage;
-    const int32_t page = t < len ? pt[t / kPage] : 0;
-    page_ok_s[0][tid] = page >= 0 && page < num_pages;
-  }
   __syncthreads();
 
-  for (int blk = 0; blk < nblk; ++blk) {
+  // One block: the next block's loads stay in flight during this block's
+  // math. MASKED adds the causal store guard; blocks whose keys all lie
+  // below every row's limit store unconditionally, so the number of stores
+  // issued after the loads is fixed and waiting for the loads does not wait
+  // for the stores as well (loads and stores share one completion counter).
+  auto block = [&](int blk, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int cur = blk & 1;
     const int64_t key0 = span0 + static_cast<int64_t>(blk) * kPfBlockKeys;
     const bool more = blk + 1 < nblk;
-    if (more)  // next block's loads stay in flight during this block's math
-      pf_load(st, index_k, pt, num_pages, key0 + kPfBlockKeys, n_wg, tid);
+    if (more)
+      pf_load(st, index_k, pages_s, span0, key0 + kPfBlockKeys, n_wg, tid);
     const uint8_t* ks = keys_s[cur];
 #pragma unroll 1
     for (int g4 = 0; g4 < kPfBlockKeys / 64; ++g4) {
@@ -356,15 +391,17 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
         kt[i] = lds_row_slice(ks + (64 * g4 + 16 * i + col) * kPfPitch, kb);
       // as in the decode scan, a key on a page outside [0, num_pages)
       // scores -inf (the 64-key group is exactly one page)
-      const bool page_ok = page_ok_s[cur][g4] != 0;
+      const bool page_ok = pages_s[blk * (kPfBlockKeys / kPage) + g4] >= 0 ||
+                           key0 + 64 * g4 >= len;
       // Per row: the four tiles' MFMAs go out back to back into separate
-      // accumulators (a scheduling barrier keeps the reduction behind them),
-      // so one MFMA latency is exposed per row instead of one per tile. Every
-      // row computes every tile; causality is enforced by the store guard.
+      // accumulators (a scheduling barrier keeps the epilogue behind them),
+      // so one MFMA latency is exposed per row instead of one per tile. On
+      // this part MFMA and VALU work of one SIMD do not overlap, so issuing
+      // the next row's MFMAs ahead of the epilogue gains nothing. Every row
+      // computes every tile; causality is enforced by the store guard.
 #pragma unroll
       for (int i = 0; i < kPfRowsPerWave; ++i) {
-        const float4 wv = *reinterpret_cast<const float4*>(
-            &w_s[wave * kPfRowsPerWave + i][4 * kb]);
+        const float4 wv = wq[i];
         v4f d[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) d[j] = mfma_fp8(qa[i], kt[j]);
@@ -372,27 +409,20 @@ __global__ __launch_bounds__(kPfWaves * kWave) void qsa_prefill_kernel(
         float part[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          part[j] = wv.x * fmaxf(d[j][0], 0.f) + wv.y * fmaxf(d[j][1], 0.f) +
-                    wv.z * fmaxf(d[j][2], 0.f) + wv.w * fmaxf(d[j][3], 0.f);
+          part[j] = weighted_relu4(d[j], wv.x, wv.y, wv.z, wv.w);
         const float red = reduce_scatter4(part);
         const float sc = page_ok ? red : -__builtin_inff();
-        if (t < nr[i]) {
-          const int64_t row = static_cast<int64_t>(b) * rows_per_req + row0 +
-                              wave * kPfRowsPerWave + i;
-          scores[row * score_stride + t] = sc;
-        }
+        const int64_t row = static_cast<int64_t>(b) * rows_per_req + row0 +
+                            wave * kPfRowsPerWave + i;
+        if (!MASKED || t < nr[i]) scores[row * score_stride + t] = sc;
       }
     }
-    if (more) {
-      pf_store(st, keys_s[cur ^ 1], tid);
-      if (tid < kPfBlockKeys / kPage) {
-        const int64_t t = key0 + kPfBlockKeys + tid * kPage;
-        const int32_t page = t < len ? pt[t / kPage] : 0;
-        page_ok_s[cur ^ 1][tid] = page >= 0 && page < num_pages;
-      }
-    }
+    if (more) pf_store(st, keys_s[cur ^ 1], tid);
     __syncthreads();  // next block landed; this one is no longer read
-  }
+  };
+  int blk = 0;
+  for (; blk < nfull; ++blk) block(blk, std::false_type{});
+  for (; blk < nblk; ++blk) block(blk, std::true_type{});
 }
 
 }  // namespace
