@@ -53,6 +53,17 @@ TSD_DEVICE float weighted_relu4(v4f d, float w0, float w1, float w2, float w3) {
   return fmaf(w3, m3, fmaf(w2, m2, fmaf(w0, m0, w1 * m1)));
 }
 
+// load_row_slice with non-temporal loads (data read once).
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+TSD_DEVICE v8i load_row_slice_nt(const uint8_t* row, int kb) {
+  const v4u lo = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + 16 * kb));
+  const v4u hi = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + 64 + 16 * kb));
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
 TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
   v4f c = {0.f, 0.f, 0.f, 0.f};
   // format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0
@@ -141,8 +152,12 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     // register set's key loads (loads complete in order)
     const int32_t my_page = lane < npg ? pt[page0 + lane] : -1;
 
-    // loads of wave pages j, j+1 (pages past npg or outside the pool load
-    // nothing; a page outside [0, num_pages) scores -inf)
+    // loads of wave pages j, j+1. They are unconditional, so the compiler
+    // knows how many loads follow the ones it waits for (loads complete in
+    // order) and the other register set's loads stay in flight: a page past
+    // npg or outside [0, num_pages) reads page 0 (which exists, num_pages >=
+    // 1 here) and scores -inf. The index keys are read once per step, so
+    // the loads are non-temporal.
     auto load2 = [&](int j, v8i (&kt)[2][4], bool (&valid)[2]) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -154,8 +169,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
             index_k + static_cast<int64_t>(valid[d] ? page : 0) * kPage * kDi;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          kt[d][i] = valid[d] ? load_row_slice(base + (16 * i + col) * kDi, kb)
-                              : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+          kt[d][i] = load_row_slice_nt(base + (16 * i + col) * kDi, kb);
       }
     };
     auto score2 = [&](int j, const v8i (&kt)[2][4], const bool (&valid)[2]) {
@@ -179,13 +193,26 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     };
     v8i ka[2][4], kc[2][4];
     bool va[2], vc[2];
-    load2(0, ka, va);
+    if (num_pages > 0) {
+      load2(0, ka, va);
+      int j = 0;
 #pragma unroll 1
-    for (int j = 0; j < npg; j += 4) {
-      load2(j + 2, kc, vc);
+      for (; j + 4 < npg; j += 4) {  // the next 4 pages' loads always in flight
+        load2(j + 2, kc, vc);
+        score2(j, ka, va);
+        load2(j + 4, ka, va);
+        score2(j + 2, kc, vc);
+      }
+      if (j + 2 < npg) load2(j + 2, kc, vc);  // the last 1 to 4 pages
       score2(j, ka, va);
-      if (j + 4 < npg) load2(j + 4, ka, va);
       score2(j + 2, kc, vc);
+    } else {  // an empty pool: every page is outside it
+#pragma unroll 1
+      for (int e = lane; e < npg * kPage; e += kWave) res[e] = -__builtin_inff();
+      if (do_hist)
+        for (int e = lane; e < npg * kPage; e += kWave)
+          if ((page0 * kPage + e) < n)
+            atomicAdd(&hist_s[topk_digit1(order_key(-__builtin_inff()))], 1u);
     }
     // the wave's scores are contiguous in the row: one burst of stores
     // (LDS order within the wave makes every lane's staged score visible)

@@ -159,10 +159,12 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
 
   for (int64_t base = lo; base < hi; base += NT) {
     const int tn = static_cast<int>(hi - base < NT ? hi - base : NT);
-    // 1. resolve slots and page scales
+    // 1. resolve slots; the page-scale loads stay in flight and are stored
+    // to LDS after the K/V gather has been issued (the barrier waits for LDS
+    // operations only)
+    float ksc = 0.f, vsc = 0.f;
     if (tid < NT) {
       int64_t slot = -1;
-      float ksc = 0.f, vsc = 0.f;
       if (tid < tn) {
         const bool spec = !dense && base == lo_s && lo_s + tid < hi_s;
         const int64_t t = dense ? base + tid : (spec ? t_spec : sel[base + tid]);
@@ -176,8 +178,6 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         }
       }
       slot_s[tid] = slot;
-      ks_s[tid] = ksc;
-      vs_s[tid] = vsc;
     }
     __syncthreads();
     // 2. gather K and V rows (16-byte vectors; masked rows become zeros):
@@ -186,11 +186,14 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     constexpr int kIt = NT * vpr / kThreads;
     static_assert(NT * vpr % kThreads == 0, "gather split");
     uint4 kx[kIt], vx[kIt];
+    int64_t slots[kIt];  // all LDS reads first: one wait covers them
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) slots[it] = slot_s[(tid + it * kThreads) / vpr];
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int i = tid + it * kThreads;
-      const int j = i / vpr, v = i % vpr;
-      const int64_t slot = slot_s[j];
+      const int v = i % vpr;
+      const int64_t slot = slots[it];
       kx[it] = make_uint4(0, 0, 0, 0);
       vx[it] = make_uint4(0, 0, 0, 0);
       if (slot >= 0) {
@@ -198,6 +201,10 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         kx[it] = *reinterpret_cast<const uint4*>(k_pool + off);
         vx[it] = *reinterpret_cast<const uint4*>(v_pool + off);
       }
+    }
+    if (tid < NT) {
+      ks_s[tid] = ksc;
+      vs_s[tid] = vsc;
     }
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
