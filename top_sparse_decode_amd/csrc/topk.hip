@@ -142,6 +142,15 @@ __global__ __launch_bounds__(kFT) void topk_filter_kernel(
   const int q = w / kFWavesPerChunk, wq = w % kFWavesPerChunk;
   const float* s = scores + row * stride;
   const Ws ws = topk_ws(ws_base, gridDim.y, nch);
+  // b1 from the row's H1: thread t holds bins [4096 - 4(t+1), 4096 - 4t).
+  // H1 is loaded before the scores and the score loads are unconditional
+  // (an index past the row reads its last score and is masked at use), so
+  // the wait for H1 leaves the scores in flight during the pick (loads
+  // complete in order).
+  constexpr int per1 = kBins1 / kFT;
+  static_assert(per1 == 4, "one uint4 run per thread");
+  const uint4 x = *reinterpret_cast<const uint4*>(
+      ws.h1 + static_cast<int64_t>(row) * kBins1 + (kBins1 - (tid + 1) * per1));
   float v[kFPer];
   auto load_pass = [&](int64_t p0) {
     const int64_t sub = p0 + static_cast<int64_t>(q) * kChunk +
@@ -149,15 +158,10 @@ __global__ __launch_bounds__(kFT) void topk_filter_kernel(
 #pragma unroll
     for (int r = 0; r < kFPer; ++r) {
       const int64_t i = sub + r * kWave + lane;
-      v[r] = i < n ? s[i] : 0.f;
+      v[r] = s[i < n ? i : n - 1];
     }
   };
   load_pass(start);
-  // b1 from the row's H1: thread t holds bins [4096 - 4(t+1), 4096 - 4t)
-  constexpr int per1 = kBins1 / kFT;
-  static_assert(per1 == 4, "one uint4 run per thread");
-  const uint4 x = *reinterpret_cast<const uint4*>(
-      ws.h1 + static_cast<int64_t>(row) * kBins1 + (kBins1 - (tid + 1) * per1));
   const uint32_t h[per1] = {x.w, x.z, x.y, x.x};  // from the top down
   for (int i = tid; i < kBins2; i += kFT) hist[i] = 0u;  // ordered by the pick
   const BinPick p1 =
@@ -262,6 +266,18 @@ TSD_DEVICE void clean_row(const Ws& ws, int row) {
   for (int i = threadIdx.x; i < kBins2 / 4; i += kRT) h2[i] = z;
 }
 
+// Blind rounds of the resolve for nch chunks per row: wave w takes chunks
+// [w*R, w*R + R), reading 64*H list entries of each (H = 2 when a wave has at
+// most 8 chunks, else 1); 0 when R*H exceeds kBlindRounds (no blind path).
+int blind_rounds(int nch) {
+  const int R = (nch + kRT / kWave - 1) / (kRT / kWave);
+  const int H = R * 2 <= kBlindRounds ? 2 : 1;
+  return R * H <= kBlindRounds ? R * H : 0;
+}
+
+// RB: blind rounds compiled in (2, 4, 8 or 16, at least blind_rounds(nch)),
+// or 0 for rows with no blind path.
+template <int RB>
 __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
@@ -287,26 +303,32 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   // round trip.
   // Round q of a lane covers chunk wave*R + q/H, entry 64*(q%H) + lane: H = 2
   // (128 entries per chunk) when a wave has at most 8 chunks, else 1.
+  // The row's records are loaded first and every blind read is
+  // unconditional (a chunk index past nch reads the last chunk and is
+  // masked at use), so the compiler can count the loads in flight and the
+  // digit-2 pick below runs while the lists arrive (loads complete in order).
+  constexpr bool kBlind = RB > 0;
+  constexpr int kRounds = kBlind ? RB : 1;
   const int R = (nch + kWavesR - 1) / kWavesR;
   const int H = R * 2 <= kBlindRounds ? 2 : 1;
-  const bool blind = R * H <= kBlindRounds;
-  uint2 bl[kBlindRounds];
-  uint32_t cntw = 0;
-  if (blind) {
-#pragma unroll
-    for (int q = 0; q < kBlindRounds; ++q) {
-      const int c = wave * R + q / H;
-      bl[q] = make_uint2(0u, 0u);
-      if (q < R * H && c < nch)
-        bl[q] = ws.lists[(static_cast<int64_t>(row) * nch + c) * kListCap +
-                         kWave * (q % H) + lane];
-    }
-    const int c = wave * R + lane;
-    if (lane < R && c < nch) cntw = ws.counts[static_cast<int64_t>(row) * nch + c];
-  }
   const uint32_t h2v = ws.h2[static_cast<int64_t>(row) * kBins2 + (kBins2 - 1 - tid)];
   const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 2
   const int64_t n = clamp_len(row_lens[row], cap);
+  uint2 bl[kRounds];
+  uint32_t cntw = 0;
+  if constexpr (kBlind) {
+    __builtin_amdgcn_sched_barrier(0);  // keep the records' loads first
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      int c = wave * R + q / H;
+      c = c < nch ? c : nch - 1;
+      bl[q] = ws.lists[(static_cast<int64_t>(row) * nch + c) * kListCap +
+                       kWave * (q % H) + lane];
+    }
+    int c = wave * R + lane;
+    c = c < nch ? c : nch - 1;
+    cntw = ws.counts[static_cast<int64_t>(row) * nch + c];
+  }
   int32_t* out = idx + static_cast<int64_t>(row) * k;
   if (n <= k) {
     for (int64_t j = tid; j < k; j += kRT)
@@ -320,24 +342,26 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   const BinPick p1{sel.x, sel.y};
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
 
-  bool blind_ok = blind;
-  if (blind) {
+  bool blind_ok = false;
+  BinPick p2b{0u, 0u};
+  if constexpr (kBlind) {
+    hist[tid] = 0u;  // digit-3 counts; ordered before use by p2's barriers
+    const uint32_t h2r[1] = {h2v};
+    p2b = pick_bin_runs<kBins2, kRT>(h2r, k - p1.above, lds, &pick);
     const int c = wave * R + lane;
     blind_ok = __ballot(lane < R && c < nc &&
                         cntw > static_cast<uint32_t>(kWave * H)) == 0;
   }
-  if (__syncthreads_and(blind_ok)) {
+  if (kBlind && __syncthreads_and(blind_ok)) {
     // ---- blind fast path ----
-    hist[tid] = 0u;  // digit-3 counts; ordered before use by p2's barriers
-    const uint32_t h2r[1] = {h2v};
-    const BinPick p2 = pick_bin_runs<kBins2, kRT>(h2r, k - p1.above, lds, &pick);
+    const BinPick p2 = p2b;
     const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
     const uint32_t need2 = k - p1.above - p2.above;
     // per-lane flags of the rounds, one bit per round (ok, above T, at T),
     // balloted again where a wave-wide view is needed
     uint32_t okb = 0;
 #pragma unroll
-    for (int q = 0; q < kBlindRounds; ++q) {
+    for (int q = 0; q < kRounds; ++q) {
       const int j = q / H;  // the wave's chunk of this round
       const int c = wave * R + j;
       const uint32_t cc = static_cast<uint32_t>(
@@ -354,7 +378,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const uint32_t need = need2 - p3.above;  // ties at T to keep
     uint32_t gtb = 0, eqb = 0, gtl = 0, eql = 0;
 #pragma unroll
-    for (int q = 0; q < kBlindRounds; ++q) {
+    for (int q = 0; q < kRounds; ++q) {
       const bool ok = (okb >> q) & 1u;
       const bool gt = ok && bl[q].y > T, eq = ok && bl[q].y == T;
       gtb |= static_cast<uint32_t>(gt) << q;
@@ -372,7 +396,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     uint32_t eqr = before >> 16;  // ties in earlier waves
     uint32_t pos = (before & 0xffffu) + (eqr < need ? eqr : need);
 #pragma unroll
-    for (int q = 0; q < kBlindRounds; ++q) {
+    for (int q = 0; q < kRounds; ++q) {
       const bool is_gt = (gtb >> q) & 1u;
       const bool is_eq = (eqb >> q) & 1u;
       const uint64_t me = __ballot(is_eq);
@@ -672,9 +696,12 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
             static_cast<uint32_t>(rows));
   hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kFT), 0, s, scores,
                      stride, row_lens, cap, k, nch, passes, ws);
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(static_cast<uint32_t>(rows)),
-                     dim3(kRT), 0, s, scores, stride, row_lens, cap, k, nch,
-                     ws, idx, count);
+  const int rb = blind_rounds(nch);
+  auto resolve = rb == 0 ? topk_resolve_kernel<0> : rb <= 2 ? topk_resolve_kernel<2>
+               : rb <= 4 ? topk_resolve_kernel<4> : rb <= 8 ? topk_resolve_kernel<8>
+               : topk_resolve_kernel<16>;
+  hipLaunchKernelGGL(resolve, dim3(static_cast<uint32_t>(rows)), dim3(kRT), 0, s,
+                     scores, stride, row_lens, cap, k, nch, ws, idx, count);
   return hipGetLastError();
 }
 
