@@ -42,7 +42,9 @@ struct Tile {
   static constexpr int kRowBytes = kD * kEsz;
   static constexpr int kPitch = kRowBytes + 16;      // LDS row pitch (bytes)
   static constexpr int kBlocks = kTokens / 16 / 4;   // 16-token blocks per wave
-  static constexpr int kZPitch = kTokens + 1;        // logits / probs pitch
+  // logits / probs pitch (floats): 16-byte aligned rows for the FP8 path's
+  // 8-wide P reads
+  static constexpr int kZPitch = ENC == TSD_FP8_E4M3 ? kTokens + 4 : kTokens + 1;
 };
 
 // 8 consecutive 16-bit values (as raw bits) starting at element `e0` of a
@@ -278,15 +280,58 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       acc[1][v] *= a;
     }
     const bool arow = col < G;
+    if constexpr (fp8) {
+      // bf16 MFMA, 32 tokens per instruction: A = P x V-scale rounded once
+      // to bf16 (heads x tokens), B = the FP8 V codes widened exactly
+      // (tokens x dims); lane group grp supplies tokens 8*grp .. 8*grp+7
+#pragma unroll
+      for (int ks = 0; ks < NT / 32; ++ks) {
+        const int t0 = 32 * ks + 8 * grp;
+        v8bf pa;
+        if (arow) {
+          const float4 p0 = *reinterpret_cast<const float4*>(zp_s + col * T::kZPitch + t0);
+          const float4 p1 = *reinterpret_cast<const float4*>(zp_s + col * T::kZPitch + t0 + 4);
+          pa = v8bf{static_cast<__bf16>(p0.x), static_cast<__bf16>(p0.y),
+                    static_cast<__bf16>(p0.z), static_cast<__bf16>(p0.w),
+                    static_cast<__bf16>(p1.x), static_cast<__bf16>(p1.y),
+                    static_cast<__bf16>(p1.z), static_cast<__bf16>(p1.w)};
+        } else {
+          pa = v8bf{};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint8_t* vc = v_s + t0 * T::kPitch + 32 * wave + 16 * j + col;
+          uint32_t w[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            w[h] = static_cast<uint32_t>(vc[(4 * h + 0) * T::kPitch]) |
+                   static_cast<uint32_t>(vc[(4 * h + 1) * T::kPitch]) << 8 |
+                   static_cast<uint32_t>(vc[(4 * h + 2) * T::kPitch]) << 16 |
+                   static_cast<uint32_t>(vc[(4 * h + 3) * T::kPitch]) << 24;
+          float f[8];
+          fp8x4_to_f32(w[0], f);
+          fp8x4_to_f32(w[1], f + 4);
+          uint32_t bb[4];  // an E4M3 value is exact in bf16: its top 16 bits
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            bb[i] = (__float_as_uint(f[2 * i]) >> 16) |
+                    (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pa, __builtin_bit_cast(v8bf, make_uint4(bb[0], bb[1], bb[2], bb[3])),
+              acc[j], 0, 0, 0);
+        }
+      }
+    } else {
 #pragma unroll 4
-    for (int st = 0; st < NT / 4; ++st) {
-      const int t = 4 * st + grp;
-      const float pa = arow ? zp_s[col * T::kZPitch + t] : 0.f;
-      const uint8_t* vrow = v_s + t * T::kPitch;
-      const float b0 = v_elem<ENC>(vrow, 32 * wave + col);
-      const float b1 = v_elem<ENC>(vrow, 32 * wave + 16 + col);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b0, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b1, acc[1], 0, 0, 0);
+      for (int st = 0; st < NT / 4; ++st) {
+        const int t = 4 * st + grp;
+        const float pa = arow ? zp_s[col * T::kZPitch + t] : 0.f;
+        const uint8_t* vrow = v_s + t * T::kPitch;
+        const float b0 = v_elem<ENC>(vrow, 32 * wave + col);
+        const float b1 = v_elem<ENC>(vrow, 32 * wave + 16 + col);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b1, acc[1], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
