@@ -3,10 +3,11 @@
 // with FP32 log-sum-exp normalisation):
 //   M = max_c lse_c, W = sum_c exp(lse_c - M),
 //   out = sum_c exp(lse_c - M) * o_c / W, out_lse = M + log W.
-// One workgroup per (row, 128 output dimensions). The first wave turns the
-// row's C <= 64 LSEs (one per lane) into normalised weights in LDS; then
-// every thread owns one output dimension and issues its C loads of o_part
-// independently, so the whole merge is a single memory round trip.
+// One workgroup per (row, 128 output dimensions). Every thread owns one
+// output dimension and issues the loads of its first 16 chunk partials at
+// once, while the first wave turns the row's C <= 64 LSEs (one per lane)
+// into normalised weights in LDS, so the merge is a single memory round
+// trip for C <= 16.
 #include "device_common.h"
 #include "launch.h"
 
@@ -14,6 +15,7 @@ namespace tsd {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kPre = 16;  // chunk partials each thread loads up front
 
 __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
     const float* __restrict__ o_part, const float* __restrict__ lse_part,
@@ -22,6 +24,12 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
   __shared__ float empty_s;
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
+  const int d = blockIdx.y * kThreads + tid;
+  const float* op = o_part + static_cast<int64_t>(row) * C * D + d;
+  float pre[kPre];  // partials of chunks 0 .. kPre-1, loaded before the weights
+#pragma unroll
+  for (int c = 0; c < kPre; ++c)
+    pre[c] = d < D && c < C ? op[static_cast<int64_t>(c) * D] : 0.f;
   if (tid < kWave) {
     const float* lse = lse_part + static_cast<int64_t>(row) * C;
     const float mine = tid < C ? lse[tid] : -__builtin_inff();
@@ -37,13 +45,14 @@ __global__ __launch_bounds__(kThreads) void lse_merge_kernel(
     }
   }
   __syncthreads();
-  const int d = blockIdx.y * kThreads + tid;
   if (d >= D) return;
-  const float* op = o_part + static_cast<int64_t>(row) * C * D + d;
   float acc = 0.f;
   if (empty_s == 0.f) {
+#pragma unroll
+    for (int c = 0; c < kPre; ++c)
+      if (c < C) acc += w_s[c] * pre[c];
 #pragma unroll 8
-    for (int c = 0; c < C; ++c) acc += w_s[c] * op[static_cast<int64_t>(c) * D];
+    for (int c = kPre; c < C; ++c) acc += w_s[c] * op[static_cast<int64_t>(c) * D];
   }
   out[static_cast<int64_t>(row) * D + d] = acc;
 }
