@@ -91,6 +91,79 @@ def test_qsa_stale_page_table_tail():
     _full_check(cfg)
 
 
+def test_qsa_invalid_pages_inside_rows_score_minus_inf():
+    """Page-table entries inside a row's length that are negative or past
+    the pool: those tokens score -inf (the scan never reads them), every
+    other score matches the oracle on the original table, and the fused
+    selection equals the top-k of those scores."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(QSA, B=2, lens=(5000, 300), top_k=256, chunks=4,
+                           seed=104)
+    wl = tsd_synth.make(cfg, DEV)
+    h = tsd_synth.to_host(wl)
+    ref = oracle_scores(h)
+    pt = wl["page_table"].clone()
+    bad = [(0, 3, -1), (0, 10, wl["num_pages"] + 7), (0, 31, -9), (0, 32, -1),
+           (1, 2, wl["num_pages"])]
+    for r, c, v in bad:
+        pt[r, c] = v
+    B, k = cfg.B, cfg.top_k
+    stride = pt.shape[1] * 64
+    S = torch.full((B, stride), float("nan"), device=DEV)
+    rl = torch.empty(B, dtype=torch.int32, device=DEV)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(B, stride, k),
+                     dtype=torch.uint8, device=DEV)
+    tsd.sparse_index_topk("qsa", S, pt, wl["seq_lens"], wl["num_pages"], k,
+                          idx, cnt, ws, rl, index_q=wl["index_q"],
+                          index_w=wl["index_w"], index_k_pool=wl["index_k"])
+    torch.cuda.synchronize()
+    gs = S.cpu().numpy()
+    lens = h["seq_lens"]
+    mask = np.zeros_like(gs, dtype=bool)
+    for r, c, _ in bad:
+        mask[r, c * 64:(c + 1) * 64] = True
+    for r in range(B):
+        n = int(lens[r])
+        bad_r = mask[r, :n]
+        assert np.isneginf(gs[r, :n][bad_r]).all()
+        err = np.abs(gs[r, :n][~bad_r] - ref[r, :n][~bad_r]).max()
+        assert err <= score_tol("qsa"), err
+        assert np.isnan(gs[r, n:]).all()
+    check_topk_identical(gs, lens.astype(np.int64), k, idx.cpu().numpy(),
+                         cnt.cpu().numpy())
+
+
+def test_qsa_empty_pool_scores_minus_inf():
+    """num_pages = 0: every token is on a page outside the pool, so every
+    score is -inf and the selection is the first k tokens (lowest index
+    among equal scores); the pool is never read."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(QSA, B=3, lens=(3000, 100, 0), top_k=128, chunks=2,
+                           seed=105)
+    wl = tsd_synth.make(cfg, DEV)
+    B, k = cfg.B, cfg.top_k
+    stride = wl["page_table"].shape[1] * 64
+    S = torch.full((B, stride), float("nan"), device=DEV)
+    rl = torch.empty(B, dtype=torch.int32, device=DEV)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    cnt = torch.empty(B, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tsd.topk_select_workspace_bytes(B, stride, k),
+                     dtype=torch.uint8, device=DEV)
+    tsd.sparse_index_topk("qsa", S, wl["page_table"], wl["seq_lens"], 0, k,
+                          idx, cnt, ws, rl, index_q=wl["index_q"],
+                          index_w=wl["index_w"], index_k_pool=wl["index_k"])
+    torch.cuda.synchronize()
+    gs, gi, gc = S.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    for r, n in enumerate(cfg.lens):
+        assert np.isneginf(gs[r, :n]).all() and np.isnan(gs[r, n:]).all()
+        m = min(n, k)
+        assert gc[r] == m
+        np.testing.assert_array_equal(gi[r, :m], np.arange(m))
+        assert (gi[r, m:] == -1).all()
+
+
 def test_qsa_partial_index_heads():
     cfg = tsd_synth.config(QSA, B=2, lens=(900, 333), top_k=128, chunks=2,
                            H_i=5, seed=103)
@@ -265,6 +338,24 @@ def test_topk_large_rows_with_ties(n, k, levels):
     ridx, rcnt = oracle.topk(s, lens, k)
     np.testing.assert_array_equal(gcnt, rcnt)
     np.testing.assert_array_equal(gidx, ridx)
+
+
+def test_topk_rows_past_one_million_entries():
+    """Rows of more than 1,048,576 entries (more chunks than the resolve's
+    blind reads cover): the staged and bitmap paths, against the oracle."""
+    rng = np.random.default_rng(2200000)
+    n = 2_200_000
+    s = np.empty((3, n), np.float32)
+    s[0] = rng.normal(size=n)
+    s[1] = (rng.integers(0, 30, size=n) / 30).astype(np.float32)  # heavy ties
+    s[2] = rng.normal(size=n)
+    s[2, 1_500_000:1_504_096] += 30.0   # the top values in one chunk
+    lens = [n, n - 3, 1_200_001]
+    for k in (2048, 4096):
+        gidx, gcnt = _topk_gpu(s, lens, k)
+        ridx, rcnt = oracle.topk(s, lens, k)
+        np.testing.assert_array_equal(gcnt, rcnt)
+        np.testing.assert_array_equal(gidx, ridx)
 
 
 def test_topk_ties_at_threshold_and_one_overflowing_chunk():
