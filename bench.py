@@ -313,6 +313,64 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
             "block_selection_step_us": us_chain}
 
 
+def ds_decode(dev, name, steps, warmup):
+    """One double-sparsity decode step (label scan + exact top-k through
+    sparse_index_topk, per-KV-head sparse attention, LSE merge) on workload
+    ``name``: K eager steps over label-pool replicas (about 1 GB of labels
+    between two visits of a replica, so the Infinity Cache cannot serve the
+    scan; K/V pools are shared, their gather being a small random read),
+    then the label scan alone over back-to-back launches with HIP events.
+    Roofline: label bytes of every cached token per scan launch."""
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd.step as step
+    cfg = tsd_synth.config(name)
+    index_b, gather_b = model_bytes(cfg)
+    R = max(1, math.ceil(1e9 / index_b))
+    wl = tsd_synth.make(cfg, dev)
+    layers = [wl] + [dict(wl, label_pool=wl["label_pool"].clone())
+                     for _ in range(R - 1)]
+    bufs = step.StepBuffers(wl)
+    plans = [step.Plan(layer, bufs, fused=True) for layer in layers]
+    plans_sep = [step.Plan(layer, bufs, fused=False) for layer in layers]
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        plans[i % R].run(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        plans[i % R].run(stream)
+    torch.cuda.synchronize()
+    step_s = (time.perf_counter() - t0) / steps
+    calls = [dict(p.calls(stream))["sparse_index_score"] for p in plans_sep]
+    for i in range(warmup):
+        calls[i % R]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        calls[i % R]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    scan_us = e0.elapsed_time(e1) * 1e3 / steps
+    scan_gbps = index_b / (scan_us * 1e-6) / 1e9
+    del layers, plans, plans_sep, bufs, wl
+    torch.cuda.empty_cache()
+    return {"workload": name, "batch": cfg.B, "context": cfg.L,
+            "heavy_channels": cfg.r, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
+            "top_k": cfg.top_k, "chunks": cfg.chunks, "kv_cache": cfg.kv_enc,
+            "steps_per_s": 1.0 / step_s, "ms_per_step": step_s * 1e3,
+            "model_bytes_per_step": index_b + gather_b,
+            "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
+            "label_scan_us": scan_us,
+            "roofline": {"bound": "hbm", "kernel": "sparse_index_score (label scan)",
+                         "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                         "bytes_per_launch": index_b}}
+
+
 def append_bench(dev, passes, warmup):
     """kv_append at decode shapes, one new token per request, timed per call
     (pre-marshalled C calls) over back-to-back launches with HIP events: the
@@ -388,6 +446,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the chunked-prefill indexer measurement")
     ap.add_argument("--prefill-passes", type=int, default=5)
+    ap.add_argument("--no-ds", action="store_true",
+                    help="skip the double-sparsity decode measurements")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the block-compressed selection measurement")
     ap.add_argument("--no-sharded", action="store_true",
@@ -559,6 +619,9 @@ def main():
     if not args.no_sharded:
         line["sharded_topk"] = sharded_select(dev, 200, 20)
     line["kv_append"] = append_bench(dev, 500, 20)
+    if not args.no_ds:
+        line["ds_decode"] = [ds_decode(dev, n, 500, 50) for n in
+                             ("ds_llama31_8b_b3_l60000", "ds_llama7b_b3_l20000_s200")]
     if not args.no_blocks:
         line["block_compressed_select"] = block_select(dev, 200, 20)
     print(json.dumps(line), flush=True)

@@ -205,6 +205,11 @@ def test_qsa_causal_prefill_rows():
     ("ds_tiny_b1_l4096", dict(lens=(4096,))),
     (DS8B, dict(B=2, lens=(2000, 900), top_k=128, chunks=3, channel_type="q")),
     (DS8B, dict(B=2, lens=(2000, 900), top_k=128, chunks=3, channel_type="qk")),
+    (DS8B, dict(B=2, lens=(5000, 333), r=64, n_outlier=40, top_k=150, chunks=3)),
+    (DS8B, dict(B=1, H_q=8, H_kv=4, lens=(4100,), r=128, n_outlier=16, top_k=90,
+                chunks=2)),
+    (DS7B, dict(B=2, H_q=12, H_kv=12, lens=(9000, 130), top_k=300, chunks=5,
+                steps=0)),
 ])
 def test_ds_decode_path(name, over):
     cfg = tsd_synth.config(name, seed=111, **over)
@@ -215,6 +220,44 @@ def test_ds_stale_tail_and_empty_request():
     cfg = tsd_synth.config(DS8B, B=3, lens=(0, 1000, 65), top_k=128, chunks=3,
                            stale_tail=True, seed=112)
     _full_check(cfg)
+
+
+def test_ds_invalid_pages_inside_rows_score_minus_inf():
+    """Label scan with page ids inside a row's length that are negative or
+    past the pool: every head's score is -inf on those pages, every other
+    score matches the oracle on the original page table."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(DS8B, B=2, lens=(9000, 500), top_k=64, chunks=2,
+                           seed=113)
+    wl = tsd_synth.make(cfg, DEV)
+    h = tsd_synth.to_host(wl)
+    ref = oracle_scores(h)
+    pt = wl["page_table"].clone()
+    bad = [(0, 0, -1), (0, 77, wl["num_pages"] + 3), (0, 140, -2),
+           (1, 7, wl["num_pages"])]
+    for r, c, v in bad:
+        pt[r, c] = v
+    H = cfg.H_kv
+    stride = pt.shape[1] * 64
+    S = torch.full((cfg.B * H, stride), float("nan"), device=DEV)
+    rl = torch.empty(cfg.B * H, dtype=torch.int32, device=DEV)
+    tsd.sparse_index_score("ds", S, pt, wl["seq_lens"], wl["num_pages"],
+                           q=wl["q"], channel_idx=wl["channel_idx"],
+                           label_pool=wl["label_pool"], row_lens_out=rl)
+    torch.cuda.synchronize()
+    gs = S.cpu().numpy()
+    for b in range(cfg.B):
+        n = int(h["seq_lens"][b])
+        m = np.zeros(n, dtype=bool)
+        for r, c, _ in bad:
+            if r == b:
+                m[c * 64:min(n, (c + 1) * 64)] = True
+        for g in range(H):
+            row = b * H + g
+            assert np.isneginf(gs[row, :n][m]).all()
+            err = np.abs(gs[row, :n][~m] - ref[row, :n][~m]).max()
+            assert err <= score_tol("ds"), err
+            assert np.isnan(gs[row, n:]).all()
 
 
 # --------------------------------------------------------------- top-k only

@@ -4,11 +4,22 @@
 //   s[b*H_kv+g][t] = sum_j qs[g][j] * label[slot(b,t)][g][j],
 //   qs[g][j]       = sum of the group's query heads at channel chan[g][j].
 //
-// About 1 flop per byte, so this is a plain bandwidth-bound VALU pass. One
-// workgroup owns one 64-token page of one request and covers every KV head:
-// the page's labels ([64][H_kv][r] 16-bit values) are one contiguous block,
-// read with 16-byte loads in order. Scores go through LDS so each
-// (request, head) row receives 64 contiguous floats.
+// About 1 flop per byte, so this is a plain bandwidth-bound VALU pass. The
+// labels of a page ([64][H_kv][r] 16-bit values) are one contiguous block.
+//
+// ds_scan_vec_kernel (r a multiple of 8, 16-byte aligned pool): one
+// workgroup owns a run of pages of one request. It computes qs once, keeps
+// the run's page ids in LDS, and streams the pages as 32 KB sub-blocks (8
+// 16-byte loads per thread), the next sub-block's loads in flight while the
+// current one is summed; the loads are unconditional (a page outside the
+// pool reads page 0 and scores -inf), so the compiler can count them. A
+// label spans VPI = r/8 consecutive vectors, held by VPI consecutive lanes
+// whose partial dots are added by lane exchanges; when every lane always
+// meets the same head and channels (256/VPI a multiple of H_kv) its slice of
+// qs sits in registers. A page's scores are staged in LDS and stored as 64
+// contiguous floats per (request, head) row.
+//
+// ds_scan_kernel: the general form, one workgroup per page.
 #include "device_common.h"
 #include "launch.h"
 
@@ -57,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
   const int items = kPage * H_kv;  // (slot s, head g), g fastest
   if (valid) {
     const uint16_t* base = label + static_cast<int64_t>(page) * kPage * hc;
-    if ((r & 7) == 0) {
+    if ((r & 7) == 0 && (reinterpret_cast<uintptr_t>(label) & 15u) == 0) {
       const int vecs = r >> 3;  // 16-byte vectors per label
       for (int it = threadIdx.x; it < items; it += kThreads) {
         const int g = it % H_kv;
@@ -99,10 +110,166 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
   }
 }
 
+constexpr int kSubVec = kThreads * 8;  // 16-byte vectors per sub-block
+
+template <int VPI, bool QREG>
+__global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
+    const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
+    const int32_t* __restrict__ chan, int r,
+    const uint16_t* __restrict__ label, const int32_t* __restrict__ page_table,
+    int64_t pt_stride, const int32_t* __restrict__ seq_lens,
+    int64_t num_pages, float* __restrict__ scores, int64_t score_stride,
+    int32_t* __restrict__ row_lens_out, int P) {
+  extern __shared__ __align__(16) float dyn_s[];
+  const int hc = H_kv * r;
+  float* qs = dyn_s;                              // [hc]
+  float* sc = dyn_s + hc;                         // [2][64 * H_kv]
+  int32_t* pages_s = reinterpret_cast<int32_t*>(sc + 2 * kPage * H_kv);  // [P]
+  const int b = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t pp0 = static_cast<int64_t>(blockIdx.x) * P;
+  int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
+  n = clamp_len(n, score_stride);
+  if (blockIdx.x == 0 && row_lens_out)
+    for (int g = tid; g < H_kv; g += kThreads)
+      row_lens_out[static_cast<int64_t>(b) * H_kv + g] = static_cast<int32_t>(n);
+  if (pp0 * kPage >= n) return;  // uniform
+  const int64_t left = (n - pp0 * kPage + kPage - 1) / kPage;
+  const int npg = left < P ? static_cast<int>(left) : P;
+  const int G = H_q / H_kv;
+  for (int i = tid; i < hc; i += kThreads) {  // group query at the channels
+    const int g = i / r;
+    const int c = chan[i];
+    float acc = 0.f;
+    if (c >= 0 && c < D) {
+      const uint16_t* qb = q + (static_cast<int64_t>(b) * H_q + g * G) * D + c;
+      for (int h = 0; h < G; ++h) acc += half_to_f32(qb[h * D], is_bf16);
+    }
+    qs[i] = acc;
+  }
+  for (int i = tid; i < npg; i += kThreads) {
+    const int32_t page = page_table[static_cast<int64_t>(b) * pt_stride + pp0 + i];
+    pages_s[i] = page >= 0 && page < num_pages ? page : -1;
+  }
+  __syncthreads();
+
+  const int VP = 8 * hc;                          // vectors per page
+  const int SB = (VP + kSubVec - 1) / kSubVec;    // sub-blocks per page
+  const int units = npg * SB;
+  const int part = tid % VPI;                     // this lane's label vector
+  float qr[8];  // QREG: this lane's slice of qs (head (tid / VPI) % H_kv)
+  auto load_unit = [&](int u, uint4 (&x)[8]) {
+    const int pg = u / SB, sub = u - pg * SB;
+    int32_t page = pages_s[pg];
+    page = page < 0 ? 0 : page;                   // invalid: page 0, masked
+    const uint4* base = reinterpret_cast<const uint4*>(label) +
+                        static_cast<int64_t>(page) * VP;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int vv = sub * kSubVec + i * kThreads + tid;
+      vv = vv < VP ? vv : VP - 1;
+      x[i] = base[vv];
+    }
+  };
+  auto sum_unit = [&](int u, const uint4 (&x)[8]) {
+    const int pg = u / SB, sub = u - pg * SB;
+    const bool ok = pages_s[pg] >= 0;
+    float* scp = sc + (pg & 1) * kPage * H_kv;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int vv = sub * kSubVec + i * kThreads + tid;
+      const int item = vv / VPI;                  // (slot, head), head fastest
+      const int g = item % H_kv;
+      float w[8];
+      const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        w[2 * e] = half_to_f32(static_cast<uint16_t>(wd[e] & 0xFFFF), is_bf16);
+        w[2 * e + 1] = half_to_f32(static_cast<uint16_t>(wd[e] >> 16), is_bf16);
+      }
+      float acc = 0.f;
+      if constexpr (QREG) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += qr[e] * w[e];
+      } else {
+        const float* qg = qs + g * r + part * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc += qg[e] * w[e];
+      }
+#pragma unroll
+      for (int m = 1; m < VPI; m <<= 1) acc += __shfl_xor(acc, m);
+      if (part == 0 && vv < VP)
+        scp[g * kPage + item / H_kv] = ok ? acc : -__builtin_inff();
+    }
+  };
+  uint4 xa[8], xb[8];
+  load_unit(0, xa);
+  if constexpr (QREG) {  // this lane always meets head (tid / VPI) % H_kv
+    const int g = (tid / VPI) % H_kv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qr[e] = qs[g * r + part * 8 + e];
+  }
+  for (int u = 0; u < units; u += 2) {
+    if (u + 1 < units) load_unit(u + 1, xb);
+    sum_unit(u, xa);
+    if (u + 2 < units) load_unit(u + 2, xa);
+    if (u + 1 < units) sum_unit(u + 1, xb);
+    // a page is complete after its last sub-block: store its scores
+    for (int d = 0; d < 2; ++d) {
+      const int uu = u + d;
+      if (uu >= units || (uu + 1) % SB != 0) continue;  // uniform
+      __syncthreads();
+      const int pg = uu / SB;
+      const float* scp = sc + (pg & 1) * kPage * H_kv;
+      for (int it = tid; it < kPage * H_kv; it += kThreads) {
+        const int g = it / kPage, sl = it % kPage;
+        const int64_t t = (pp0 + pg) * kPage + sl;
+        if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = scp[it];
+      }
+      __syncthreads();  // the buffer is written again two pages later
+    }
+  }
+}
+
+template <int VPI>
+bool launch_vec(const tsd_score_args& a, hipStream_t s) {
+  const int hc = a.H_kv * a.r;
+  const int64_t total_pages = a.pt_stride * a.B;
+  int P = static_cast<int>(total_pages / 1536);  // about 1,536 workgroups or more
+  P = P < 1 ? 1 : (P > 64 ? 64 : P);
+  const size_t lds = static_cast<size_t>(hc + 2 * kPage * a.H_kv + P) * 4;
+  dim3 grid(static_cast<uint32_t>((a.pt_stride + P - 1) / P), static_cast<uint32_t>(a.B));
+  const bool qreg = (kThreads / VPI) % a.H_kv == 0;
+  if (qreg)
+    hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, true>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
+                       a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
+                       a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
+                       a.score_stride, a.row_lens_out, P);
+  else
+    hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, false>), grid, dim3(kThreads), lds, s,
+                       static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
+                       a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
+                       a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
+                       a.score_stride, a.row_lens_out, P);
+  return true;
+}
+
 }  // namespace
 
 hipError_t launch_ds_scan(const tsd_score_args& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.label_pool) & 15u) == 0;
+  if (aligned && a.num_pages > 0 && a.r % 8 == 0) {
+    switch (a.r / 8) {
+      case 1: launch_vec<1>(a, s); return hipGetLastError();
+      case 2: launch_vec<2>(a, s); return hipGetLastError();
+      case 4: launch_vec<4>(a, s); return hipGetLastError();
+      case 8: launch_vec<8>(a, s); return hipGetLastError();
+      case 16: launch_vec<16>(a, s); return hipGetLastError();
+      default: break;  // r = 24, 40, ...: the general kernel
+    }
+  }
   dim3 grid(static_cast<uint32_t>(a.pt_stride), static_cast<uint32_t>(a.B));
   hipLaunchKernelGGL(ds_scan_kernel, grid, dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16,
