@@ -319,8 +319,8 @@ def ds_decode(dev, name, steps, warmup):
     ``name``: K eager steps over label-pool replicas (about 1 GB of labels
     between two visits of a replica, so the Infinity Cache cannot serve the
     scan; K/V pools are shared, their gather being a small random read),
-    then the label scan alone over back-to-back launches with HIP events.
-    Roofline: label bytes of every cached token per scan launch."""
+    then each of the four calls alone over back-to-back launches with HIP
+    events. Roofline: label bytes of every cached token per scan launch."""
     import torch
 
     import tsd_synth
@@ -343,18 +343,22 @@ def ds_decode(dev, name, steps, warmup):
         plans[i % R].run(stream)
     torch.cuda.synchronize()
     step_s = (time.perf_counter() - t0) / steps
-    calls = [dict(p.calls(stream))["sparse_index_score"] for p in plans_sep]
-    for i in range(warmup):
-        calls[i % R]()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        calls[i % R]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    scan_us = e0.elapsed_time(e1) * 1e3 / steps
+    table = [dict(p.calls(stream)) for p in plans_sep]
+    us = {}
+    for call in ("sparse_index_score", "topk_select", "sparse_gqa_decode",
+                 "lse_merge"):
+        for i in range(warmup):
+            plans_sep[i % R].run(stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            table[i % R][call]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[call] = e0.elapsed_time(e1) * 1e3 / steps
+    scan_us = us["sparse_index_score"]
     scan_gbps = index_b / (scan_us * 1e-6) / 1e9
     del layers, plans, plans_sep, bufs, wl
     torch.cuda.empty_cache()
@@ -364,7 +368,7 @@ def ds_decode(dev, name, steps, warmup):
             "steps_per_s": 1.0 / step_s, "ms_per_step": step_s * 1e3,
             "model_bytes_per_step": index_b + gather_b,
             "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
-            "label_scan_us": scan_us,
+            "label_scan_us": scan_us, "kernel_us": us,
             "roofline": {"bound": "hbm", "kernel": "sparse_index_score (label scan)",
                          "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
                          "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,

@@ -350,18 +350,21 @@ def test_fused_topk_reuses_a_zeroed_workspace():
         check_topk_identical(outs[0][0], lens, k, outs[0][1], outs[0][2])
 
 
-def test_topk_special_rows_bit_exact():
+@pytest.mark.parametrize("stride", [10000, 70000])
+def test_topk_special_rows_bit_exact(stride):
+    """Degenerate rows on the one-workgroup path (rows of at most 32,768
+    entries) and, with the same rows in a wider buffer, the chunked path."""
     rng = np.random.default_rng(5)
-    stride, k = 10000, 300
-    rows = []
+    k = 300
     lens = [0, 1, 299, 300, 301, 10000, 10000, 10000, 10000, 9999, 5000]
-    s = rng.normal(size=(len(lens), stride)).astype(np.float32)
-    s[5] = 3.25                                  # all equal
-    s[6] = rng.choice([-0.0, 0.0], size=stride)  # signed zeros only
-    s[7, ::7] = np.inf
-    s[7, 1::7] = -np.inf
-    s[8] = rng.integers(0, 4, size=stride).astype(np.float32)  # heavy ties
-    s[9] = -np.abs(s[9])                         # all negative
+    s = np.full((len(lens), stride), np.nan, dtype=np.float32)
+    s[:, :10000] = rng.normal(size=(len(lens), 10000)).astype(np.float32)
+    s[5, :10000] = 3.25                          # all equal
+    s[6, :10000] = rng.choice([-0.0, 0.0], size=10000)  # signed zeros only
+    s[7, :10000:7] = np.inf
+    s[7, 1:10000:7] = -np.inf
+    s[8, :10000] = rng.integers(0, 4, size=10000).astype(np.float32)  # ties
+    s[9, :10000] = -np.abs(s[9, :10000])         # all negative
     s[10, :5000] = np.linspace(1, 0, 5000)       # strictly decreasing
     gidx, gcnt = _topk_gpu(s, lens, k)
     ridx, rcnt = oracle.topk(s, lens, k)
@@ -369,6 +372,56 @@ def test_topk_special_rows_bit_exact():
     np.testing.assert_array_equal(gidx, ridx)
     assert (gidx[5, :300] == np.arange(300)).all()
     assert (gidx[0] == -1).all() and gcnt[0] == 0
+
+
+@pytest.mark.parametrize("max_len,k", [(300, 1), (4096, 256), (4097, 4096),
+                                       (8192, 2048), (8193, 300), (16385, 1024),
+                                       (20224, 1024), (32768, 4096), (32769, 1),
+                                       (60032, 3000)])
+def test_topk_one_workgroup_rows(max_len, k):
+    """Rows of at most 32,768 entries (the whole row in one workgroup's
+    registers), across the register templates and their boundaries, and
+    just past them on the chunked path: normal values, three levels (ties
+    at the threshold), rows of n = k, k + 1, a ragged tail and an empty row,
+    against the oracle."""
+    rng = np.random.default_rng(max_len * 7 + k)
+    rows = 6
+    s = np.empty((rows, max_len), np.float32)
+    s[0] = rng.normal(size=max_len)
+    s[1] = (rng.integers(0, 3, size=max_len) / 3).astype(np.float32)
+    s[2] = rng.normal(size=max_len)
+    s[3] = rng.normal(size=max_len)
+    s[4] = np.float32(1.0)
+    s[5] = rng.normal(size=max_len)
+    lens = [max_len, max_len - 1, min(k, max_len), min(k + 1, max_len),
+            max(1, max_len // 3 + 17), 0]
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+
+
+def test_topk_one_workgroup_rows_clear_an_unflagged_workspace():
+    """The one-workgroup path reads no workspace, yet an unflagged call still
+    leaves the histogram words zero for the flagged calls that follow."""
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(31)
+    rows, max_len, k = 4, 20000, 1024
+    s = rng.normal(size=(rows, max_len)).astype(np.float32)
+    lens = [20000, 19999, 5000, 1024]
+    ws = torch.full((tsd.topk_select_workspace_bytes(rows, max_len, k),), 0x3C,
+                    dtype=torch.uint8, device=DEV)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    for zeroed in (False, True):
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+        cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+        tsd.topk_select(torch.from_numpy(s).to(DEV),
+                        torch.tensor(lens, dtype=torch.int32, device=DEV), k,
+                        max_len, idx, cnt, ws, ws_zeroed=zeroed)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(cnt.cpu().numpy(), rcnt)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+        assert not _hist_words(ws, rows).any()
 
 
 @pytest.mark.parametrize("n,k,levels", [(50000, 3000, 3), (262144, 2048, 50),

@@ -28,6 +28,12 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               const int32_t* row_lens, int max_len, int k,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s);
+// Rows of at most 32,768 elements: the whole selection in one launch, one
+// workgroup per row (no workspace).
+bool topk_small_fits(int max_len);
+hipError_t launch_topk_small(const float* scores, int64_t stride, int rows,
+                             const int32_t* row_lens, int max_len, int k,
+                             int32_t* idx, int32_t* count, hipStream_t s);
 hipError_t launch_topk(const float* scores, int64_t stride, int rows,
                        const int32_t* row_lens, int max_len, int k,
                        int32_t* idx, int32_t* count, void* ws, bool zeroed,

@@ -47,6 +47,7 @@ constexpr int kMaxChunks = 4096;       // max_len <= 2^24
 constexpr int kStage = 8192;           // survivors the pass-3 fast path holds
 constexpr int kPerLane = kStage / kRT; // survivors per lane on that path
 constexpr int kBlindRounds = 16;       // list reads per lane on the blind path
+constexpr int kSmallMax = 32 * kRT;   // longest rows of the one-workgroup path
 
 TSD_DEVICE uint32_t digit1(uint32_t key) { return topk_digit1(key); }
 TSD_DEVICE uint32_t digit2(uint32_t key) {
@@ -266,22 +267,34 @@ TSD_DEVICE void clean_row(const Ws& ws, int row) {
   for (int i = threadIdx.x; i < kBins2 / 4; i += kRT) h2[i] = z;
 }
 
-// Blind rounds of the resolve for nch chunks per row: wave w takes chunks
-// [w*R, w*R + R), reading 64*H list entries of each (H = 2 when a wave has at
-// most 8 chunks, else 1); 0 when R*H exceeds kBlindRounds (no blind path).
-int blind_rounds(int nch) {
+// Blind plan of the resolve for nch chunks per row: wave w takes chunks
+// [w*R, w*R + R) and reads the first 64*H list entries of each, R*H rounds
+// per lane. H is the smallest power of two whose 64*H entries hold three
+// times the survivors a chunk keeps on average (k of max_len, so about
+// 4096*k/max_len), at most the whole list (512 entries) and at most
+// kBlindRounds rounds in all; rounds = 0 when R alone exceeds kBlindRounds
+// (no blind path).
+struct BlindPlan {
+  int rounds, H;
+};
+BlindPlan blind_plan(int nch, int k, int max_len) {
   const int R = (nch + kRT / kWave - 1) / (kRT / kWave);
-  const int H = R * 2 <= kBlindRounds ? 2 : 1;
-  return R * H <= kBlindRounds ? R * H : 0;
+  if (R > kBlindRounds) return {0, 1};
+  const int64_t want = 3 * (static_cast<int64_t>(kChunk) * k / (max_len > 0 ? max_len : 1));
+  int H = 1;
+  while (H < kListCap / kWave && static_cast<int64_t>(kWave) * H < want &&
+         R * H * 2 <= kBlindRounds)
+    H *= 2;
+  return {R * H, H};
 }
 
-// RB: blind rounds compiled in (2, 4, 8 or 16, at least blind_rounds(nch)),
+// RB: blind rounds compiled in (2, 4, 8 or 16, at least the blind plan's),
 // or 0 for rows with no blind path.
 template <int RB>
 __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
-    void* __restrict__ ws_base, int32_t* __restrict__ idx,
+    int H, void* __restrict__ ws_base, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
   __shared__ uint32_t off_s[kMaxChunks + 1];  // survivors before chunk c
   __shared__ __align__(16) uint32_t hist[kBins3];
@@ -301,8 +314,8 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   // count are ignored; when every live chunk holds at most 64*H survivors
   // this is the whole survivor sequence, wave-contiguous, after a single
   // round trip.
-  // Round q of a lane covers chunk wave*R + q/H, entry 64*(q%H) + lane: H = 2
-  // (128 entries per chunk) when a wave has at most 8 chunks, else 1.
+  // Round q < R*H of a lane covers chunk wave*R + q/H, entry 64*(q%H) + lane
+  // (H from the launcher's blind plan).
   // The row's records are loaded first and every blind read is
   // unconditional (a chunk index past nch reads the last chunk and is
   // masked at use), so the compiler can count the loads in flight and the
@@ -310,7 +323,6 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   constexpr bool kBlind = RB > 0;
   constexpr int kRounds = kBlind ? RB : 1;
   const int R = (nch + kWavesR - 1) / kWavesR;
-  const int H = R * 2 <= kBlindRounds ? 2 : 1;
   const uint32_t h2v = ws.h2[static_cast<int64_t>(row) * kBins2 + (kBins2 - 1 - tid)];
   const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 2
   const int64_t n = clamp_len(row_lens[row], cap);
@@ -634,6 +646,162 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   clean_row(ws, row);
 }
 
+// Rows of at most 1,024 * RPT elements: one workgroup per row holds the
+// whole row in registers, element r * 1024 + t in round r of thread t, so
+// the row is read once and every pass runs on chip. Digits 1, 2 and 3 are
+// histogrammed in LDS in turn (each pass over the candidates of the
+// previous digits), giving T and the number of ties at T to keep; then the
+// (round, wave) blocks of 64 consecutive indices, in index order, are
+// ranked by an exclusive scan of their counts above T and at T, and each
+// kept entry is stored at (kept before its block) + (kept lanes before it
+// in the block).
+// Lanes of the last round that lie past the row take key 0, the smallest
+// key, in every pass: the k-th largest key is unchanged, none of them is
+// above it, and as ties they follow every real tie in index order, of
+// which there are at least as many as are kept, so none is kept. Rounds
+// wholly past the row are skipped (a uniform branch).
+// Digit 1 is counted in four copies of the histogram, lane l adding to copy
+// l % 4, each copy starting one bank after the previous, so lanes of one
+// wave that share a bin mostly update different words.
+template <int RPT>
+__global__ __launch_bounds__(kRT) void topk_small_kernel(
+    const float* __restrict__ scores, int64_t stride,
+    const int32_t* __restrict__ row_lens, int64_t cap, int k,
+    int32_t* __restrict__ idx, int32_t* __restrict__ count) {
+  constexpr int kWavesR = kRT / kWave;
+  constexpr int kBlocks = RPT * kWavesR;  // (round, wave) blocks
+  constexpr int kCopies = 4;
+  constexpr int kCopyPitch = kBins1 + 1;
+  static_assert(kBlocks <= kRT, "one block count per thread");
+  static_assert(kBins1 == 4 * kRT && kBins2 == kRT && kBins3 == kRT, "bins");
+  __shared__ uint32_t h1[kCopies * kCopyPitch];
+  __shared__ __align__(16) uint32_t h2[kBins2];
+  __shared__ __align__(16) uint32_t h3[kBins3];
+  __shared__ uint32_t gt_s[kBlocks], eq_s[kBlocks];
+  __shared__ uint32_t lds[kRT / kWave + 1];
+  __shared__ BinPick pick;
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int64_t n = clamp_len(row_lens[row], cap);
+  int32_t* out = idx + static_cast<int64_t>(row) * k;
+  if (n <= k) {
+    for (int64_t j = tid; j < k; j += kRT)
+      out[j] = j < n ? static_cast<int32_t>(j) : -1;
+    if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
+    return;
+  }
+  // every load is unconditional (an index past the row reads its last
+  // element), so the first histogram consumes the row while the rest of it
+  // is still in flight
+  const int n32 = static_cast<int>(n);  // n <= 32,768 here
+  // rounds holding elements, a scalar; each pass takes a fresh copy so no
+  // per-round condition is kept from one pass to the next
+  const int nr = __builtin_amdgcn_readfirstlane((n32 + kRT - 1) / kRT);
+  auto rounds = [nr]() {
+    int v = nr;
+    asm volatile("" : "+s"(v));
+    return v;
+  };
+  const float* s = scores + row * stride;
+  uint32_t key[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int i = r * kRT + tid;
+    key[r] = __float_as_uint(s[i < n32 ? i : n32 - 1]);
+  }
+  for (int i = tid; i < kCopies * kCopyPitch; i += kRT) h1[i] = 0u;
+  h2[tid] = 0u;
+  h3[tid] = 0u;
+  __syncthreads();
+  uint32_t* h1c = h1 + (lane & (kCopies - 1)) * kCopyPitch;
+  {
+    const int nr1 = rounds();
+    const int lim = n32 - tid;  // round r of this lane is in the row iff r * 1024 < lim
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const uint32_t live = 0u - static_cast<uint32_t>(r * kRT < lim);
+      key[r] = order_key(__uint_as_float(key[r])) & live;
+      if (r < nr1) atomicAdd(&h1c[digit1(key[r])], 1u);
+    }
+  }
+  __syncthreads();
+  BinPick p1;
+  {
+    uint32_t h[kBins1 / kRT];  // this thread's run of bins, from the top down
+    const int base = kBins1 - (tid + 1) * (kBins1 / kRT);
+#pragma unroll
+    for (int j = 0; j < kBins1 / kRT; ++j) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < kCopies; ++q) c += h1[q * kCopyPitch + base + kBins1 / kRT - 1 - j];
+      h[j] = c;
+    }
+    p1 = pick_bin_runs<kBins1, kRT>(h, static_cast<uint32_t>(k), lds, &pick);
+  }
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  {
+    const int nr2 = rounds();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      if (r < nr2 && digit1(key[r]) == p1.bin) atomicAdd(&h2[digit2(key[r])], 1u);
+  }
+  __syncthreads();
+  const BinPick p2 = pick_bin<kBins2, kRT>(h2, k - p1.above, lds, &pick);
+  const uint32_t pre = (p1.bin << kB2) | p2.bin;  // first 22 bits of T
+  const uint32_t need2 = k - p1.above - p2.above;
+  {
+    const int nr3 = rounds();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      if (r < nr3 && prefix12(key[r]) == pre) atomicAdd(&h3[key[r] & (kBins3 - 1)], 1u);
+  }
+  __syncthreads();
+  const BinPick p3 = pick_bin<kBins3, kRT>(h3, need2, lds, &pick);
+  const uint32_t T = (pre << kB3) | p3.bin;
+  const uint32_t need = need2 - p3.above;  // ties at T to keep
+  // counts above T and at T of every (round, wave) block
+  const int nr4 = rounds();
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const uint32_t g = static_cast<uint32_t>(__popcll(__ballot(key[r] > T)));
+    const uint32_t q = static_cast<uint32_t>(__popcll(__ballot(key[r] == T)));
+    if (lane == 0) {
+      gt_s[r * kWavesR + wave] = r < nr4 ? g : 0u;
+      eq_s[r * kWavesR + wave] = r < nr4 ? q : 0u;
+    }
+  }
+  __syncthreads();
+  {
+    const uint32_t g = tid < kBlocks ? gt_s[tid] : 0u;
+    const uint32_t q = tid < kBlocks ? eq_s[tid] : 0u;
+    const uint32_t gb = block_exclusive_scan<kRT>(g, lds);
+    const uint32_t qb = block_exclusive_scan<kRT>(q, lds);
+    if (tid < kBlocks) {
+      gt_s[tid] = gb;
+      eq_s[tid] = qb;
+    }
+  }
+  __syncthreads();
+  const int gbl = lane < RPT ? static_cast<int>(gt_s[lane * kWavesR + wave]) : 0;
+  const int qbl = lane < RPT ? static_cast<int>(eq_s[lane * kWavesR + wave]) : 0;
+  const int nr5 = rounds();
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    if (r >= nr5) continue;
+    const uint32_t gb = static_cast<uint32_t>(__builtin_amdgcn_readlane(gbl, r));
+    const uint32_t qb = static_cast<uint32_t>(__builtin_amdgcn_readlane(qbl, r));
+    const bool gt = key[r] > T, eq = key[r] == T;
+    const uint64_t me = __ballot(eq);
+    const uint32_t rank = qb + static_cast<uint32_t>(__popcll(me & lt));
+    const bool kept = gt || (eq && rank < need);
+    const uint64_t mk = __ballot(kept);
+    const uint32_t p = gb + (qb < need ? qb : need) +
+                       static_cast<uint32_t>(__popcll(mk & lt));
+    if (kept && p < static_cast<uint32_t>(k)) out[p] = r * kRT + tid;
+  }
+  if (tid == 0 && count) count[row] = k;
+}
+
 int nch_for(int max_len) { return max_len > 0 ? (max_len + kChunk - 1) / kChunk : 1; }
 
 }  // namespace
@@ -696,12 +864,28 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
             static_cast<uint32_t>(rows));
   hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kFT), 0, s, scores,
                      stride, row_lens, cap, k, nch, passes, ws);
-  const int rb = blind_rounds(nch);
+  const BlindPlan bp = blind_plan(nch, k, max_len);
+  const int rb = bp.rounds;
   auto resolve = rb == 0 ? topk_resolve_kernel<0> : rb <= 2 ? topk_resolve_kernel<2>
                : rb <= 4 ? topk_resolve_kernel<4> : rb <= 8 ? topk_resolve_kernel<8>
                : topk_resolve_kernel<16>;
   hipLaunchKernelGGL(resolve, dim3(static_cast<uint32_t>(rows)), dim3(kRT), 0, s,
-                     scores, stride, row_lens, cap, k, nch, ws, idx, count);
+                     scores, stride, row_lens, cap, k, nch, bp.H, ws, idx, count);
+  return hipGetLastError();
+}
+
+bool topk_small_fits(int max_len) { return max_len <= kSmallMax; }
+
+hipError_t launch_topk_small(const float* scores, int64_t stride, int rows,
+                             const int32_t* row_lens, int max_len, int k,
+                             int32_t* idx, int32_t* count, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t cap = max_len < stride ? max_len : stride;
+  const int rpt = (max_len + kRT - 1) / kRT;
+  auto kern = rpt <= 4 ? topk_small_kernel<4> : rpt <= 8 ? topk_small_kernel<8>
+            : rpt <= 16 ? topk_small_kernel<16> : topk_small_kernel<32>;
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows)), dim3(kRT), 0, s,
+                     scores, stride, row_lens, cap, k, idx, count);
   return hipGetLastError();
 }
 
@@ -712,6 +896,9 @@ hipError_t launch_topk(const float* scores, int64_t stride, int rows,
   if (rows == 0) return hipSuccess;
   hipError_t e = zeroed ? hipSuccess : launch_topk_clear(ws, rows, s);
   if (e != hipSuccess) return e;
+  if (topk_small_fits(max_len))
+    return launch_topk_small(scores, stride, rows, row_lens, max_len, k, idx,
+                             count, s);
   e = launch_topk_hist1(scores, stride, rows, row_lens, max_len, k, ws, s);
   if (e != hipSuccess) return e;
   return launch_topk_finish(scores, stride, rows, row_lens, max_len, k, idx,

@@ -149,6 +149,14 @@ int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
   hipError_t e = hipSuccess;
   if (!(flags & TSD_TOPK_WS_ZEROED)) e = tsd::launch_topk_clear(ws, rows, stream);
   if (e != hipSuccess) return launch_status(e);
+  if (tsd::topk_small_fits(static_cast<int>(max_len))) {
+    e = a->mode == TSD_SCORE_QSA_INDEX ? tsd::launch_qsa_scan(*a, stream)
+                                       : tsd::launch_ds_scan(*a, stream);
+    if (e != hipSuccess) return launch_status(e);
+    return launch_status(tsd::launch_topk_small(
+        a->scores, a->score_stride, rows, a->row_lens_out,
+        static_cast<int>(max_len), k, idx, count, stream));
+  }
   if (a->mode == TSD_SCORE_QSA_INDEX && a->rows_per_req < 64) {
     e = tsd::launch_qsa_scan(*a, stream, ws, k);
   } else if (a->mode == TSD_SCORE_QSA_INDEX) {  // prefill rows: tiled kernel

@@ -84,7 +84,7 @@ WORKLOADS = {
         n_outlier=16, outlier_scale=6.0, steps=200),
     "ds_llama31_8b_b3_l60000": Config(
         "ds_llama31_8b_b3_l60000", "ds", B=3, L=60000, H_q=32, H_kv=8, D=128,
-        top_k=3000, chunks=12, kv_enc="bf16", seed=3, r=32, n_outlier=32,
+        top_k=3000, chunks=24, kv_enc="bf16", seed=3, r=32, n_outlier=32,
         outlier_scale=6.0),
     "qsa_decode_b8_l262144_k2048": Config(
         "qsa_decode_b8_l262144_k2048", "qsa", B=8, L=262144, H_q=32, H_kv=4,
