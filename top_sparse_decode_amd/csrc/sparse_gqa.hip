@@ -19,8 +19,10 @@
 //      16-bit type, so the products are exact and accumulate in FP32;
 //   4. an online softmax (base 2) per head updates the running max and sum;
 //      the page's V scale is folded into the probabilities;
-//   5. O += P V on v_mfma_f32_16x16x4_f32 (FP32 operands, no rounding of P),
-//      each wave owning 32 output dimensions of every head.
+//   5. O += P V on MFMA, each wave owning 32 output dimensions of every
+//      head: for 16-bit caches on v_mfma_f32_16x16x32_{bf16,f16} with P as
+//      the sum of two 16-bit parts (within 2^-17 of P) and V as stored; for
+//      FP8 caches with P rounded once to bf16 and V widened exactly.
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,10 +43,20 @@ struct Tile {
   static constexpr int kTokens = ENC == TSD_FP8_E4M3 ? 128 : 64;
   static constexpr int kRowBytes = kD * kEsz;
   static constexpr int kPitch = kRowBytes + 16;      // LDS row pitch (bytes)
+  // V rows: the P.V step reads, per lane group, 8 consecutive rows of one
+  // column range, the groups 8 rows apart. 32 more bytes after every 8 rows
+  // keep the groups off each other's banks (8 rows of a 16-byte aligned
+  // pitch span a multiple of 32 banks). 16-bit rows are 288 bytes apart, 8
+  // banks mod 32, so the 4 rows one 16-lane transpose load touches lie in
+  // disjoint banks.
+  static constexpr int kVPitch = ENC == TSD_FP8_E4M3 ? kPitch : kRowBytes + 32;
+  static constexpr int kVPad = 32;
+  static constexpr int kVBytes = kTokens * kVPitch + (kTokens / 8) * kVPad;
+  static constexpr __host__ __device__ int vrow(int t) { return t * kVPitch + (t >> 3) * kVPad; }
   static constexpr int kBlocks = kTokens / 16 / 4;   // 16-token blocks per wave
-  // logits / probs pitch (floats): 16-byte aligned rows for the FP8 path's
-  // 8-wide P reads
-  static constexpr int kZPitch = ENC == TSD_FP8_E4M3 ? kTokens + 4 : kTokens + 1;
+  // logits / probs pitch (floats): 16-byte aligned rows for the 8-wide P
+  // reads of the P.V step
+  static constexpr int kZPitch = kTokens + 4;
 };
 
 // 8 consecutive 16-bit values (as raw bits) starting at element `e0` of a
@@ -75,6 +87,16 @@ TSD_DEVICE uint4 k8_as_q(const uint8_t* row, int e0) {
   }
 }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// gfx950 LDS transpose load of 16-bit elements (ds_read_b64_tr_b16): within
+// each 16-lane group, lane i receives element i % 4 of the 8-byte segments
+// that lanes 4m + i / 4 point at, for m = 0 .. 3.
+TSD_DEVICE v4s lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(p));
+}
+
 template <bool QBF>
 TSD_DEVICE v4f mfma_qk(uint4 a, uint4 b, v4f c) {
   if constexpr (QBF) {
@@ -83,16 +105,6 @@ TSD_DEVICE v4f mfma_qk(uint4 a, uint4 b, v4f c) {
   } else {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(
         __builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
-  }
-}
-
-template <int ENC>
-TSD_DEVICE float v_elem(const uint8_t* row, int d) {
-  if constexpr (ENC == TSD_FP8_E4M3) {
-    return fp8x2_to_f32<false>(static_cast<uint32_t>(row[d])).x;
-  } else {
-    const uint16_t h = reinterpret_cast<const uint16_t*>(row)[d];
-    return half_to_f32(h, ENC == TSD_BF16);
   }
 }
 
@@ -110,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
   constexpr int NT = T::kTokens;
   constexpr bool fp8 = ENC == TSD_FP8_E4M3;
   __shared__ __align__(16) uint8_t k_s[NT * T::kPitch];
-  __shared__ __align__(16) uint8_t v_s[NT * T::kPitch];
+  __shared__ __align__(16) uint8_t v_s[T::kVBytes];
   __shared__ float zp_s[16 * T::kZPitch];  // logits, then probabilities
   __shared__ int64_t slot_s[NT];
   __shared__ float ks_s[NT], vs_s[NT];
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       const int i = tid + it * kThreads;
       const int j = i / vpr, v = i % vpr;
       *reinterpret_cast<uint4*>(k_s + j * T::kPitch + 16 * v) = kx[it];
-      *reinterpret_cast<uint4*>(v_s + j * T::kPitch + 16 * v) = vx[it];
+      *reinterpret_cast<uint4*>(v_s + T::vrow(j) + 16 * v) = vx[it];
     }
     __syncthreads();
     // 3. logits on MFMA: wave owns tokens [16*kBlocks*wave, +16*kBlocks)
@@ -300,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const uint8_t* vc = v_s + t0 * T::kPitch + 32 * wave + 16 * j + col;
+          const uint8_t* vc = v_s + T::vrow(t0) + 32 * wave + 16 * j + col;
           uint32_t w[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -322,15 +334,59 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         }
       }
     } else {
-#pragma unroll 4
-      for (int st = 0; st < NT / 4; ++st) {
-        const int t = 4 * st + grp;
-        const float pa = arow ? zp_s[col * T::kZPitch + t] : 0.f;
-        const uint8_t* vrow = v_s + t * T::kPitch;
-        const float b0 = v_elem<ENC>(vrow, 32 * wave + col);
-        const float b1 = v_elem<ENC>(vrow, 32 * wave + 16 + col);
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b0, acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, b1, acc[1], 0, 0, 0);
+      // MFMA of the cache's 16-bit type, 32 tokens per instruction: A = P
+      // as the sum of two 16-bit parts (hi = P rounded, lo = the remainder
+      // rounded; their sum is within 2^-17 of P relative for bf16, 2^-21
+      // for fp16, plus 2^-25 absolute for fp16 subnormals), B = the V rows
+      // as stored (tokens x dims); lane group grp supplies tokens
+      // 8*grp .. 8*grp+7
+#pragma unroll
+      for (int ks = 0; ks < NT / 32; ++ks) {
+        const int t0 = 32 * ks + 8 * grp;
+        uint4 ph = make_uint4(0u, 0u, 0u, 0u), pl = make_uint4(0u, 0u, 0u, 0u);
+        if (arow) {
+          const float4 p0 = *reinterpret_cast<const float4*>(zp_s + col * T::kZPitch + t0);
+          const float4 p1 = *reinterpret_cast<const float4*>(zp_s + col * T::kZPitch + t0 + 4);
+          const float pf[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t h2[2], l2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float x = pf[2 * i + e];
+              if constexpr (QBF) {
+                const __bf16 hb = static_cast<__bf16>(x);
+                const __bf16 lb = static_cast<__bf16>(x - static_cast<float>(hb));
+                h2[e] = __builtin_bit_cast(uint16_t, hb);
+                l2[e] = __builtin_bit_cast(uint16_t, lb);
+              } else {
+                const _Float16 hh = static_cast<_Float16>(x);
+                const _Float16 lh = static_cast<_Float16>(x - static_cast<float>(hh));
+                h2[e] = __builtin_bit_cast(uint16_t, hh);
+                l2[e] = __builtin_bit_cast(uint16_t, lh);
+              }
+            }
+            hw[i] = h2[0] | (h2[1] << 16);
+            lw[i] = l2[0] | (l2[1] << 16);
+          }
+          ph = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+          pl = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        }
+        // B by LDS transpose loads: lane L of a 16-lane group points at row
+        // t + L/4, columns d + 4*(L%4) .. +3, and receives column d + L of
+        // rows t .. t+3; two loads give tokens t0 .. t0+7 of one dimension
+        const int q = col;  // the lane's index in its group of 16
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint8_t* vb = v_s + 2 * (32 * wave + 16 * j + 4 * (q & 3));
+          const v4s lo = lds_read_tr16(vb + T::vrow(t0 + (q >> 2)));
+          const v4s hi = lds_read_tr16(vb + T::vrow(t0 + 4 + (q >> 2)));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          const uint4 bv = make_uint4(l2.x, l2.y, h2.x, h2.y);
+          acc[j] = mfma_qk<QBF>(ph, bv, acc[j]);
+          acc[j] = mfma_qk<QBF>(pl, bv, acc[j]);
+        }
       }
     }
     __syncthreads();
