@@ -12,7 +12,11 @@
 // the run's page ids in LDS, and streams the pages as 32 KB sub-blocks (8
 // 16-byte loads per thread), the next sub-block's loads in flight while the
 // current one is summed; the loads are unconditional (a page outside the
-// pool reads page 0 and scores -inf), so the compiler can count them. A
+// pool reads page 0 and scores -inf), so the compiler can count them, and
+// non-temporal (every label is read once). Where the launch would give one
+// page per workgroup anyway and the page splits into whole-token sub-blocks,
+// each workgroup takes one sub-block and keeps a single register buffer,
+// which raises the workgroups per CU from 5 to 8. A
 // label spans VPI = r/8 consecutive vectors, held by VPI consecutive lanes
 // whose partial dots are added by lane exchanges; when every lane always
 // meets the same head and channels (256/VPI a multiple of H_kv) its slice of
@@ -29,6 +33,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxHeadChan = 4096;  // H_kv * r held in LDS
 constexpr int kMaxScoreLds = 64 * 128;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
     const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
@@ -112,7 +117,10 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
 
 constexpr int kSubVec = kThreads * 8;  // 16-byte vectors per sub-block
 
-template <int VPI, bool QREG>
+// ONE: every workgroup streams a single unit, sub-block blockIdx.x % SB of
+// page blockIdx.x / SB (SB a power of two, so a unit holds 64 / SB whole
+// tokens), with no second register buffer, so more workgroups fit a CU.
+template <int VPI, bool QREG, bool ONE>
 __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
     const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
     const int32_t* __restrict__ chan, int r,
@@ -127,15 +135,19 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
   int32_t* pages_s = reinterpret_cast<int32_t*>(sc + 2 * kPage * H_kv);  // [P]
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
-  const int64_t pp0 = static_cast<int64_t>(blockIdx.x) * P;
+  const int VP = 8 * hc;                          // vectors per page
+  const int SB = (VP + kSubVec - 1) / kSubVec;    // sub-blocks per page
+  const int64_t pp0 = ONE ? blockIdx.x / SB : static_cast<int64_t>(blockIdx.x) * P;
+  const int sub0 = ONE ? static_cast<int>(blockIdx.x % SB) : 0;
+  const int tpu = kPage / SB;                     // ONE: tokens of the unit
   int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
   n = clamp_len(n, score_stride);
   if (blockIdx.x == 0 && row_lens_out)
     for (int g = tid; g < H_kv; g += kThreads)
       row_lens_out[static_cast<int64_t>(b) * H_kv + g] = static_cast<int32_t>(n);
-  if (pp0 * kPage >= n) return;  // uniform
+  if (pp0 * kPage + sub0 * tpu >= n) return;  // uniform
   const int64_t left = (n - pp0 * kPage + kPage - 1) / kPage;
-  const int npg = left < P ? static_cast<int>(left) : P;
+  const int npg = ONE ? 1 : (left < P ? static_cast<int>(left) : P);
   const int G = H_q / H_kv;
   for (int i = tid; i < hc; i += kThreads) {  // group query at the channels
     const int g = i / r;
@@ -153,13 +165,11 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
   }
   __syncthreads();
 
-  const int VP = 8 * hc;                          // vectors per page
-  const int SB = (VP + kSubVec - 1) / kSubVec;    // sub-blocks per page
-  const int units = npg * SB;
+  const int units = ONE ? 1 : npg * SB;
   const int part = tid % VPI;                     // this lane's label vector
   float qr[8];  // QREG: this lane's slice of qs (head (tid / VPI) % H_kv)
   auto load_unit = [&](int u, uint4 (&x)[8]) {
-    const int pg = u / SB, sub = u - pg * SB;
+    const int pg = ONE ? 0 : u / SB, sub = ONE ? sub0 : u - pg * SB;
     int32_t page = pages_s[pg];
     page = page < 0 ? 0 : page;                   // invalid: page 0, masked
     const uint4* base = reinterpret_cast<const uint4*>(label) +
@@ -168,11 +178,12 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
     for (int i = 0; i < 8; ++i) {
       int vv = sub * kSubVec + i * kThreads + tid;
       vv = vv < VP ? vv : VP - 1;
-      x[i] = base[vv];
+      const v4u t = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(base + vv));
+      x[i] = make_uint4(t.x, t.y, t.z, t.w);
     }
   };
   auto sum_unit = [&](int u, const uint4 (&x)[8]) {
-    const int pg = u / SB, sub = u - pg * SB;
+    const int pg = ONE ? 0 : u / SB, sub = ONE ? sub0 : u - pg * SB;
     const bool ok = pages_s[pg] >= 0;
     float* scp = sc + (pg & 1) * kPage * H_kv;
 #pragma unroll
@@ -202,13 +213,24 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
         scp[g * kPage + item / H_kv] = ok ? acc : -__builtin_inff();
     }
   };
-  uint4 xa[8], xb[8];
+  uint4 xa[8];
   load_unit(0, xa);
   if constexpr (QREG) {  // this lane always meets head (tid / VPI) % H_kv
     const int g = (tid / VPI) % H_kv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) qr[e] = qs[g * r + part * 8 + e];
   }
+  if constexpr (ONE) {
+    sum_unit(0, xa);
+    __syncthreads();
+    for (int it = tid; it < tpu * H_kv; it += kThreads) {
+      const int g = it / tpu, sl = sub0 * tpu + it % tpu;
+      const int64_t t = pp0 * kPage + sl;
+      if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = sc[g * kPage + sl];
+    }
+    return;
+  } else {
+  uint4 xb[8];
   for (int u = 0; u < units; u += 2) {
     if (u + 1 < units) load_unit(u + 1, xb);
     sum_unit(u, xa);
@@ -229,29 +251,40 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
       __syncthreads();  // the buffer is written again two pages later
     }
   }
+  }
 }
 
+template <int VPI, bool QREG, bool ONE>
+void launch_vec3(const tsd_score_args& a, dim3 grid, size_t lds, int P, hipStream_t s) {
+  hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, QREG, ONE>), grid, dim3(kThreads), lds, s,
+                     static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
+                     a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
+                     a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
+                     a.score_stride, a.row_lens_out, P);
+}
+
+// Runs of P pages per workgroup, P for about 1,536 workgroups or more; where
+// that is one page per workgroup and the page's sub-blocks split its tokens
+// evenly, one sub-block per workgroup instead.
 template <int VPI>
 bool launch_vec(const tsd_score_args& a, hipStream_t s) {
   const int hc = a.H_kv * a.r;
   const int64_t total_pages = a.pt_stride * a.B;
-  int P = static_cast<int>(total_pages / 1536);  // about 1,536 workgroups or more
+  int P = static_cast<int>(total_pages / 1536);
   P = P < 1 ? 1 : (P > 64 ? 64 : P);
+  const int SB = (8 * hc + kSubVec - 1) / kSubVec;
+  // a unit then holds 64 / SB whole tokens: the page is one sub-block, or a
+  // power-of-two number of full ones
+  const bool one = P == 1 && (SB == 1 || ((8 * hc) % kSubVec == 0 &&
+                                          (SB & (SB - 1)) == 0 && SB <= kPage));
   const size_t lds = static_cast<size_t>(hc + 2 * kPage * a.H_kv + P) * 4;
-  dim3 grid(static_cast<uint32_t>((a.pt_stride + P - 1) / P), static_cast<uint32_t>(a.B));
+  dim3 grid(static_cast<uint32_t>(one ? a.pt_stride * SB : (a.pt_stride + P - 1) / P),
+            static_cast<uint32_t>(a.B));
   const bool qreg = (kThreads / VPI) % a.H_kv == 0;
-  if (qreg)
-    hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, true>), grid, dim3(kThreads), lds, s,
-                       static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
-                       a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
-                       a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
-                       a.score_stride, a.row_lens_out, P);
-  else
-    hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, false>), grid, dim3(kThreads), lds, s,
-                       static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
-                       a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
-                       a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
-                       a.score_stride, a.row_lens_out, P);
+  if (qreg && one) launch_vec3<VPI, true, true>(a, grid, lds, P, s);
+  else if (qreg) launch_vec3<VPI, true, false>(a, grid, lds, P, s);
+  else if (one) launch_vec3<VPI, false, true>(a, grid, lds, P, s);
+  else launch_vec3<VPI, false, false>(a, grid, lds, P, s);
   return true;
 }
 
