@@ -7,7 +7,7 @@
 // 10 bits; all counts are integer atomics, so the result is deterministic.
 //   pass 1 (per 4096-element chunk, or inside the index scan): histogram of
 //          digit 1 -> H1[row].
-//   pass 2 (4 chunks per workgroup pass): the threshold digit b1 (the bin
+//   pass 2 (2 or 4 chunks per workgroup pass): the threshold digit b1 (the bin
 //          holding the k-th largest) is resolved from H1; every key whose
 //          digit 1 is >= b1 (above it:
 //          certainly kept; equal: a candidate) is compacted in index order
@@ -112,8 +112,11 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
 
 // Pass 2: survivors (digit 1 >= b1) compacted in index order into each
 // chunk's list; digit-2 histogram of the candidates (digit 1 == b1).
-// A workgroup of 16 waves takes 4 consecutive chunks per pass (4 waves per
-// chunk, 1,024 elements per wave) and `passes` consecutive passes. It
+// A workgroup of 16 waves takes FC consecutive chunks per pass (16/FC
+// waves per chunk) and `passes` consecutive passes: FC = 2 while the
+// launch stays within about 1,024 workgroups (twice the workgroups of
+// FC = 4, 1.6 us faster on 8 rows of 262,144), else FC = 4 (fewer, longer
+// passes: 0.3 ms faster on 2,048 rows of a million). It
 // resolves b1 itself from the row's H1 (one uint4 run of 4 bins per thread,
 // read while its first scores are in flight); the row's first workgroup
 // records (b1, above) for pass 3. Survivors are counted by ballots, the
@@ -121,11 +124,8 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
 // slot in the chunk's list.
 constexpr int kFT = 1024;                        // filter threads
 constexpr int kFW = kFT / kWave;                 // 16 waves
-constexpr int kFChunks = 4;                      // chunks per pass
-constexpr int kFWavesPerChunk = kFW / kFChunks;  // 4
-constexpr int kFSub = kChunk / kFWavesPerChunk;  // elements per wave
-constexpr int kFPer = kFSub / kWave;             // elements per lane
 
+template <int FC>
 __global__ __launch_bounds__(kFT) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
@@ -136,6 +136,10 @@ __global__ __launch_bounds__(kFT) void topk_filter_kernel(
   __shared__ BinPick pick;
   const int row = blockIdx.y;
   const int64_t n = clamp_len(row_lens[row], cap);
+  constexpr int kFChunks = FC;                     // chunks per pass
+  constexpr int kFWavesPerChunk = kFW / kFChunks;
+  constexpr int kFSub = kChunk / kFWavesPerChunk;  // elements per wave
+  constexpr int kFPer = kFSub / kWave;             // elements per lane
   constexpr int64_t kSpan = static_cast<int64_t>(kFChunks) * kChunk;
   const int64_t start = static_cast<int64_t>(blockIdx.x) * passes * kSpan;
   if (n <= k || start >= n) return;
@@ -843,10 +847,11 @@ hipError_t launch_topk_hist1(const float* scores, int64_t stride, int rows,
   return hipGetLastError();
 }
 
-// Filter passes per workgroup: one, unless the launch would exceed about
-// 1,024 workgroups, in which case a workgroup takes consecutive passes.
-int filter_passes(int nch, int rows) {
-  const int64_t per_row = (nch + kFChunks - 1) / kFChunks;
+// Filter passes per workgroup for FC chunks per pass: one, unless the
+// launch would exceed about 1,024 workgroups, in which case a workgroup
+// takes consecutive passes.
+int filter_passes(int nch, int rows, int fc) {
+  const int64_t per_row = (nch + fc - 1) / fc;
   int passes = 1;
   while (per_row * rows / passes > 1024 && passes < per_row) passes *= 2;
   return passes;
@@ -857,13 +862,15 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s) {
   const int nch = nch_for(max_len);
-  const int passes = filter_passes(nch, rows);
+  const int fc = filter_passes(nch, rows, 2) == 1 ? 2 : 4;
+  const int passes = filter_passes(nch, rows, fc);
   const int64_t cap = max_len < stride ? max_len : stride;
-  const int64_t per_row = (nch + kFChunks - 1) / kFChunks;
+  const int64_t per_row = (nch + fc - 1) / fc;
   dim3 grid(static_cast<uint32_t>((per_row + passes - 1) / passes),
             static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(topk_filter_kernel, grid, dim3(kFT), 0, s, scores,
-                     stride, row_lens, cap, k, nch, passes, ws);
+  hipLaunchKernelGGL(fc == 2 ? topk_filter_kernel<2> : topk_filter_kernel<4>, grid,
+                     dim3(kFT), 0, s, scores, stride, row_lens, cap, k, nch,
+                     passes, ws);
   const BlindPlan bp = blind_plan(nch, k, max_len);
   const int rb = bp.rounds;
   auto resolve = rb == 0 ? topk_resolve_kernel<0> : rb <= 2 ? topk_resolve_kernel<2>
