@@ -216,6 +216,34 @@ def test_ds_decode_path(name, over):
     _full_check(cfg)
 
 
+@pytest.mark.parametrize("H_q,H_kv,r,lens", [
+    (32, 32, 32, (3000, 77)),    # H_kv*r = 1,024: 4 sub-blocks of a page, one per workgroup
+    (48, 24, 32, (2000, 129)),   # 768: 3 sub-blocks, runs of pages, two register buffers
+    (32, 8, 32, (200000,)),      # 3,125 pages: two pages per workgroup
+])
+def test_ds_label_scan_vector_layouts(H_q, H_kv, r, lens):
+    """The label scan's vector layouts beyond the workloads' (one sub-block
+    per workgroup at four sub-blocks per page, page runs with three, runs of
+    two pages on a long row), every score against the oracle."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(DS8B, B=len(lens), H_q=H_q, H_kv=H_kv, r=r,
+                           n_outlier=r, lens=lens, top_k=64, chunks=2,
+                           seed=117 + H_kv)
+    wl = tsd_synth.make(cfg, DEV)
+    h = tsd_synth.to_host(wl)
+    ref = oracle_scores(h)
+    stride = wl["page_table"].shape[1] * 64
+    S = torch.full((cfg.B * H_kv, stride), float("nan"), device=DEV)
+    rl = torch.empty(cfg.B * H_kv, dtype=torch.int32, device=DEV)
+    tsd.sparse_index_score("ds", S, wl["page_table"], wl["seq_lens"], wl["num_pages"],
+                           q=wl["q"], channel_idx=wl["channel_idx"],
+                           label_pool=wl["label_pool"], row_lens_out=rl)
+    torch.cuda.synchronize()
+    want = np.repeat(np.array(lens), H_kv)
+    np.testing.assert_array_equal(rl.cpu().numpy(), want)
+    check_scores(S.cpu().numpy(), ref, want, score_tol("ds"))
+
+
 def test_ds_stale_tail_and_empty_request():
     cfg = tsd_synth.config(DS8B, B=3, lens=(0, 1000, 65), top_k=128, chunks=3,
                            stale_tail=True, seed=112)
