@@ -404,7 +404,8 @@ def test_topk_special_rows_bit_exact(stride):
 
 @pytest.mark.parametrize("max_len,k", [(300, 1), (4096, 256), (4097, 4096),
                                        (8192, 2048), (8193, 300), (16385, 1024),
-                                       (20224, 1024), (32768, 4096), (32769, 1),
+                                       (16384, 2048), (20224, 1024), (23000, 512),
+                                       (28000, 3000), (32768, 4096), (32769, 1),
                                        (60032, 3000)])
 def test_topk_one_workgroup_rows(max_len, k):
     """Rows of at most 32,768 entries (the whole row in one workgroup's

@@ -888,9 +888,21 @@ hipError_t launch_topk_small(const float* scores, int64_t stride, int rows,
                              int32_t* idx, int32_t* count, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t cap = max_len < stride ? max_len : stride;
+  // rounds of 1,024 rounded up to a multiple of 4: a round past every row
+  // still costs its load and its counting ballots
   const int rpt = (max_len + kRT - 1) / kRT;
-  auto kern = rpt <= 4 ? topk_small_kernel<4> : rpt <= 8 ? topk_small_kernel<8>
-            : rpt <= 16 ? topk_small_kernel<16> : topk_small_kernel<32>;
+  decltype(&topk_small_kernel<4>) kern;
+  switch ((rpt + 3) / 4) {
+    case 0:
+    case 1: kern = topk_small_kernel<4>; break;
+    case 2: kern = topk_small_kernel<8>; break;
+    case 3: kern = topk_small_kernel<12>; break;
+    case 4: kern = topk_small_kernel<16>; break;
+    case 5: kern = topk_small_kernel<20>; break;
+    case 6: kern = topk_small_kernel<24>; break;
+    case 7: kern = topk_small_kernel<28>; break;
+    default: kern = topk_small_kernel<32>; break;
+  }
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(rows)), dim3(kRT), 0, s,
                      scores, stride, row_lens, cap, k, idx, count);
   return hipGetLastError();
