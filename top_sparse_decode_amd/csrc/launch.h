@@ -28,9 +28,10 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               const int32_t* row_lens, int max_len, int k,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s);
-// Rows of at most 32,768 elements: the whole selection in one launch, one
+// Rows of at most 32,768 elements (24,576 unless there are many rows or k
+// is a large share of a row): the whole selection in one launch, one
 // workgroup per row (no workspace).
-bool topk_small_fits(int max_len);
+bool topk_small_fits(int max_len, int rows, int k);
 hipError_t launch_topk_small(const float* scores, int64_t stride, int rows,
                              const int32_t* row_lens, int max_len, int k,
                              int32_t* idx, int32_t* count, hipStream_t s);

@@ -881,7 +881,15 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
   return hipGetLastError();
 }
 
-bool topk_small_fits(int max_len) { return max_len <= kSmallMax; }
+// The one-workgroup path where it measured faster than the chunked one:
+// rows of up to 24,576 entries; up to 32,768 with at least 64 rows (the
+// chunked path's grid is then large) or when a chunk of 4,096 would keep
+// about 400 entries or more (its 512-entry lists would overflow).
+bool topk_small_fits(int max_len, int rows, int k) {
+  if (max_len > kSmallMax) return false;
+  if (max_len <= 24 * kRT) return true;
+  return rows >= 64 || static_cast<int64_t>(k) * kChunk >= 400ll * max_len;
+}
 
 hipError_t launch_topk_small(const float* scores, int64_t stride, int rows,
                              const int32_t* row_lens, int max_len, int k,
@@ -915,7 +923,7 @@ hipError_t launch_topk(const float* scores, int64_t stride, int rows,
   if (rows == 0) return hipSuccess;
   hipError_t e = zeroed ? hipSuccess : launch_topk_clear(ws, rows, s);
   if (e != hipSuccess) return e;
-  if (topk_small_fits(max_len))
+  if (topk_small_fits(max_len, rows, k))
     return launch_topk_small(scores, stride, rows, row_lens, max_len, k, idx,
                              count, s);
   e = launch_topk_hist1(scores, stride, rows, row_lens, max_len, k, ws, s);

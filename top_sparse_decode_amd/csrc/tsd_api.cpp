@@ -149,7 +149,7 @@ int sparse_index_topk(const tsd_score_args* a, int k, int32_t* idx,
   hipError_t e = hipSuccess;
   if (!(flags & TSD_TOPK_WS_ZEROED)) e = tsd::launch_topk_clear(ws, rows, stream);
   if (e != hipSuccess) return launch_status(e);
-  if (tsd::topk_small_fits(static_cast<int>(max_len))) {
+  if (tsd::topk_small_fits(static_cast<int>(max_len), rows, k)) {
     e = a->mode == TSD_SCORE_QSA_INDEX ? tsd::launch_qsa_scan(*a, stream)
                                        : tsd::launch_ds_scan(*a, stream);
     if (e != hipSuccess) return launch_status(e);
