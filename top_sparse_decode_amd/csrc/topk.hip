@@ -25,6 +25,10 @@
 // A chunk whose survivors overflow its list is read raw by pass 3 (the same
 // entries, recomputed from the scores), so the result never depends on the
 // list capacity. Rows with n <= k keep every index.
+// Short rows (at most 32,768 entries; see topk_small_fits) take a single
+// launch instead: one workgroup per row holds the whole row in registers and
+// runs the same three digits and the same ordered placement on chip, with no
+// workspace.
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
