@@ -971,6 +971,12 @@ def test_graph_replay_matches_eager():
     (DS8B, dict(B=2, lens=(3000, 700), top_k=200, chunks=3)),
     (DS7B, dict(B=2, H_q=8, H_kv=8, lens=(1500, 65), top_k=100, chunks=4,
                 steps=0)),
+    # rows past the one-workgroup top-k (label scan, digit-1 histogram,
+    # filter, resolve), with one, two and three sub-blocks per page
+    (DS8B, dict(B=3, lens=(40000, 27000, 300), top_k=1000, chunks=4)),
+    (DS8B, dict(B=2, lens=(30000, 12345), r=64, n_outlier=40, top_k=500,
+                chunks=4)),
+    (DS8B, dict(B=1, H_q=48, H_kv=24, lens=(40000,), top_k=700, chunks=4)),
 ])
 def test_fused_score_select_matches_separate_calls(name, over):
     step = _step()
@@ -987,6 +993,7 @@ def test_fused_score_select_matches_separate_calls(name, over):
         assert torch.equal(x, y)
     assert torch.equal(torch.nan_to_num(a.scores, nan=-7.0),
                        torch.nan_to_num(b.scores, nan=-7.0))
+    assert not _hist_words(b.ws, b.rows).any(), "histograms left nonzero"
 
 
 def _prefill_case(lens, R, seed, stale_tail=False):
