@@ -313,14 +313,15 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
             "block_selection_step_us": us_chain}
 
 
-def ds_decode(dev, name, steps, warmup):
-    """One double-sparsity decode step (label scan + exact top-k through
-    sparse_index_topk, per-KV-head sparse attention, LSE merge) on workload
-    ``name``: K eager steps over label-pool replicas (about 1 GB of labels
-    between two visits of a replica, so the Infinity Cache cannot serve the
-    scan; K/V pools are shared, their gather being a small random read),
-    then each of the four calls alone over back-to-back launches with HIP
-    events. Roofline: label bytes of every cached token per scan launch."""
+def decode_leg(dev, name, steps, warmup):
+    """One decode step (index or label scan + exact top-k through
+    sparse_index_topk, sparse attention, LSE merge) on workload ``name``: K
+    eager steps over replicas of the scanned pool (label pool for double
+    sparsity, index-K for QSA; about 1 GB between two visits of a replica,
+    so the Infinity Cache cannot serve the scan; K/V pools are shared, their
+    gather being a small random read), then each of the four calls alone
+    over back-to-back launches with HIP events. Roofline: the scanned key
+    bytes of every cached token per scan launch."""
     import torch
 
     import tsd_synth
@@ -329,8 +330,8 @@ def ds_decode(dev, name, steps, warmup):
     index_b, gather_b = model_bytes(cfg)
     R = max(1, math.ceil(1e9 / index_b))
     wl = tsd_synth.make(cfg, dev)
-    layers = [wl] + [dict(wl, label_pool=wl["label_pool"].clone())
-                     for _ in range(R - 1)]
+    pool = "label_pool" if cfg.mode == "ds" else "index_k"
+    layers = [wl] + [dict(wl, **{pool: wl[pool].clone()}) for _ in range(R - 1)]
     bufs = step.StepBuffers(wl)
     plans = [step.Plan(layer, bufs, fused=True) for layer in layers]
     plans_sep = [step.Plan(layer, bufs, fused=False) for layer in layers]
@@ -362,17 +363,21 @@ def ds_decode(dev, name, steps, warmup):
     scan_gbps = index_b / (scan_us * 1e-6) / 1e9
     del layers, plans, plans_sep, bufs, wl
     torch.cuda.empty_cache()
-    return {"workload": name, "batch": cfg.B, "context": cfg.L,
-            "heavy_channels": cfg.r, "H_q": cfg.H_q, "H_kv": cfg.H_kv,
-            "top_k": cfg.top_k, "chunks": cfg.chunks, "kv_cache": cfg.kv_enc,
-            "steps_per_s": 1.0 / step_s, "ms_per_step": step_s * 1e3,
-            "model_bytes_per_step": index_b + gather_b,
-            "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
-            "label_scan_us": scan_us, "kernel_us": us,
-            "roofline": {"bound": "hbm", "kernel": "sparse_index_score (label scan)",
-                         "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
-                         "bytes_per_launch": index_b}}
+    out = {"workload": name, "batch": cfg.B, "context": cfg.L,
+           "H_q": cfg.H_q, "H_kv": cfg.H_kv, "top_k": cfg.top_k,
+           "chunks": cfg.chunks, "kv_cache": cfg.kv_enc, "replicas": R,
+           "steps_per_s": 1.0 / step_s, "ms_per_step": step_s * 1e3,
+           "model_bytes_per_step": index_b + gather_b,
+           "step_model_gbps": (index_b + gather_b) / step_s / 1e9,
+           "scan_us": scan_us, "kernel_us": us,
+           "roofline": {"bound": "hbm", "kernel": "sparse_index_score ("
+                        + ("label" if cfg.mode == "ds" else "index") + " scan)",
+                        "achieved": scan_gbps, "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": scan_gbps / HBM_PEAK_GBPS,
+                        "bytes_per_launch": index_b}}
+    if cfg.mode == "ds":
+        out["heavy_channels"] = cfg.r
+    return out
 
 
 def append_bench(dev, passes, warmup):
@@ -452,6 +457,8 @@ def main():
     ap.add_argument("--prefill-passes", type=int, default=5)
     ap.add_argument("--no-ds", action="store_true",
                     help="skip the double-sparsity decode measurements")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 1,048,576-token single-request decode step")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the block-compressed selection measurement")
     ap.add_argument("--no-sharded", action="store_true",
@@ -623,8 +630,10 @@ def main():
     if not args.no_sharded:
         line["sharded_topk"] = sharded_select(dev, 200, 20)
     line["kv_append"] = append_bench(dev, 500, 20)
+    if not args.no_long:
+        line["long_decode"] = decode_leg(dev, "qsa_decode_b1_l1048576_k2048", 500, 50)
     if not args.no_ds:
-        line["ds_decode"] = [ds_decode(dev, n, 500, 50) for n in
+        line["ds_decode"] = [decode_leg(dev, n, 500, 50) for n in
                              ("ds_llama31_8b_b3_l60000", "ds_llama7b_b3_l20000_s200")]
     if not args.no_blocks:
         line["block_compressed_select"] = block_select(dev, 200, 20)

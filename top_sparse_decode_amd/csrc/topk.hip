@@ -276,24 +276,25 @@ TSD_DEVICE void clean_row(const Ws& ws, int row) {
 }
 
 // Blind plan of the resolve for nch chunks per row: wave w takes chunks
-// [w*R, w*R + R) and reads the first 64*H list entries of each, R*H rounds
-// per lane. H is the smallest power of two whose 64*H entries hold three
-// times the survivors a chunk keeps on average (k of max_len, so about
-// 4096*k/max_len), at most the whole list (512 entries) and at most
-// kBlindRounds rounds in all; rounds = 0 when R alone exceeds kBlindRounds
-// (no blind path).
+// [w*R, w*R + R) and reads the first E list entries of each; entry p of the
+// wave's sequence (p = 64*q + lane in round q) is entry p % E of the wave's
+// chunk p / E, so the sequence stays in index order. E is the smallest power
+// of two from 16 that holds three times the survivors a chunk keeps on
+// average (about 4096*k/max_len), at most the whole list (512 entries) and
+// at most kBlindRounds rounds of 64 entries; rounds = 0 when even 16 entries
+// per chunk exceed that (no blind path).
 struct BlindPlan {
-  int rounds, H;
+  int rounds, logE;
 };
 BlindPlan blind_plan(int nch, int k, int max_len) {
   const int R = (nch + kRT / kWave - 1) / (kRT / kWave);
-  if (R > kBlindRounds) return {0, 1};
+  if (R * 16 > kBlindRounds * kWave) return {0, 4};
   const int64_t want = 3 * (static_cast<int64_t>(kChunk) * k / (max_len > 0 ? max_len : 1));
-  int H = 1;
-  while (H < kListCap / kWave && static_cast<int64_t>(kWave) * H < want &&
-         R * H * 2 <= kBlindRounds)
-    H *= 2;
-  return {R * H, H};
+  int logE = 4;
+  while ((1 << logE) < kListCap && (1 << logE) < want &&
+         R * (2 << logE) <= kBlindRounds * kWave)
+    ++logE;
+  return {(R * (1 << logE) + kWave - 1) / kWave, logE};
 }
 
 // RB: blind rounds compiled in (2, 4, 8 or 16, at least the blind plan's),
@@ -302,7 +303,7 @@ template <int RB>
 __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
-    int H, void* __restrict__ ws_base, int32_t* __restrict__ idx,
+    int logE, void* __restrict__ ws_base, int32_t* __restrict__ idx,
     int32_t* __restrict__ count) {
   __shared__ uint32_t off_s[kMaxChunks + 1];  // survivors before chunk c
   __shared__ __align__(16) uint32_t hist[kBins3];
@@ -317,13 +318,12 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   constexpr int kWavesR = kRT / kWave;
   const Ws ws = topk_ws(ws_base, gridDim.x, nch);
   // Blind reads, issued with the row length: wave w takes chunks
-  // [w*R, w*R + R) and reads the first 64*H entries of each chunk's list
-  // and, in lane j, the count of its j-th chunk. Entries past a chunk's
-  // count are ignored; when every live chunk holds at most 64*H survivors
-  // this is the whole survivor sequence, wave-contiguous, after a single
-  // round trip.
-  // Round q < R*H of a lane covers chunk wave*R + q/H, entry 64*(q%H) + lane
-  // (H from the launcher's blind plan).
+  // [w*R, w*R + R) and reads the first E entries of each chunk's list and,
+  // in lane j, the count of its j-th chunk. Entries past a chunk's count are
+  // ignored; when every live chunk holds at most E survivors this is the
+  // whole survivor sequence, wave-contiguous, after a single round trip.
+  // Round q of a lane covers entry p = 64*q + lane of the wave: entry p % E
+  // of its chunk p / E (E = 2^logE from the launcher's blind plan).
   // The row's records are loaded first and every blind read is
   // unconditional (a chunk index past nch reads the last chunk and is
   // masked at use), so the compiler can count the loads in flight and the
@@ -331,6 +331,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
   constexpr bool kBlind = RB > 0;
   constexpr int kRounds = kBlind ? RB : 1;
   const int R = (nch + kWavesR - 1) / kWavesR;
+  const int ents = 1 << logE;  // list entries read per chunk
   const uint32_t h2v = ws.h2[static_cast<int64_t>(row) * kBins2 + (kBins2 - 1 - tid)];
   const uint2 sel = ws.sel[row];  // digit-1 bin of the row, from pass 2
   const int64_t n = clamp_len(row_lens[row], cap);
@@ -340,10 +341,11 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     __builtin_amdgcn_sched_barrier(0);  // keep the records' loads first
 #pragma unroll
     for (int q = 0; q < RB; ++q) {
-      int c = wave * R + q / H;
+      const int p = q * kWave + lane;
+      int c = wave * R + (p >> logE);
       c = c < nch ? c : nch - 1;
       bl[q] = ws.lists[(static_cast<int64_t>(row) * nch + c) * kListCap +
-                       kWave * (q % H) + lane];
+                       (p & (ents - 1))];
     }
     int c = wave * R + lane;
     c = c < nch ? c : nch - 1;
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     p2b = pick_bin_runs<kBins2, kRT>(h2r, k - p1.above, lds, &pick);
     const int c = wave * R + lane;
     blind_ok = __ballot(lane < R && c < nc &&
-                        cntw > static_cast<uint32_t>(kWave * H)) == 0;
+                        cntw > static_cast<uint32_t>(ents)) == 0;
   }
   if (kBlind && __syncthreads_and(blind_ok)) {
     // ---- blind fast path ----
@@ -382,12 +384,14 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
     uint32_t okb = 0;
 #pragma unroll
     for (int q = 0; q < kRounds; ++q) {
-      const int j = q / H;  // the wave's chunk of this round
+      const int p = q * kWave + lane;
+      const int j = p >> logE;  // the wave's chunk of this entry (< 64)
       const int c = wave * R + j;
+      // its count sits in lane j: one lane for the whole round when ents >= 64
       const uint32_t cc = static_cast<uint32_t>(
-          __builtin_amdgcn_readlane(static_cast<int>(cntw), j));
-      const bool ok = q < R * H && c < nc &&
-                      static_cast<uint32_t>(kWave * (q % H) + lane) < cc;
+          ents >= kWave ? __builtin_amdgcn_readlane(static_cast<int>(cntw), (q * kWave) >> logE)
+                     : __shfl(static_cast<int>(cntw), j));
+      const bool ok = j < R && c < nc && static_cast<uint32_t>(p & (ents - 1)) < cc;
       okb |= static_cast<uint32_t>(ok) << q;
       if (ok && prefix12(bl[q].y) == pre)
         atomicAdd(&hist[bl[q].y & (kBins3 - 1)], 1u);
@@ -881,7 +885,7 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                : rb <= 4 ? topk_resolve_kernel<4> : rb <= 8 ? topk_resolve_kernel<8>
                : topk_resolve_kernel<16>;
   hipLaunchKernelGGL(resolve, dim3(static_cast<uint32_t>(rows)), dim3(kRT), 0, s,
-                     scores, stride, row_lens, cap, k, nch, bp.H, ws, idx, count);
+                     scores, stride, row_lens, cap, k, nch, bp.logE, ws, idx, count);
   return hipGetLastError();
 }
 
