@@ -211,8 +211,8 @@ int topk_select(const float *scores, int64_t stride, int rows,
  * skips its own histogram pass and one read of the scores (QSA_INDEX mode;
  * DS_LABEL runs the two steps back to back); rows of up to 32,768 entries
  * are selected, as by topk_select, in one launch that reads each row once
- * and uses the workspace only for its zeroing contract (see topk_select). The scores
- * are still written to a->scores.
+ * and uses the workspace only for its zeroing contract (see topk_select).
+ * The scores are still written to a->scores.
  *   a->row_lens_out  required: receives each row's key count
  *   rows             B * H_kv (DS) or B * rows_per_req (QSA)
  *   max_len          min(a->score_stride, a->pt_stride * 64)
