@@ -478,7 +478,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU: this build has no multi-GPU path "
+        print("bench.py runs on one GPU: this library has no multi-GPU path "
               "(sharding is described in the design notes); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)

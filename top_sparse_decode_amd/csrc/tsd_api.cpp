@@ -322,7 +322,7 @@ const char* tsd_strerror(int status) {
     case TSD_E_K: return "top_k must lie in [1, 4096]";
     case TSD_E_CHUNKS: return "chunks must lie in [1, 64]";
     case TSD_E_WORKSPACE: return "workspace missing or too small";
-    case TSD_E_UNSUPPORTED: return "configuration not supported by this build";
+    case TSD_E_UNSUPPORTED: return "configuration not supported by this library";
     case TSD_E_MODE: return "unknown score mode";
     case TSD_E_ABI: return "argument struct from another ABI version";
     default:
