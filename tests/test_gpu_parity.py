@@ -78,6 +78,8 @@ DS7B = "ds_llama7b_b3_l20000_s200"
     ((1000, 0, 130), 300, 3),
     ((64, 65, 128), 64, 1),
     ((2048, 700), 2048, 16),
+    # 32 rows of a 4,096-page table: 64 pages per scan wave
+    ((262144,) + tuple((i * 997) % 9000 for i in range(1, 32)), 256, 4),
 ])
 def test_qsa_decode_path(lens, k, C):
     cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=k, chunks=C,
@@ -968,6 +970,10 @@ def test_graph_replay_matches_eager():
     (QSA, dict(B=3, lens=(9000, 4097, 130), top_k=512, chunks=8)),
     (QSA, dict(B=2, lens=(700, 129), top_k=100, chunks=4, stale_tail=True)),
     (QSA, dict(B=2, lens=(2048, 50), top_k=2048, chunks=16)),
+    # 64 pages per scan wave (32 rows of a 4,096-page table)
+    (QSA, dict(B=32, lens=(262144,) + tuple((i * 997) % 9000
+                                             for i in range(1, 32)),
+               top_k=256, chunks=4)),
     (DS8B, dict(B=2, lens=(3000, 700), top_k=200, chunks=3)),
     (DS7B, dict(B=2, H_q=8, H_kv=8, lens=(1500, 65), top_k=100, chunks=4,
                 steps=0)),

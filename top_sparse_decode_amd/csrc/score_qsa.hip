@@ -11,7 +11,7 @@
 // single streaming pass over the index-K pages: every byte is read once, the
 // query rows sit in registers for the whole scan.
 //
-// Work split: one wave owns one query row and a run of up to 32 consecutive
+// Work split: one wave owns one query row and a run of up to 64 consecutive
 // 64-token pages; a page is 4 MFMA tiles of 16 keys. The 16x16 f32 result gives lane
 // l the dots of key (l % 16) with heads 4*(l/16) .. 4*(l/16)+3; the weighted
 // ReLU is applied per lane and a 3-shuffle reduce-scatter over the 4 lane
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     int rows_per_req, int H_i, int waves_per_row, float* __restrict__ scores,
     int64_t score_stride, int32_t* __restrict__ row_lens_out,
     void* __restrict__ topk_base, int hist_k) {
-  static_assert(G % 4 == 0, "pages per wave");
+  static_assert(G % 4 == 0 && G <= kWave, "pages per wave: one page id per lane");
   __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
   __shared__ float res_s[kWavesPerBlock][G * kPage];
   const int lane = threadIdx.x & (kWave - 1), wl = threadIdx.x >> 6;
@@ -474,9 +474,11 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                        a.row_lens_out);
     return hipGetLastError();
   }
-  // pages per wave: the most (up to 32) that still gives >= 1,024 waves
+  // pages per wave: 64 when that still gives >= 2,048 waves (two resident
+  // workgroups per CU, so the launch runs in a single pass), else the most
+  // (up to 32) that still gives >= 1,024 waves
   const int64_t pages = a.pt_stride * static_cast<int64_t>(rows);
-  int G = 32;
+  int G = pages / 64 >= 2048 ? 64 : 32;
   while (G > 4 && pages / G < 1024) G /= 2;
   int64_t waves_per_row = (a.pt_stride + G - 1) / G;
   if (topk_ws)  // whole workgroups per row
@@ -490,11 +492,15 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                         int64_t, int32_t*, void*, int);
   Kern kern;
   if (topk_ws)
-    kern = G == 32 ? qsa_scan_kernel<32, true> : G == 16 ? qsa_scan_kernel<16, true>
-         : G == 8 ? qsa_scan_kernel<8, true> : qsa_scan_kernel<4, true>;
+    kern = G == 64 ? qsa_scan_kernel<64, true>
+         : G == 32 ? qsa_scan_kernel<32, true>
+         : G == 16 ? qsa_scan_kernel<16, true>
+         : G == 8  ? qsa_scan_kernel<8, true> : qsa_scan_kernel<4, true>;
   else
-    kern = G == 32 ? qsa_scan_kernel<32, false> : G == 16 ? qsa_scan_kernel<16, false>
-         : G == 8 ? qsa_scan_kernel<8, false> : qsa_scan_kernel<4, false>;
+    kern = G == 64 ? qsa_scan_kernel<64, false>
+         : G == 32 ? qsa_scan_kernel<32, false>
+         : G == 16 ? qsa_scan_kernel<16, false>
+         : G == 8  ? qsa_scan_kernel<8, false> : qsa_scan_kernel<4, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)),
                      dim3(kWavesPerBlock * kWave), 0, s, a.index_q, a.index_w,
                      a.index_k_pool, a.page_table, a.pt_stride, a.seq_lens,
