@@ -103,6 +103,28 @@ def scan_traffic():
 FP8_MFMA_PEAK_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X
 
 
+def inputs_digest(wl):
+    """SHA-256 over one generated workload (every tensor's name, dtype,
+    shape and bytes, then the other fields' reprs, in key order), so that
+    runs can show they measured the same inputs. Tensors are copied to the
+    host in 256 MB slices."""
+    import hashlib
+    import torch
+    h = hashlib.sha256()
+    for key in sorted(wl):
+        v = wl[key]
+        h.update(key.encode())
+        if isinstance(v, torch.Tensor):
+            h.update(f"{v.dtype}{tuple(v.shape)}".encode())
+            flat = v.detach().contiguous().reshape(-1).view(torch.uint8)
+            step_b = 1 << 28
+            for i in range(0, flat.numel(), step_b):
+                h.update(flat[i:i + step_b].cpu().numpy().tobytes())
+        else:
+            h.update(repr(v).encode())
+    return h.hexdigest()
+
+
 def prefill_indexer(dev, passes, warmup):
     """Chunked-prefill indexer: 2,048 causal query rows x 16 heads x 128 FP8
     dims against 1,048,576 index keys (the tiled MFMA kernel), then per-row
@@ -621,6 +643,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "bytes_per_launch": index_b, "traffic": scan_traffic()},
     }
+    line["inputs_sha256"] = inputs_digest(layers[0])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
     if not args.no_prefill:
