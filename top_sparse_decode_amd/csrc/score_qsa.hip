@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
 // A workgroup of 8 waves owns 64 consecutive query rows of one request (8
 // per wave, their index heads held as MFMA A operands and their head weights
 // in registers, 2 waves per SIMD) and a span of 16,384 keys whose page ids it
-// keeps in LDS. The span is walked in blocks of 256 keys (4 pages) that the
+// keeps in LDS. The span is walked in blocks of 512 keys (8 pages) that the
 // workgroup gathers once into LDS, the next block's loads in flight during
 // the current one; every wave then takes each 16-key tile of the block as a
 // B operand and issues one MFMA per row, so each key byte read from memory
@@ -252,8 +252,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
 constexpr int kPfWaves = 8;
 constexpr int kPfRowsPerWave = 8;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // rows per workgroup
-constexpr int kPfBlockKeys = 256;                   // keys per LDS block
-constexpr int kPfSpanBlocks = 64;                   // blocks per workgroup
+constexpr int kPfBlockKeys = 512;                   // keys per LDS block
+constexpr int kPfSpanBlocks = 32;                   // blocks per workgroup
 constexpr int kPfSpan = kPfBlockKeys * kPfSpanBlocks;
 constexpr int kPfPitch = kDi + 16;                  // LDS bytes per key
 
@@ -266,7 +266,7 @@ TSD_DEVICE v8i lds_row_slice(const uint8_t* row, int kb) {
   return v;
 }
 
-// Gathers the 256 keys of block `key0` (4 pages) into registers: thread tid
+// Gathers the 512 keys of block `key0` (8 pages) into registers: thread tid
 // holds 16-byte vectors tid, tid + 512, ... of the block; keys at or past the
 // workgroup's longest row, or on an invalid page, read as zeros.
 constexpr int kPfThreads = kPfWaves * kWave;
