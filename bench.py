@@ -253,7 +253,9 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
     the step scores and selects kb blocks (kb * Bs tokens) and expands them.
     Times the full compression of every cached block (once per prompt), the
     per-step compression of each request's last block, the block score+select
-    and the expansion: n back-to-back calls captured in a HIP graph, one
+    and the expansion, then the attention over the expanded tokens against
+    the attention on the block indices (and both chains from compression to
+    attention): n back-to-back calls captured in a HIP graph, one
     replay timed with HIP events (device time, without the per-call host
     marshalling of the binding)."""
     import torch
@@ -320,11 +322,33 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
     us_sel = timed(select, passes)
     us_exp = timed(expand, passes)
     us_chain = timed(lambda: (compress_step(), select(), expand()), passes)
+    # the attention that consumes the selection: over the expanded tokens,
+    # or directly over the block indices (idx_block), which drops the
+    # expansion launch
+    C = cfg.chunks
+    o = torch.empty((B, cfg.H_q, C, 128), device=dev)
+    lse = torch.empty((B, cfg.H_q, C), device=dev)
+
+    def attend(ix, cn, blk):
+        tsd.sparse_gqa_decode(wl["q"], wl["k_pool"], wl["v_pool"],
+                              wl["page_table"], wl["seq_lens"],
+                              wl["num_pages"], ix, cn, C, o, lse,
+                              k_scale=wl["k_scale"], v_scale=wl["v_scale"],
+                              idx_block=blk)
+
+    tok3, tcnt2 = tok.view(B, 1, kb * Bs), tcnt.view(B, 1)
+    bidx3, bcnt2 = bidx.view(B, 1, kb), bcnt.view(B, 1)
+    us_att_tok = timed(lambda: attend(tok3, tcnt2, 0), passes)
+    us_att_blk = timed(lambda: attend(bidx3, bcnt2, Bs), passes)
+    us_step_tok = timed(lambda: (compress_step(), select(), expand(),
+                                 attend(tok3, tcnt2, 0)), passes)
+    us_step_blk = timed(lambda: (compress_step(), select(),
+                                 attend(bidx3, bcnt2, Bs)), passes)
     tokens = float(wl["seq_lens"].to(torch.int64).sum())
     blocks = float(nblk.to(torch.int64).sum())
     comp_bytes = tokens * 128 + blocks * 128   # raw keys read, block keys written
     scan_bytes = blocks * 128                  # compressed keys read per step
-    del wl, lay, S
+    del wl, lay, S, o, lse
     torch.cuda.empty_cache()
     return {"workload": cfg.name, "block_size": Bs, "top_k_blocks": kb,
             "top_k_tokens": kb * Bs, "blocks_per_request": max_blocks,
@@ -332,7 +356,11 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
             "compress_all_gbps": comp_bytes / (us_all * 1e-6) / 1e9,
             "compress_step_us": us_step, "block_select_us": us_sel,
             "block_scan_model_bytes": scan_bytes, "expand_us": us_exp,
-            "block_selection_step_us": us_chain}
+            "block_selection_step_us": us_chain,
+            "attention_expanded_us": us_att_tok,
+            "attention_on_blocks_us": us_att_blk,
+            "step_with_expansion_us": us_step_tok,
+            "step_on_blocks_us": us_step_blk}
 
 
 def decode_leg(dev, name, steps, warmup):

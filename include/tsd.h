@@ -277,6 +277,15 @@ int topk_merge_sharded(const float *scores, int64_t stride,
  * pt_stride * 64) is at most dense_len attends to every token 0 .. len-1 as
  * its selection (m = len; idx and count are not read for it). dense_len = 0
  * turns this off.
+ * Block selections (idx_block = Bs in {2, 4, ..., 64}; 0 or 1 = token
+ * indices): idx row holds the first count ascending indices of selected
+ * blocks of Bs tokens (block j = tokens [j*Bs, min((j+1)*Bs, len)), as
+ * index_k_compress builds them), k being the block capacity. The selection is
+ * then the blocks' tokens in order, position p being token
+ * idx[p / Bs] * Bs + p % Bs, and m = count * Bs less the tokens of the last
+ * block at or past len: the token list expand_blocks writes for such a
+ * selection, so the result equals attention over that list. An entry outside
+ * [0, ceil(len / Bs)) keeps its positions and its tokens are skipped.
  * For a 16-bit cache q must have the cache's encoding; an FP8 cache takes
  * bf16 or fp16 queries. H_q % H_kv == 0, G <= 16, 1 <= chunks <= 64,
  * 1 <= k <= 4096, dense_len >= 0.
@@ -308,7 +317,7 @@ typedef struct tsd_attn_args {
   float *o_part;
   float *lse_part;
   int32_t dense_len;             /* requests with len <= dense_len: dense    */
-  int32_t reserved0;
+  int32_t idx_block;             /* 0 or 1: token indices; else block size   */
 } tsd_attn_args;
 
 int sparse_gqa_decode(const tsd_attn_args *a, hipStream_t stream);

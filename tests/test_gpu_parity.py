@@ -726,6 +726,62 @@ def test_block_compressed_decode_path(Bs, lens, kb):
                        o.cpu().numpy(), lse.cpu().numpy(), out_tol(cfg.kv_enc))
 
 
+@pytest.mark.parametrize("name,Bs,lens,kb,C", [
+    (QSA, 4, (30000, 4097, 100, 6), 512, 7),
+    (QSA, 16, (65536, 2000, 17), 128, 16),
+    (QSA, 64, (5000, 64, 65), 16, 5),
+    (DS8B, 8, (9000, 1001), 200, 4),
+])
+def test_block_index_attention_equals_expanded_tokens(name, Bs, lens, kb, C):
+    """sparse_gqa_decode on block indices (idx_block = Bs) gives exactly the
+    result of expand_blocks followed by attention over those tokens: full
+    and short selections, with the partial last block selected or not, for
+    a shared (FP8) and a per-KV-head (BF16) selection."""
+    import top_sparse_decode_amd as tsd
+    cfg = tsd_synth.config(name, B=len(lens), lens=lens, top_k=kb * Bs,
+                           chunks=C, seed=230 + Bs)
+    wl = tsd_synth.make(cfg, DEV)
+    B = cfg.B
+    H_sel = 1 if cfg.mode == "qsa" else cfg.H_kv
+    g = torch.Generator().manual_seed(231)
+    sel = torch.full((B, H_sel, kb), -1, dtype=torch.int32)
+    cnt = torch.zeros((B, H_sel), dtype=torch.int32)
+    for b, n in enumerate(lens):
+        nb = (n + Bs - 1) // Bs
+        for hs in range(H_sel):
+            c = min(kb, nb) if (b + hs) % 3 else max(1, min(kb, nb) // 2)
+            pick = torch.randperm(nb, generator=g)[:c]
+            if (b + hs) % 2 == 0 and nb - 1 not in pick.tolist():
+                pick[0] = nb - 1  # the (possibly partial) last block
+            sel[b, hs, :c] = pick.sort().values.to(torch.int32)
+            cnt[b, hs] = c
+    sel_d, cnt_d = sel.to(DEV), cnt.to(DEV)
+    kt = kb * Bs
+    tok = torch.empty((B, H_sel, kt), dtype=torch.int32, device=DEV)
+    tcnt = torch.empty((B, H_sel), dtype=torch.int32, device=DEV)
+    tsd.expand_blocks(sel_d.view(B * H_sel, kb), cnt_d.view(-1), Bs,
+                      wl["seq_lens"].repeat_interleave(H_sel),
+                      tok.view(B * H_sel, kt), tcnt.view(-1))
+    outs = []
+    for ix, cn, blk in ((tok, tcnt, 0), (sel_d, cnt_d, Bs)):
+        o = torch.full((B, cfg.H_q, C, 128), float("nan"), device=DEV)
+        lse = torch.full((B, cfg.H_q, C), float("nan"), device=DEV)
+        tsd.sparse_gqa_decode(wl["q"], wl["k_pool"], wl["v_pool"],
+                              wl["page_table"], wl["seq_lens"],
+                              wl["num_pages"], ix, cn, C, o, lse,
+                              k_scale=wl.get("k_scale"),
+                              v_scale=wl.get("v_scale"), idx_block=blk)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0])
+    assert torch.equal(outs[0][1], outs[1][1])
+    # the expansion's token counts are the block selection's token lengths
+    nb_tok = [[int(cnt[b, hs]) * Bs
+               - max(0, (int(sel[b, hs, cnt[b, hs] - 1]) + 1) * Bs - lens[b])
+               for hs in range(H_sel)] for b in range(B)]
+    np.testing.assert_array_equal(tcnt.cpu().numpy(), np.array(nb_tok))
+
+
 # -------------------------------------------------- sparse-decode threshold
 @pytest.mark.parametrize("name,lens,dense_len", [
     ("ds_llama31_8b_b3_l60000", (300, 5000, 1000), 1000),

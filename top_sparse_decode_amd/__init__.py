@@ -54,7 +54,7 @@ class AttnArgs(ctypes.Structure):
         ("pt_stride", _I64), ("seq_lens", _P), ("num_pages", _I64),
         ("idx", _P), ("count", _P), ("H_sel", _I32), ("k", _I32),
         ("chunks", _I32), ("softmax_scale", _F32), ("o_part", _P),
-        ("lse_part", _P), ("dense_len", _I32), ("reserved0", _I32),
+        ("lse_part", _P), ("dense_len", _I32), ("idx_block", _I32),
     ]
 
 
@@ -315,9 +315,11 @@ def topk_merge_sharded(scores, idx_local, count_local, k, idx, count=None,
 def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
                       count, chunks, o_part, lse_part, k_scale=None,
                       v_scale=None, softmax_scale=None, dense_len=0,
-                      stream=None):
+                      idx_block=0, stream=None):
     """Chunked sparse GQA attention over the selection ``idx`` [B,H_sel,k]
-    into ``o_part`` [B,H_q,chunks,128] and ``lse_part`` [B,H_q,chunks]."""
+    into ``o_part`` [B,H_q,chunks,128] and ``lse_part`` [B,H_q,chunks].
+    ``idx_block`` > 1: ``idx`` holds ascending indices of selected blocks of
+    that many tokens (``count`` = blocks) instead of token indices."""
     _dev("q", q, dtypes=_HALF)
     _dev("k_pool", k_pool, dtypes=_HALF + _FP8)
     _dev("v_pool", v_pool, dtypes=_HALF + _FP8)
@@ -345,6 +347,7 @@ def sparse_gqa_decode(q, k_pool, v_pool, page_table, seq_lens, num_pages, idx,
                        else float(softmax_scale))
     a.o_part, a.lse_part = _ptr(o_part), _ptr(lse_part)
     a.dense_len = int(dense_len)
+    a.idx_block = int(idx_block)
     _check("sparse_gqa_decode", _lib.sparse_gqa_decode(ctypes.byref(a),
                                                        _stream(stream)))
 

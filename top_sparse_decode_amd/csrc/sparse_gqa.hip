@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     const int32_t* __restrict__ seq_lens, int64_t num_pages,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
     int H_sel, int k, int C, float softmax_scale, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int dense_len) {
+    float* __restrict__ lse_part, int dense_len, int lbs) {
   using T = Tile<ENC>;
   constexpr int NT = T::kTokens;
   constexpr bool fp8 = ENC == TSD_FP8_E4M3;
@@ -134,18 +134,37 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
   const int h0 = g * G;
   const int srow = H_sel == 1 ? 0 : g;
   const int32_t* sel = idx + (static_cast<int64_t>(b) * H_sel + srow) * k;
-  // The chunk bounds depend on the selection's length m, which is k for
-  // every row longer than k: the first tile's entries for m = k are loaded
-  // together with the count and kept wherever they match the real bounds.
+  // Entries are token indices (lbs = 0) or ascending indices of blocks of
+  // 2^lbs tokens, position p of the selection then being token
+  // sel[p >> lbs] * 2^lbs + p % 2^lbs (only a last block can be partial).
+  // The chunk bounds depend on the selection's length m, which is the full
+  // capacity for every row long enough: the first tile's entries for that m
+  // are loaded together with the count (and, for blocks, the last entry) and
+  // kept wherever they match the real bounds.
   const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
   // at or below the sparse-decode threshold the selection is every token
   const bool dense = n <= dense_len;
-  const int64_t lo_s = c * static_cast<int64_t>(k) / C;
-  const int64_t hi_s = (c + 1) * static_cast<int64_t>(k) / C;
-  int32_t t_spec = -1;
-  if (!dense && tid < NT && lo_s + tid < hi_s) t_spec = sel[lo_s + tid];
-  const int64_t m =
-      dense ? n : clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
+  const int bsz = 1 << lbs;
+  const int64_t cap = static_cast<int64_t>(k) << lbs;  // capacity in tokens
+  auto token_at = [&](int64_t p) -> int64_t {
+    if (lbs == 0) return sel[p];
+    return static_cast<int64_t>(sel[p >> lbs]) * bsz + (p & (bsz - 1));
+  };
+  const int64_t lo_s = c * cap / C;
+  const int64_t hi_s = (c + 1) * cap / C;
+  int64_t t_spec = -1;
+  if (!dense && tid < NT && lo_s + tid < hi_s) t_spec = token_at(lo_s + tid);
+  const int32_t last_spec = (lbs > 0 && !dense) ? sel[k - 1] : -1;
+  int64_t m = n;
+  if (!dense) {
+    const int64_t cnt = clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
+    m = cnt << lbs;
+    if (lbs > 0 && cnt > 0) {  // drop the part of the last block past len
+      const int32_t last = cnt == k ? last_spec : sel[cnt - 1];
+      const int64_t over = (static_cast<int64_t>(last) + 1) * bsz - n;
+      m -= over < 0 ? 0 : (over > bsz ? bsz : over);
+    }
+  }
   const int64_t lo = c * m / C, hi = (c + 1) * m / C;
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
   const float zscale = softmax_scale * kLog2e;
@@ -181,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       int64_t slot = -1;
       if (tid < tn) {
         const bool spec = !dense && base == lo_s && lo_s + tid < hi_s;
-        const int64_t t = dense ? base + tid : (spec ? t_spec : sel[base + tid]);
+        const int64_t t = dense ? base + tid : (spec ? t_spec : token_at(base + tid));
         if (t >= 0 && t < n) {
           const int32_t page = pt[t / kPage];
           if (page >= 0 && page < num_pages) {
@@ -421,7 +440,8 @@ hipError_t launch_enc(const tsd_attn_args& a, hipStream_t s) {
                      static_cast<const uint8_t*>(a.v_pool), a.k_scale,
                      a.v_scale, a.page_table, a.pt_stride, a.seq_lens,
                      a.num_pages, a.idx, a.count, a.H_sel, a.k, a.chunks,
-                     a.softmax_scale, a.o_part, a.lse_part, a.dense_len);
+                     a.softmax_scale, a.o_part, a.lse_part, a.dense_len,
+                     a.idx_block > 1 ? __builtin_ctz(static_cast<unsigned>(a.idx_block)) : 0);
   return hipGetLastError();
 }
 

@@ -90,6 +90,9 @@ int validate_attn(const tsd_attn_args* a) {
   if (a->k < 1 || a->k > TSD_MAX_TOPK) return TSD_E_K;
   if (a->chunks < 1 || a->chunks > TSD_MAX_CHUNKS) return TSD_E_CHUNKS;
   if (a->dense_len < 0) return TSD_E_SHAPE;
+  if (a->idx_block < 0 || a->idx_block > TSD_PAGE_SIZE ||
+      (a->idx_block & (a->idx_block - 1)) != 0)
+    return TSD_E_UNSUPPORTED;
   if (!any_enc(a->kv_dtype) || !half_enc(a->q_dtype)) return TSD_E_DTYPE;
   if (a->kv_dtype != TSD_FP8_E4M3 && a->q_dtype != a->kv_dtype)
     return TSD_E_DTYPE;
