@@ -285,6 +285,9 @@ def _attn(**kw):
     (dict(idx=None), "NULL"),
     (dict(page_size=128), "PAGE_SIZE"),
     (dict(dense_len=-1), "SHAPE"),
+    (dict(idx_block=3), "UNSUPPORTED"),
+    (dict(idx_block=-1), "UNSUPPORTED"),
+    (dict(idx_block=128), "UNSUPPORTED"),
 ])
 def test_attn_rejections(kw, code):
     assert _attn(**kw) == E[code]
@@ -293,6 +296,8 @@ def test_attn_rejections(kw, code):
 def test_attn_empty_batch_and_null():
     assert LIB.sparse_gqa_decode(None, None) == E["NULL"]
     assert _attn(B=0, q=None, idx=None, page_table=None, seq_lens=None) == 0
+    assert _attn(B=0, q=None, idx=None, page_table=None, seq_lens=None,
+                 idx_block=64) == 0
 
 
 def test_merge_rejections():
