@@ -239,6 +239,44 @@ def test_ds_scores_brute_force(orc):
                                        atol=1e-12)
 
 
+def test_ds_score_points_brute_force(orc):
+    """Point-wise label scores (the oracle's checker for sampled entries of
+    long rows): row = b * H_kv + g. Random (row, t) pairs over 3 requests of
+    2 KV heads each are compared with a numpy brute force of the label score
+    at that point (the group's summed query at the heavy channels dotted
+    with the label of the token's mapped slot) and with the full score
+    matrix; a pair past its row's length or a row outside [0, B * H_kv)
+    raises."""
+    wl = tsd_synth.make(_ds_cfg(B=3, lens=(300, 65, 130)))
+    h = tsd_synth.to_host(wl)
+    q = _f64(wl["q"]); lab = _f64(wl["label_pool"])
+    ch = wl["channel_idx"].numpy()
+    pt = wl["page_table"].numpy()
+    lens = wl["seq_lens"].numpy()
+    H_kv, G = 2, 4
+    rng = np.random.default_rng(3)
+    rows = rng.integers(0, 3 * H_kv, size=200)
+    ts = np.array([rng.integers(0, lens[r // H_kv]) for r in rows])
+    rows[:6], ts[:6] = np.arange(6), lens[np.arange(6) // H_kv] - 1
+    pts = orc.ds_score_points(h["q"], "bf16", h["channel_idx"], h["label_pool"],
+                              "bf16", h["page_table"], h["seq_lens"],
+                              h["num_pages"], rows, ts)
+    for i, (r, t) in enumerate(zip(rows, ts)):
+        b, g = divmod(int(r), H_kv)
+        slot = pt[b, t // 64] * 64 + t % 64
+        qs = q[b, g * G:(g + 1) * G][:, ch[g]].sum(axis=0)
+        assert abs(pts[i] - lab[slot, g, :] @ qs) <= 1e-12 * max(1, abs(pts[i]))
+    full = orc.ds_scores(h["q"], "bf16", h["channel_idx"], h["label_pool"],
+                         "bf16", h["page_table"], h["seq_lens"], h["num_pages"])
+    assert np.array_equal(pts, full[rows, ts])
+    for bad_r, bad_t in ((1, 300), (2, 65), (6, 0), (-1, 0)):
+        with pytest.raises(orc.OracleError):
+            orc.ds_score_points(h["q"], "bf16", h["channel_idx"],
+                                h["label_pool"], "bf16", h["page_table"],
+                                h["seq_lens"], h["num_pages"],
+                                np.array([bad_r]), np.array([bad_t]))
+
+
 def test_ds_full_channels_give_group_logits(orc):
     """r = D with identity channels: the label score is (sum of the group's
     query heads) . K_t, i.e. the group's summed attention logits."""
