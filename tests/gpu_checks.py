@@ -68,6 +68,26 @@ def check_scores(gpu, ref64, row_lens, tol, rows=None):
     return worst
 
 
+def score_error_vs_window(gpu, ref64, row_lens, k):
+    """Per row: the largest score error over the row divided by the tie
+    window 1e-5 * max(1, |s_k|) of its k-th oracle score. When twice that
+    error fits in the window, every end-to-end selection difference is a
+    near-tie by construction (a swap of t and u needs both within two error
+    bounds of s_k), whatever the data. Returns the per-row ratios."""
+    out = []
+    for r in range(gpu.shape[0]):
+        n = int(row_lens[r])
+        if n == 0:
+            out.append(0.0)
+            continue
+        ref = ref64[r, :n]
+        m = min(k, n)
+        sk = np.partition(ref.astype(np.float32).astype(np.float64), n - m)[n - m]
+        err = np.abs(gpu[r, :n].astype(np.float64) - ref).max()
+        out.append(err / (TIE_WINDOW * max(1.0, abs(sk))))
+    return np.array(out)
+
+
 def check_topk_identical(scores32, row_lens, k, gpu_idx, gpu_count, rows=None):
     """Same f32 scores in -> identical arrays out."""
     rows = np.arange(scores32.shape[0]) if rows is None else np.asarray(rows)
@@ -77,25 +97,37 @@ def check_topk_identical(scores32, row_lens, k, gpu_idx, gpu_count, rows=None):
 
 
 def check_sets_within_window(gpu_idx, gpu_cnt, ref_idx, ref_cnt, ref_s32,
-                             row_lens, k, rows=None):
+                             row_lens, k, rows=None, label=""):
     """End-to-end selections: equal sizes, differences only at near-ties.
-    Returns the number of rows whose sets differ."""
+    Every array is aligned row by row; ``rows`` only names the rows in the
+    printout (default 0, 1, ...).
+    Prints, per row, the size of the symmetric difference, the largest
+    distance of a differing token's oracle score from the k-th score s_k
+    (in units of the window 1e-5 * max(1, |s_k|)) and the oracle's own gap
+    between the k-th and the (k+1)-th score. Returns the number of rows
+    whose sets differ."""
     rows = range(gpu_idx.shape[0]) if rows is None else rows
     differing = 0
-    for r in rows:
-        n = int(row_lens[r])
-        assert gpu_cnt[r] == ref_cnt[r] == min(k, n)
-        m = int(ref_cnt[r])
-        a = set(gpu_idx[r, :m].tolist())
-        b = set(ref_idx[r, :m].tolist())
-        assert (gpu_idx[r, m:] == -1).all()
-        assert (np.diff(gpu_idx[r, :m]) > 0).all()
+    for i, r in enumerate(rows):
+        n = int(row_lens[i])
+        assert gpu_cnt[i] == ref_cnt[i] == min(k, n)
+        m = int(ref_cnt[i])
+        a = set(gpu_idx[i, :m].tolist())
+        b = set(ref_idx[i, :m].tolist())
+        assert (gpu_idx[i, m:] == -1).all()
+        assert (np.diff(gpu_idx[i, :m]) > 0).all()
+        s = ref_s32[i, :n].astype(np.float64)
+        srt = np.sort(s)[::-1]
+        sk = srt[m - 1] if m else 0.0
+        gap = (srt[m - 1] - srt[m]) if m < n else float("inf")
+        window = TIE_WINDOW * max(1.0, abs(sk))
         diff = a ^ b
+        far = max((abs(s[t] - sk) for t in diff), default=0.0)
+        print(f"sets {label} row {r}: n={n} k={m} differing={len(diff)} "
+              f"max|s_t-s_k|/window={far / window:.3g} s_k={sk:.6g} "
+              f"gap(k,k+1)={gap:.3g}", flush=True)
         if diff:
             differing += 1
-            s = ref_s32[r, :n].astype(np.float64)
-            sk = np.sort(s)[::-1][m - 1]
-            window = TIE_WINDOW * max(1.0, abs(sk))
             for t in diff:
                 assert abs(s[t] - sk) <= window, (r, t, s[t], sk)
     return differing

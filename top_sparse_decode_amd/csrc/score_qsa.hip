@@ -6,17 +6,27 @@
 //
 // Per key the contraction is 16 heads x 128 dims = 2048 MACs over 128 bytes,
 // 32 flop per HBM byte: more than the FP32 vector units can sustain at HBM
-// speed, so each 16-key tile is one v_mfma_scale_f32_16x16x128_f8f6f4 with the
-// index heads as M, the keys as N and the 128 dims as K. The kernel stays a
-// single streaming pass over the index-K pages: every byte is read once, the
-// query rows sit in registers for the whole scan.
+// speed, so the decode scan runs each 16-key tile on the matrix cores (index
+// heads as M, keys as N, the 128 dims as K). It uses the bf16 16x16x32 MFMA
+// on exactly widened FP8 values rather than the FP8 16x16x128 MFMA: on this
+// part the FP8 instruction drops low-order bits of its products while it
+// adds them (measured: up to about 4e-4 of the largest product of a dot),
+// while every product of two E4M3 values is exact in the bf16 instruction
+// and its FP32 accumulation of the workloads' dots is exact, so the decode
+// scores carry only the FP32 rounding of the weighted head sum. The kernel
+// stays a single streaming pass over the index-K pages: every byte is read
+// once, the query rows sit in registers for the whole scan.
 //
 // Work split: one wave owns one query row and a run of up to 64 consecutive
-// 64-token pages; a page is 4 MFMA tiles of 16 keys. The 16x16 f32 result gives lane
+// 64-token pages; a page is 4 tiles of 16 keys. The 16x16 f32 result gives lane
 // l the dots of key (l % 16) with heads 4*(l/16) .. 4*(l/16)+3; the weighted
 // ReLU is applied per lane and a 3-shuffle reduce-scatter over the 4 lane
 // groups leaves lane l with the full score of key l of the page, so a page
 // stores 256 contiguous bytes of scores.
+//
+// The chunked-prefill kernel below is a dense contraction that is bound by
+// the matrix cores, and it keeps the FP8 instruction at twice the bf16 rate;
+// its scores carry that instruction's accumulation error.
 #include <type_traits>
 
 #include "device_common.h"
@@ -46,7 +56,7 @@ TSD_DEVICE v8i load_row_slice(const uint8_t* row, int kb) {
 
 // Weighted ReLU of one lane's 4 heads of an MFMA tile, in a fixed order of
 // rounding (written out with fmaf so that no contraction choice of the
-// compiler changes it): both index kernels call it, so they agree bitwise.
+// compiler changes it): both index kernels call it.
 TSD_DEVICE float weighted_relu4(v4f d, float w0, float w1, float w2, float w3) {
   const float m0 = fmaxf(d[0], 0.f), m1 = fmaxf(d[1], 0.f);
   const float m2 = fmaxf(d[2], 0.f), m3 = fmaxf(d[3], 0.f);
@@ -62,6 +72,43 @@ TSD_DEVICE v8i load_row_slice_nt(const uint8_t* row, int kb) {
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
+}
+
+// The 32 FP8 codes of a lane's operand slice (as load_row_slice packs them)
+// widened exactly to bf16 (every E4M3 value is a bf16 value) as the four
+// operands of the bf16 16x16x32 MFMA: operand s holds the codes of dwords
+// 2s and 2s + 1. Index heads and keys are widened the same way, so each
+// instruction still pairs dims of q with the same dims of k.
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+struct Bf16Slice {
+  v8bf s[4];
+};
+
+TSD_DEVICE Bf16Slice widen_fp8(v8i v) {
+  Bf16Slice r;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w = static_cast<uint32_t>(v[2 * s + j]);
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+      r.s[s][4 * j + 0] = lo[0];
+      r.s[s][4 * j + 1] = lo[1];
+      r.s[s][4 * j + 2] = hi[0];
+      r.s[s][4 * j + 3] = hi[1];
+    }
+  return r;
+}
+
+// 16 heads x 16 keys x 128 dims on the bf16 MFMA, FP32 accumulation.
+TSD_DEVICE v4f mfma_bf16_dot(const Bf16Slice& a, v8i b_fp8) {
+  const Bf16Slice b = widen_fp8(b_fp8);
+  v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.s[s], b.s[s], c, 0, 0, 0);
+  return c;
 }
 
 TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
@@ -134,10 +181,11 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     const int kb = lane >> 4;   // which 32-byte slice of the 128 dims
 
     // A operand: index head `col` of this row (zero for padded heads).
-    v8i qa = {0, 0, 0, 0, 0, 0, 0, 0};
+    v8i qa8 = {0, 0, 0, 0, 0, 0, 0, 0};
     if (col < H_i)
-      qa = load_row_slice(
+      qa8 = load_row_slice(
           index_q + (static_cast<int64_t>(row) * H_i + col) * kDi, kb);
+    const Bf16Slice qa = widen_fp8(qa8);
     // Weights of the 4 heads whose dots this lane receives.
     float w[4];
 #pragma unroll
@@ -179,7 +227,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
         float part[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const v4f dd = mfma_fp8(qa, kt[d][i]);
+          const v4f dd = mfma_bf16_dot(qa, kt[d][i]);
           part[i] = weighted_relu4(dd, w[0], w[1], w[2], w[3]);
         }
         // reduce-scatter over the 4 lane groups: lane l gets key l
@@ -247,8 +295,8 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
 // the current one; every wave then takes each 16-key tile of the block as a
 // B operand and issues one MFMA per row, so each key byte read from memory
 // feeds 64 rows. The per-row epilogue (weighted_relu4) and the cross-lane
-// reduce-scatter are the decode scan's, so both kernels produce bit-identical
-// scores. Keys past a row's causal limit are computed but never stored.
+// reduce-scatter are the decode scan's; the dots come from the FP8 MFMA.
+// Keys past a row's causal limit are computed but never stored.
 constexpr int kPfWaves = 8;
 constexpr int kPfRowsPerWave = 8;
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // rows per workgroup
