@@ -181,26 +181,35 @@ int sparse_index_score(const tsd_score_args *a, hipStream_t stream);
  *   ws       device workspace of at least topk_select_workspace_bytes()
  *            bytes, 16-byte aligned, caller-owned (one workspace per
  *            concurrent call); TSD_E_WORKSPACE if NULL, too small or
- *            misaligned. Its first rows * 5120 32-bit words are histograms
- *            that must be zero when the selection starts: without
- *            TSD_TOPK_WS_ZEROED the call zeroes them itself (one small
- *            launch), and every call returns with them zero again, so a
- *            caller may pass TSD_TOPK_WS_ZEROED when the workspace was
- *            zero-filled or last used by a completed call (on the same
- *            stream, or ordered before this one) with at least as many rows.
- *            The rest of the workspace needs no initialisation.
- *   flags    0 or TSD_TOPK_WS_ZEROED; other bits: TSD_E_UNSUPPORTED
+ *            misaligned. Its contents on entry do not matter: the call
+ *            zeroes the histograms it needs (one small launch) and returns
+ *            with its first rows * 5120 32-bit words zero again.
  * 1 <= k <= 4096; 0 <= rows <= 65535; stride >= max_len >= 0;
  * max_len <= 16,777,216.
  * ------------------------------------------------------------------------ */
-#define TSD_TOPK_WS_ZEROED 1
-
 size_t topk_select_workspace_bytes(int rows, int max_len, int k);
 
 int topk_select(const float *scores, int64_t stride, int rows,
                 const int32_t *row_lens, int max_len, int k, int32_t *idx,
-                int32_t *count, void *ws, size_t ws_bytes, int flags,
-                hipStream_t stream);
+                int32_t *count, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * topk_select_ex
+ *
+ * topk_select with flags. TSD_TOPK_WS_ZEROED tells the call that the first
+ * rows * 5120 32-bit words of ws (the histograms) are zero already, which
+ * skips the zeroing launch: true when the workspace was zero-filled, or was
+ * last used by a completed selection call (topk_select, topk_select_ex or
+ * sparse_index_topk, on the same stream or ordered before this one) with at
+ * least as many rows, since every such call leaves them zero. Other flag
+ * bits: TSD_E_UNSUPPORTED. Everything else as for topk_select.
+ * ------------------------------------------------------------------------ */
+#define TSD_TOPK_WS_ZEROED 1
+
+int topk_select_ex(const float *scores, int64_t stride, int rows,
+                   const int32_t *row_lens, int max_len, int k, int32_t *idx,
+                   int32_t *count, void *ws, size_t ws_bytes, int flags,
+                   hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * sparse_index_topk
@@ -217,7 +226,7 @@ int topk_select(const float *scores, int64_t stride, int rows,
  *   rows             B * H_kv (DS) or B * rows_per_req (QSA)
  *   max_len          min(a->score_stride, a->pt_stride * 64)
  *   ws / ws_bytes    topk_select_workspace_bytes(rows, max_len, k) bytes
- *   idx, count, k, flags   as for topk_select
+ *   idx, count, k, flags   as for topk_select_ex
  * ------------------------------------------------------------------------ */
 int sparse_index_topk(const tsd_score_args *a, int k, int32_t *idx,
                       int32_t *count, void *ws, size_t ws_bytes, int flags,
@@ -454,6 +463,11 @@ const char *tsd_strerror(int status);
 
 /* TSD_ABI_VERSION of the built library. */
 int tsd_abi_version(void);
+
+/* SHA-256 (64 hex digits, static string) of the sources the library was
+ * built from, so that a binding can refuse a library built from other
+ * sources than the ones beside it. */
+const char *tsd_source_sha256(void);
 
 /* sizeof the argument structs as compiled into the library, so a binding
  * can check its own layout. */

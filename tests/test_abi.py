@@ -116,13 +116,49 @@ def test_fused_score_topk_rejections():
     assert call(flags=2) == E["UNSUPPORTED"]
 
 
-def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, flags=0, **kw):
+def _topk(rows=2, max_len=100, k=10, stride=128, ws_bytes=None, flags=None,
+          **kw):
+    """topk_select, or topk_select_ex when flags are given."""
     need = LIB.topk_select_workspace_bytes(rows, max_len, k)
     args = dict(scores=FAKE, row_lens=FAKE, idx=FAKE, ws=FAKE)
     args.update(kw)
-    return LIB.topk_select(args["scores"], stride, rows, args["row_lens"],
-                           max_len, k, args["idx"], None, args["ws"],
-                           need if ws_bytes is None else ws_bytes, flags, None)
+    common = (args["scores"], stride, rows, args["row_lens"], max_len, k,
+              args["idx"], None, args["ws"],
+              need if ws_bytes is None else ws_bytes)
+    if flags is None:
+        return LIB.topk_select(*common, None)
+    return LIB.topk_select_ex(*common, flags, None)
+
+
+def _prototype(name):
+    """Parameter types of a function declared in the public header, with
+    the parameter names dropped and spacing normalised."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, name
+    out = []
+    for p in m.group(1).split(","):
+        p = " ".join(p.replace("*", " * ").split())
+        out.append(re.sub(r"\s*\w+$", "", p).strip())
+    return out
+
+
+def test_topk_select_prototype_is_the_contract():
+    """topk_select takes exactly (scores, stride, rows, row_lens, max_len, k,
+    idx, count, ws, ws_bytes, stream); the zeroed-workspace shortcut has a
+    name of its own."""
+    assert _prototype("topk_select") == [
+        "const float *", "int64_t", "int", "const int32_t *", "int", "int",
+        "int32_t *", "int32_t *", "void *", "size_t", "hipStream_t"]
+    assert _prototype("topk_select_ex") == _prototype("topk_select")[:-1] + [
+        "int", "hipStream_t"]
+    assert _prototype("sparse_gqa_decode") == ["const tsd_attn_args *",
+                                               "hipStream_t"]
+    assert _prototype("sparse_index_score") == ["const tsd_score_args *",
+                                                "hipStream_t"]
+    assert _prototype("lse_merge") == [
+        "const float *", "const float *", "int", "int", "int", "float *",
+        "float *", "hipStream_t"]
 
 
 def test_topk_rejections():
@@ -135,6 +171,8 @@ def test_topk_rejections():
     assert _topk(ws=ctypes.c_void_p(0x10008)) == E["WORKSPACE"]  # misaligned
     assert _topk(scores=None) == E["NULL"]
     assert _topk(flags=4) == E["UNSUPPORTED"]
+    assert _topk(flags=4, k=0) == E["K"]
+    assert _topk(flags=1, ws_bytes=16) == E["WORKSPACE"]
     assert _topk(rows=0, flags=1) == 0
     assert _topk(rows=70000) == E["UNSUPPORTED"]
     assert _topk(max_len=(1 << 24) + 1, stride=(1 << 24) + 1) == E["UNSUPPORTED"]

@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import glob
+import importlib.util
 import os
 import shutil
 import subprocess
@@ -47,9 +48,20 @@ def sources():
                   glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _source_sha256() -> str:
+    spec = importlib.util.spec_from_file_location(
+        "_tsd_srchash", os.path.join(PKG, "_srchash.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.source_sha256()
+
+
+def _compile(src: str, digest: str, build_dir: str = None,
+             extra: list = ()) -> str:
+    build_dir = build_dir or BUILD
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     cmd = ([hipcc()] + DEVICE_FLAGS + EXTRA_FLAGS.get(os.path.basename(src), [])
+           + [f'-DTSD_SOURCE_SHA256="{digest}"'] + list(extra)
            + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -57,22 +69,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libtsd.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD,
+          host_flags: list = ()) -> str:
+    """Compile every source and link libtsd.so (always rebuilds).
+    ``host_flags`` are added to every compile and to the link (a sanitized
+    variant passes host-only sanitizer flags here, with ``out`` and
+    ``build_dir`` elsewhere)."""
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
+    digest = _source_sha256()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + [
-        "-o", tmp]
+        objs = list(ex.map(lambda s: _compile(s, digest, build_dir,
+                                              host_flags), srcs))
+    tmp = out + ".tmp"
+    cmd = ([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"]
+           + list(host_flags) + objs + ["-o", tmp])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 def ensure_built() -> str:

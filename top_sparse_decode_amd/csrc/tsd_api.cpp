@@ -7,6 +7,11 @@
 #include "launch.h"
 #include "tsd.h"
 
+// Set by the build to the SHA-256 of the library's sources.
+#ifndef TSD_SOURCE_SHA256
+#define TSD_SOURCE_SHA256 "unknown"
+#endif
+
 namespace {
 
 constexpr int64_t kMaxGrid = std::numeric_limits<int32_t>::max();
@@ -188,8 +193,15 @@ size_t topk_select_workspace_bytes(int rows, int max_len, int k) {
 
 int topk_select(const float* scores, int64_t stride, int rows,
                 const int32_t* row_lens, int max_len, int k, int32_t* idx,
-                int32_t* count, void* ws, size_t ws_bytes, int flags,
-                hipStream_t stream) {
+                int32_t* count, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return topk_select_ex(scores, stride, rows, row_lens, max_len, k, idx, count,
+                        ws, ws_bytes, 0, stream);
+}
+
+int topk_select_ex(const float* scores, int64_t stride, int rows,
+                   const int32_t* row_lens, int max_len, int k, int32_t* idx,
+                   int32_t* count, void* ws, size_t ws_bytes, int flags,
+                   hipStream_t stream) {
   const int rc = validate_topk(scores, stride, rows, row_lens, max_len, k,
                                idx, ws, ws_bytes);
   if (rc) return rc;
@@ -335,6 +347,7 @@ const char* tsd_strerror(int status) {
 }
 
 int tsd_abi_version(void) { return TSD_ABI_VERSION; }
+const char* tsd_source_sha256(void) { return TSD_SOURCE_SHA256; }
 size_t tsd_sizeof_score_args(void) { return sizeof(tsd_score_args); }
 size_t tsd_sizeof_attn_args(void) { return sizeof(tsd_attn_args); }
 size_t tsd_sizeof_append_args(void) { return sizeof(tsd_append_args); }

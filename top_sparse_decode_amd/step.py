@@ -201,7 +201,8 @@ class Plan:
         else:
             first = (("sparse_index_score",
                       lambda: lib.sparse_index_score(self._score_ref, h)),
-                     ("topk_select", lambda: lib.topk_select(*self.topk_args, h)))
+                     ("topk_select",
+                      lambda: lib.topk_select_ex(*self.topk_args, h)))
         return first + (
             ("sparse_gqa_decode", lambda: lib.sparse_gqa_decode(self._attn_ref, h)),
             ("lse_merge", lambda: lib.lse_merge(*self.merge_args, h)))
