@@ -23,7 +23,9 @@ import numpy as np
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_DIR, "tsd_oracle.c")
-LIB_PATH = os.path.join(_DIR, "libtsd_oracle.so")
+# TSD_ORACLE_LIB names another build of the same source (the tests'
+# sanitizer build), used as it is.
+LIB_PATH = os.environ.get("TSD_ORACLE_LIB") or os.path.join(_DIR, "libtsd_oracle.so")
 
 DTYPE = {"bf16": 1, "fp16": 2, "fp8_e4m3": 3, "f32": 4}
 _ERR = {-1: "bad argument", -2: "page id out of range",
@@ -49,7 +51,8 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if (not os.path.exists(LIB_PATH)
+    if not os.environ.get("TSD_ORACLE_LIB") and (
+            not os.path.exists(LIB_PATH)
             or os.path.getmtime(LIB_PATH) < os.path.getmtime(_SRC)):
         build()
     lib = ctypes.CDLL(LIB_PATH)
