@@ -86,7 +86,9 @@ enum {
   TSD_E_WORKSPACE = -8,   /* workspace NULL or smaller than required         */
   TSD_E_UNSUPPORTED = -9, /* a valid but unsupported configuration (D, r...) */
   TSD_E_MODE = -10,       /* unknown score mode                              */
-  TSD_E_ABI = -11         /* args struct built for another ABI version       */
+  TSD_E_ABI = -11,        /* args struct built for another ABI version       */
+  TSD_E_SCRATCH = -12     /* needs more than the built-in scratch of
+                             topk_select_noalloc                             */
 };
 
 /* Supported bounds of this version. */
@@ -210,6 +212,30 @@ int topk_select_ex(const float *scores, int64_t stride, int rows,
                    const int32_t *row_lens, int max_len, int k, int32_t *idx,
                    int32_t *count, void *ws, size_t ws_bytes, int flags,
                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * topk_select_noalloc
+ *
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * selection of topk_select, identical results, with its workspace in a
+ * fixed device array inside the library instead of a caller buffer. The
+ * call allocates nothing; the array (topk_select_noalloc_max_bytes() =
+ * 8 MiB) exists once per GPU the library runs on and lives until the
+ * process ends. A selection that needs more than that,
+ * topk_select_workspace_bytes(rows, max_len, k) > the maximum, returns
+ * TSD_E_SCRATCH with nothing launched (8 rows of 262,144 need 2.3 MB, one
+ * row of 1,048,576 1.1 MB). Every call on a GPU shares that GPU's array and
+ * clears what must start at zero itself, so calls that overlap on one GPU
+ * (other streams, other threads) race: order them. The first call on a
+ * device looks up the array's address there. Arguments and errors
+ * otherwise as for topk_select.
+ * ------------------------------------------------------------------------ */
+size_t topk_select_noalloc_max_bytes(void);
+
+int topk_select_noalloc(const float *scores, int64_t stride, int rows,
+                        const int32_t *row_lens, int max_len, int k,
+                        int32_t *idx, int32_t *count, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * sparse_index_topk

@@ -15,7 +15,8 @@ HEADER = os.path.join(ROOT, "include", "tsd.h")
 LIB = tsd._lib
 
 E = dict(OK=0, NULL=-1, DTYPE=-2, SHAPE=-3, PAGE_SIZE=-4, GQA=-5, K=-6,
-         CHUNKS=-7, WORKSPACE=-8, UNSUPPORTED=-9, MODE=-10, ABI=-11)
+         CHUNKS=-7, WORKSPACE=-8, UNSUPPORTED=-9, MODE=-10, ABI=-11,
+         SCRATCH=-12)
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
 
 
@@ -352,3 +353,22 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         tsd.lse_merge(torch.zeros(2, 3, 8), torch.zeros(2, 3), torch.zeros(2, 8))
+
+
+def test_noalloc_rejections():
+    """topk_select_noalloc validates like topk_select and refuses a
+    selection larger than its built-in scratch before touching the
+    device."""
+    f = LIB.topk_select_noalloc
+
+    def call(rows=2, max_len=100, k=10, stride=128, scores=FAKE):
+        return f(scores, stride, rows, FAKE, max_len, k, FAKE, None, None)
+    assert LIB.topk_select_noalloc_max_bytes() == 8 << 20
+    assert call(k=0) == E["K"]
+    assert call(max_len=200) == E["SHAPE"]
+    assert call(rows=-1) == E["SHAPE"]
+    assert call(scores=None) == E["NULL"]
+    assert call(rows=70000) == E["UNSUPPORTED"]
+    assert call(rows=0, scores=None) == 0
+    assert call(rows=64, max_len=1 << 20, stride=1 << 20, k=2048) == E["SCRATCH"]
+    assert b"scratch" in LIB.tsd_strerror(E["SCRATCH"])

@@ -111,6 +111,10 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, _P, _P,
                                           _P, ctypes.c_size_t, ctypes.c_int,
                                           _P]),
+        "topk_select_noalloc": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P,
+                                               ctypes.c_int, ctypes.c_int, _P,
+                                               _P, _P]),
+        "topk_select_noalloc_max_bytes": (ctypes.c_size_t, []),
         "sparse_index_topk": (ctypes.c_int, [ctypes.POINTER(ScoreArgs),
                                              ctypes.c_int, _P, _P, _P,
                                              ctypes.c_size_t, ctypes.c_int, _P]),
@@ -156,6 +160,7 @@ def _load():
 _lib = _load()
 EXPORTS = ("sparse_index_score", "sparse_index_topk",
            "topk_select_workspace_bytes", "topk_select", "topk_select_ex",
+           "topk_select_noalloc", "topk_select_noalloc_max_bytes",
            "topk_merge_sharded", "sparse_gqa_decode", "lse_merge",
            "kv_append", "index_k_compress", "expand_blocks", "tsd_strerror",
            "tsd_abi_version", "tsd_source_sha256",
@@ -379,6 +384,26 @@ def topk_select(scores, row_lens, k, max_len, idx, count=None, workspace=None,
             *args, TSD_TOPK_WS_ZEROED, _stream(stream)))
     else:
         _check("topk_select", _lib.topk_select(*args, _stream(stream)))
+
+
+def topk_select_noalloc(scores, row_lens, k, max_len, idx, count=None,
+                        stream=None):
+    """topk_select without a caller workspace: the library's fixed device
+    scratch (topk_select_noalloc_max_bytes(), shared by every call on the
+    GPU) holds it, so nothing is allocated; calls on one GPU must not
+    overlap."""
+    _shape("scores", scores, None, None)
+    rows = scores.shape[0]
+    _shape("row_lens", row_lens, rows)
+    _shape("idx", idx, rows, k)
+    _shape("count", count, rows)
+    _dev("scores", scores, torch.float32)
+    _dev("row_lens", row_lens, torch.int32)
+    _dev("idx", idx, torch.int32)
+    _dev("count", count, torch.int32)
+    _check("topk_select_noalloc", _lib.topk_select_noalloc(
+        _ptr(scores), scores.shape[-1], rows, _ptr(row_lens), int(max_len),
+        int(k), _ptr(idx), _ptr(count), _stream(stream)))
 
 
 def topk_merge_sharded(scores, idx_local, count_local, k, idx, count=None,

@@ -340,6 +340,9 @@ const char* tsd_strerror(int status) {
     case TSD_E_UNSUPPORTED: return "configuration not supported by this library";
     case TSD_E_MODE: return "unknown score mode";
     case TSD_E_ABI: return "argument struct from another ABI version";
+    case TSD_E_SCRATCH:
+      return "selection needs more than the built-in scratch of "
+             "topk_select_noalloc";
     default:
       return status > 0 ? "HIP launch failed (status is the hipError_t)"
                         : "unknown status";
