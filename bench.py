@@ -43,34 +43,70 @@ def model_bytes(cfg):
     return index, gather
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(layer, seconds):
-    """The CPU oracle (single thread, as it stands) on whole requests of one
-    step, until about ``seconds`` of work; scaled to steps/s."""
-    import numpy as np  # noqa: F401
+    """The CPU oracle as it stands (plain C, double accumulation) on whole
+    requests of one decode step: first one thread, request after request,
+    until about ``seconds`` of work; then every usable core, one request per
+    task from a pool of as many tasks as cores (at least one step's worth;
+    the oracle's calls release the interpreter lock, so the threads run in
+    parallel). Both scaled to steps/s (requests done / requests per step /
+    wall time)."""
+    import concurrent.futures as cf
 
     import oracle
     import tsd_synth
     h = tsd_synth.to_host(layer)
     B = h["B"]
-    done, t0 = 0, time.perf_counter()
-    for b in range(B):
+
+    def one(b):
         sub = dict(h)
         sub["B"] = 1
         for key in ("q", "page_table", "seq_lens"):
             sub[key] = h[key][b:b + 1]
         if h["mode"] == "qsa":
-            sub["index_q"], sub["index_w"] = h["index_q"][b:b + 1], h["index_w"][b:b + 1]
+            sub["index_q"] = h["index_q"][b:b + 1]
+            sub["index_w"] = h["index_w"][b:b + 1]
         oracle.decode_step(sub)
+
+    oracle._load()
+    done, t0 = 0, time.perf_counter()
+    for b in range(B):
+        one(b)
         done += 1
         if time.perf_counter() - t0 >= seconds:
             break
-    el = time.perf_counter() - t0
-    return {"value": (done / B) / el, "unit": "steps/s", "cores": 1,
+    el1 = time.perf_counter() - t0
+    single = (done / B) / el1
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    tasks = max(B, cores)
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(one, [i % B for i in range(tasks)]))
+    elN = time.perf_counter() - t0
+    what = (f"every cached token scored, exact top-{h['top_k']}, sparse "
+            f"attention over {h['H_q']} heads, merge")
+    return {"value": (tasks / B) / elN, "unit": "steps/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{done} of {B} requests of one step (each: every cached "
-                      f"token scored, exact top-{h['top_k']}, sparse attention "
-                      f"over {h['H_q']} heads, merge) in {el:.1f} s, scaled to "
-                      f"steps/s"}
+            "sample": f"{tasks} request-tasks of one step ({B} requests; each: "
+                      f"{what}) on {cores} threads in {elN:.1f} s; one "
+                      f"thread: {done} of {B} requests in {el1:.1f} s; "
+                      f"scaled to steps/s",
+            "single_thread": {"value": single, "unit": "steps/s", "cores": 1},
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles",
@@ -167,7 +203,8 @@ def prefill_indexer(dev, passes, warmup):
             "roofline": {"bound": "mfma", "kernel": "sparse_index_score",
                          "achieved": tflops, "peak": FP8_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s",
-                         "frac": tflops / FP8_MFMA_PEAK_TFLOPS}}
+                         "frac": tflops / FP8_MFMA_PEAK_TFLOPS},
+            "vs_target": vs_target(cfg.name, ms_score)}
 
 
 def sharded_select(dev, passes, warmup, W=4):
@@ -363,7 +400,29 @@ def block_select(dev, passes, warmup, Bs=4, kb=512):
             "step_on_blocks_us": us_step_blk}
 
 
-def decode_leg(dev, name, steps, warmup):
+# Steps/s targets on one MI355X: 70 % of the HBM roofline of each decode
+# workload's model bytes (index or label keys of every cached token plus the
+# selected tokens' K/V), and for the prefill indexer 50 % of dense FP8 MFMA
+# peak on its causal contraction (ms per pass). The tiny workload fits in the
+# L2 caches and has no roofline target.
+TARGETS = {"qsa_decode_b8_l262144_k2048": ("steps_per_s", 19.6e3),
+           "qsa_decode_b1_l1048576_k2048": ("steps_per_s", 41.0e3),
+           "ds_llama31_8b_b3_l60000": ("steps_per_s", 43.4e3),
+           "ds_llama7b_b3_l20000_s200": ("steps_per_s", 50.0e3),
+           "qsa_prefill_r2048_l1048576_k2048": ("score_ms", 3.5)}
+
+
+def vs_target(name, value):
+    """{"target": t, "unit": u, "achieved_over_target": f} (f >= 1 meets the
+    target; for times, target / value), or None without a target."""
+    if name not in TARGETS:
+        return None
+    unit, t = TARGETS[name]
+    f = t / value if unit.endswith("_ms") else value / t
+    return {"target": t, "unit": unit, "achieved_over_target": f}
+
+
+def decode_leg(dev, name, steps, warmup, replicas=None):
     """One decode step (index or label scan + exact top-k through
     sparse_index_topk, sparse attention, LSE merge) on workload ``name``: K
     eager steps over replicas of the scanned pool (label pool for double
@@ -378,7 +437,7 @@ def decode_leg(dev, name, steps, warmup):
     import top_sparse_decode_amd.step as step
     cfg = tsd_synth.config(name)
     index_b, gather_b = model_bytes(cfg)
-    R = max(1, math.ceil(1e9 / index_b))
+    R = replicas or max(1, math.ceil(1e9 / index_b))
     wl = tsd_synth.make(cfg, dev)
     pool = "label_pool" if cfg.mode == "ds" else "index_k"
     layers = [wl] + [dict(wl, **{pool: wl[pool].clone()}) for _ in range(R - 1)]
@@ -427,6 +486,96 @@ def decode_leg(dev, name, steps, warmup):
                         "bytes_per_launch": index_b}}
     if cfg.mode == "ds":
         out["heavy_channels"] = cfg.r
+    out["vs_target"] = vs_target(name, out["steps_per_s"])
+    return out
+
+
+def tiny_leg(dev, steps, warmup):
+    """The tiny double-sparsity workload (1 request, 4,096 tokens, 8 query
+    heads on 1 KV head, top-256): its 262 KB per step stay in the caches,
+    so it is reported as latency (us per step), one layer, eager steps."""
+    out = decode_leg(dev, "ds_tiny_b1_l4096", steps, warmup, replicas=1)
+    out["us_per_step"] = out["ms_per_step"] * 1e3
+    out.pop("roofline", None)
+    out["bound"] = "latency (working set in cache)"
+    return out
+
+
+def ds_append_loop(dev, warmup_loops=1, replicas=None):
+    """The LLaMA-7B-shaped double-sparsity workload as the pages run it: 200
+    decode steps, each first storing every request's new token (K, V and its
+    label row, kv_append) and then decoding (sparse_index_topk,
+    sparse_gqa_decode, lse_merge), lengths 20,001 .. 20,200, a fresh query
+    per step. Each step runs on ``replicas`` layers (own label pools, shared
+    K/V pools) so the label bytes read between two visits of a layer exceed
+    the Infinity Cache. The timed region is the whole loop, the per-step
+    query and length updates included; steps/s counts one layer's append +
+    decode."""
+    import torch
+
+    import tsd_synth
+    import top_sparse_decode_amd as tsd
+    import top_sparse_decode_amd.step as step
+    cfg = tsd_synth.config("ds_llama7b_b3_l20000_s200")
+    index_b, gather_b = model_bytes(cfg)
+    R = replicas or max(1, math.ceil(1e9 / index_b))
+    wl = tsd_synth.make(cfg, dev)
+    layers = [wl] + [dict(wl, label_pool=wl["label_pool"].clone())
+                     for _ in range(R - 1)]
+    bufs = step.StepBuffers(wl)
+    plans = [step.Plan(layer, bufs, fused=True) for layer in layers]
+    base = wl["seq_lens"].clone()
+    pt = wl["page_table"]
+    B, S = cfg.B, cfg.steps
+    pos = (base.long() - 1)[:, None] + torch.arange(S, device=dev)[None]
+    slots = pt.long().gather(1, pos // 64) * 64 + pos % 64
+    k_rows = wl["k_pool"][slots].contiguous()      # [B, S, H_kv, D]
+    v_rows = wl["v_pool"][slots].contiguous()
+    one = torch.ones(B, dtype=torch.int32, device=dev)
+    pos32 = pos.to(torch.int32)
+    lens_s = [(base + s).contiguous() for s in range(S)]
+    new_k = [k_rows[:, s:s + 1].contiguous() for s in range(S)]
+    new_v = [v_rows[:, s:s + 1].contiguous() for s in range(S)]
+    new_pos = [pos32[:, s].contiguous() for s in range(S)]
+    appends = [[tsd.kv_append(pt, wl["num_pages"], new_pos[s], one, 1,
+                              k_new=new_k[s], v_new=new_v[s],
+                              k_pool=wl["k_pool"], v_pool=wl["v_pool"],
+                              channel_idx=wl["channel_idx"],
+                              label_pool=layer["label_pool"], prepare=True)
+                for layer in layers] for s in range(S)]
+
+    def loop():
+        for s in range(S):
+            wl["seq_lens"].copy_(lens_s[s])
+            wl["q"].copy_(wl["step_q"][s])
+            for li, plan in enumerate(plans):
+                rc = appends[s][li]()
+                if rc:
+                    raise RuntimeError(f"kv_append failed: {rc}")
+                plan.run()
+
+    for _ in range(warmup_loops):
+        loop()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    loop()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = wall / (S * R)
+    mean_len = float(base.float().mean()) + (S - 1) / 2
+    label_b = B * mean_len * cfg.H_kv * cfg.r * 2
+    del layers, plans, bufs, wl, k_rows, v_rows
+    torch.cuda.empty_cache()
+    out = {"workload": cfg.name, "batch": B, "decode_steps": S,
+           "lengths": [int(base[0]), int(base[0]) + S - 1],
+           "replicas": R, "steps_per_s": 1.0 / per, "us_per_step": per * 1e6,
+           "tokens_per_s_per_layer": B / per,
+           "model_bytes_per_step": label_b + gather_b,
+           "step_model_gbps": (label_b + gather_b) / per / 1e9,
+           "in_timed_region": "kv_append (K, V, label) + sparse_index_topk + "
+                              "sparse_gqa_decode + lse_merge per layer, query "
+                              "and length updates per step"}
+    out["vs_target"] = vs_target(cfg.name, out["steps_per_s"])
     return out
 
 
@@ -511,6 +660,10 @@ def main():
                     help="skip the 1,048,576-token single-request decode step")
     ap.add_argument("--no-blocks", action="store_true",
                     help="skip the block-compressed selection measurement")
+    ap.add_argument("--no-tiny", action="store_true",
+                    help="skip the tiny double-sparsity workload")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the 200-step append + decode loop")
     ap.add_argument("--no-sharded", action="store_true",
                     help="skip the page-owner sharded top-k emulation")
     ap.add_argument("--no-graph", action="store_true",
@@ -671,6 +824,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "bytes_per_launch": index_b, "traffic": scan_traffic()},
     }
+    line["vs_target"] = vs_target(cfg.name, line["value"])
     line["inputs_sha256"] = inputs_digest(layers[0])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(layers[0], args.cpu_seconds)
@@ -686,6 +840,10 @@ def main():
     if not args.no_ds:
         line["ds_decode"] = [decode_leg(dev, n, 500, 50) for n in
                              ("ds_llama31_8b_b3_l60000", "ds_llama7b_b3_l20000_s200")]
+    if not args.no_loop:
+        line["ds_append_decode_loop"] = ds_append_loop(dev)
+    if not args.no_tiny:
+        line["tiny_decode"] = tiny_leg(dev, 500, 50)
     if not args.no_blocks:
         line["block_compressed_select"] = block_select(dev, 200, 20)
     print(json.dumps(line), flush=True)

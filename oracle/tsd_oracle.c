@@ -77,16 +77,15 @@ double tsd_oracle_decode_fp16(uint16_t bits) {
 /* The 256 FP8 values, tabulated once from the decoder above so that large
  * scans do not call ldexp per element. */
 static double fp8_table[256];
-static int fp8_table_ready = 0;
 
-static double fp8(uint8_t code) {
-  if (!fp8_table_ready) {
-    for (int c = 0; c < 256; ++c)
-      fp8_table[c] = tsd_oracle_decode_fp8e4m3((uint8_t)c);
-    fp8_table_ready = 1;
-  }
-  return fp8_table[code];
+/* Filled when the library is loaded, before any call, so that calls from
+ * several threads only read it. */
+__attribute__((constructor)) static void fp8_table_fill(void) {
+  for (int c = 0; c < 256; ++c)
+    fp8_table[c] = tsd_oracle_decode_fp8e4m3((uint8_t)c);
 }
+
+static double fp8(uint8_t code) { return fp8_table[code]; }
 
 static double decode_elem(const void *base, int dtype, int64_t i) {
   switch (dtype) {
