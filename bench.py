@@ -819,7 +819,13 @@ def main():
         "eager_steps_per_s": K / wall_eager,
         "graph_steps_per_s": K / wall_graph if wall_graph else None,
         "copy_gbps": copy_gbps,
-        "roofline": {"bound": "hbm", "kernel": "sparse_index_score",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("qsa_scan_kernel<G, false> (sparse_index_score "
+                                "alone; the step's sparse_index_topk runs the "
+                                "same scan with the digit-1 histogram built in "
+                                "LDS, <G, true>, the same bytes)"
+                                if cfg.mode == "qsa" else
+                                "ds_scan_vec_kernel (sparse_index_score alone)"),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "bytes_per_launch": index_b, "traffic": scan_traffic()},
