@@ -389,9 +389,11 @@ int lse_merge(const float *o_part, const float *lse_part, int rows, int C,
  *    pool gets code(value / scale) with the page's f32 scale: a page none
  *    of whose tokens precede positions[b] is started by the call and its
  *    scale becomes amax / 448 (1 for amax 0) over the values the call
- *    writes to it (all heads and dims; K and V separately), stored in
- *    k_scale / v_scale; any other page keeps its stored scale, and values
- *    beyond 448 * scale saturate. Scale and quotient are computed in f32;
+ *    writes to it (all heads and dims; K and V separately) when the call
+ *    writes all 64 of its tokens, and 4 * amax / 448 when it writes fewer
+ *    (headroom for the tokens later calls append), stored in k_scale /
+ *    v_scale; any other page keeps its stored scale, and values beyond
+ *    448 * scale saturate. Scale and quotient are computed in f32;
  *    code() rounds to nearest, ties to even.
  *  - label (when channel_idx is not NULL): label_pool [slots, H_kv, r]
  *    (new_dtype) gets K_new[g][channel_idx[g][j]] for j < r (a channel

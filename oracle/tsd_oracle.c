@@ -413,7 +413,9 @@ int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
         if (lp * page_size < pos) continue;  /* page began before this call */
         if (t != lp * page_size && i != 0) continue;  /* once per page */
         float ka = 0.f, va = 0.f;
-        for (int32_t i2 = i; i2 < n && (pos + i2) / page_size == lp; ++i2)
+        int32_t written = 0;
+        for (int32_t i2 = i; i2 < n && (pos + i2) / page_size == lp; ++i2) {
+          ++written;
           for (int64_t e = 0; e < row; ++e) {
             const int64_t at = ((int64_t)b * max_new + i2) * row + e;
             const float kv = fabsf(half_or_f32(k_new, new_dtype, at));
@@ -421,8 +423,12 @@ int tsd_oracle_kv_append(int B, int64_t pt_stride, const int32_t *page_table,
             if (kv > ka) ka = kv;
             if (vv > va) va = vv;
           }
-        k_scale[page] = ka > 0.f ? ka / 448.0f : 1.0f;
-        v_scale[page] = va > 0.f ? va / 448.0f : 1.0f;
+        }
+        /* a page the call does not fill gets 4x the range of its values:
+         * two binades for the tokens later calls append to it */
+        const float room = written == page_size ? 1.0f : 4.0f;
+        k_scale[page] = ka > 0.f ? ka / 448.0f * room : 1.0f;
+        v_scale[page] = va > 0.f ? va / 448.0f * room : 1.0f;
       }
     }
     for (int32_t i = 0; i < n; ++i) {

@@ -491,7 +491,8 @@ def test_append_16bit_rows_label_and_index(orc):
 
 def test_append_fp8_pages_match_the_page_quantizer(orc):
     # a call that fills a fresh page gives the per-page quantization of the
-    # workload generator (scale = amax/448 in f32, round to nearest even)
+    # workload generator (scale = amax/448 in f32, round to nearest even); a
+    # page it starts but does not fill gets four times that range
     rng = np.random.default_rng(5)
     H, D = 2, 16
     x = (rng.normal(size=(1, 64 + 10, H, D)) * 3).astype(np.float32)
@@ -504,14 +505,18 @@ def test_append_fp8_pages_match_the_page_quantizer(orc):
     got = orc.kv_append(pt, 3, [0], [74], 74, k_new=kn, v_new=kn,
                         k_pool=kp, v_pool=kp.copy(), kv_enc="fp8_e4m3",
                         k_scale=ks, v_scale=ks.copy())
-    for lp_, page, lo, hi in [(0, 2, 0, 64), (1, 0, 64, 74)]:
-        vals = xb[0, lo:hi].float()
-        pad = torch.zeros((64, H, D))
-        pad[:hi - lo] = vals
-        codes, scale = tsd_synth.quantize_fp8_per_page(pad)
-        assert got["k_scale"][page] == scale[0].item()
-        np.testing.assert_array_equal(got["k_pool"][page * 64:page * 64 + hi - lo],
-                                      codes[:hi - lo].numpy())
+    # the full page: the generator's page quantizer (amax / 448)
+    pad = xb[0, 0:64].float()
+    codes, scale = tsd_synth.quantize_fp8_per_page(pad)
+    assert got["k_scale"][2] == scale[0].item()
+    np.testing.assert_array_equal(got["k_pool"][2 * 64:3 * 64], codes.numpy())
+    # the page the call leaves unfinished (10 of 64 tokens): 4 x amax / 448,
+    # codes = torch's float8 cast of value / scale, saturating at 448
+    vals = xb[0, 64:74].float()
+    s4 = np.float32(np.float32(vals.abs().max().item()) / np.float32(448.0)) * np.float32(4.0)
+    assert got["k_scale"][0] == s4
+    q = torch.clamp(vals / torch.tensor(s4), -448.0, 448.0).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(got["k_pool"][0:10], q.view(torch.uint8).numpy())
     assert got["k_scale"][1] == 7.0  # untouched page keeps its scale
     # appending to a started page keeps its scale and saturates above 448*s
     kn2 = _bf16_codes(np.full((1, 1, H, D), 1e4))

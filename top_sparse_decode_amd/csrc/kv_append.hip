@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kAT = 256;
 constexpr float kFp8Max = 448.f;
+constexpr float kAppendHeadroom = 4.f;
 
 TSD_DEVICE float clamp448(float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); }
 
@@ -92,8 +93,13 @@ __global__ __launch_bounds__(kAT) void kv_append_kernel(tsd_append_args a) {
         }
         ka = block_max(ka, lds);
         va = block_max(va, lds);
-        sk = ka > 0.f ? ka / kFp8Max : 1.f;
-        sv = va > 0.f ? va / kFp8Max : 1.f;
+        // a page this call does not fill keeps two binades of headroom for
+        // the tokens later calls append (a power of two: exact, and FP8
+        // precision is relative, so only values below 2^-6 of the range
+        // lose bits)
+        const float room = nt == kPage ? 1.f : kAppendHeadroom;
+        sk = ka > 0.f ? ka / kFp8Max * room : 1.f;
+        sv = va > 0.f ? va / kFp8Max * room : 1.f;
         if (tid == 0) {
           a.k_scale[page] = sk;
           a.v_scale[page] = sv;
