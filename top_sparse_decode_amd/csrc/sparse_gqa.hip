@@ -4,7 +4,8 @@
 // tokens, partial outputs merged by FP32 log-sum-exp; "Context parallelism
 // for QSA attention and the sparse indexer": a sparse GQA call per block).
 //
-// One workgroup (4 waves) per (request b, KV head g, chunk c) handles the G
+// One workgroup (8 waves for FP8 rows, 4 for 16-bit rows) per (request b,
+// KV head g, chunk c) handles the G
 // query heads of the group over the chunk's run of the ascending selection
 // list (every token 0 .. len-1 for a request at or below the sparse-decode
 // threshold), one tile of tokens at a time (128 tokens for FP8 rows, 64 for
@@ -19,8 +20,8 @@
 //      16-bit type, so the products are exact and accumulate in FP32;
 //   4. an online softmax (base 2) per head updates the running max and sum;
 //      the page's V scale is folded into the probabilities;
-//   5. O += P V on MFMA, each wave owning 32 output dimensions of every
-//      head: for 16-bit caches on v_mfma_f32_16x16x32_{bf16,f16} with P as
+//   5. O += P V on MFMA, each wave owning 128 / waves output dimensions of
+//      every head: for 16-bit caches on v_mfma_f32_16x16x32_{bf16,f16} with P as
 //      the sum of two 16-bit parts (within 2^-17 of P) and V as stored; for
 //      FP8 caches with P rounded once to bf16 and V widened exactly.
 #include "device_common.h"
@@ -29,7 +30,6 @@
 namespace tsd {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -53,11 +53,32 @@ struct Tile {
   static constexpr int kVPad = 32;
   static constexpr int kVBytes = kTokens * kVPitch + (kTokens / 8) * kVPad;
   static constexpr __host__ __device__ int vrow(int t) { return t * kVPitch + (t >> 3) * kVPad; }
-  static constexpr int kBlocks = kTokens / 16 / 4;   // 16-token blocks per wave
+  // waves per workgroup: an FP8 tile is short on arithmetic per byte, so
+  // twice the waves split each phase of a tile (one 16-token block per wave,
+  // 16 output dimensions per wave)
+  static constexpr int kWaves = ENC == TSD_FP8_E4M3 ? 8 : 4;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr int kBlocks = kTokens / 16 / kWaves;  // 16-token blocks per wave
+  static constexpr int kDW = kD / kWaves;  // output dimensions per wave
+  static constexpr int kJ = kDW / 16;      // 16-wide MFMA column blocks per wave
   // logits / probs pitch (floats): 16-byte aligned rows for the 8-wide P
   // reads of the P.V step
   static constexpr int kZPitch = kTokens + 4;
 };
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Two FP8 E4M3 codes (the low or, with HI, the high half of w) widened to a pair of
+// 16-bit values (QBF: bf16, else fp16) by the hardware converter at scale
+// 1; exact, since every E4M3 value is a bf16 and an fp16 value.
+template <bool QBF, bool HI>
+TSD_DEVICE uint32_t widen2(uint32_t w) {
+  if constexpr (QBF)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
 
 // 8 consecutive 16-bit values (as raw bits) starting at element `e0` of a
 // K row in LDS, in the encoding of the query (QBF: bf16, else fp16).
@@ -65,23 +86,8 @@ template <int ENC, bool QBF>
 TSD_DEVICE uint4 k8_as_q(const uint8_t* row, int e0) {
   if constexpr (ENC == TSD_FP8_E4M3) {
     const uint2 raw = *reinterpret_cast<const uint2*>(row + e0);
-    float f[8];
-    fp8x4_to_f32(raw.x, f);
-    fp8x4_to_f32(raw.y, f + 4);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo, hi;
-      if constexpr (QBF) {  // exact: an E4M3 value fits bf16
-        lo = __float_as_uint(f[2 * i]) >> 16;
-        hi = __float_as_uint(f[2 * i + 1]) >> 16;
-      } else {              // exact: an E4M3 value fits fp16
-        lo = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i]));
-        hi = __builtin_bit_cast(uint16_t, static_cast<_Float16>(f[2 * i + 1]));
-      }
-      w[i] = lo | (hi << 16);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+    return make_uint4(widen2<QBF, false>(raw.x), widen2<QBF, true>(raw.x),
+                      widen2<QBF, false>(raw.y), widen2<QBF, true>(raw.y));
   } else {
     return *reinterpret_cast<const uint4*>(row + 2 * e0);
   }
@@ -109,7 +115,7 @@ TSD_DEVICE v4f mfma_qk(uint4 a, uint4 b, v4f c) {
 }
 
 template <int ENC, bool QBF>
-__global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
+__global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
     const uint16_t* __restrict__ q, int H_q, int H_kv,
     const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
     const float* __restrict__ k_scale, const float* __restrict__ v_scale,
@@ -120,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     float* __restrict__ lse_part, int dense_len, int lbs) {
   using T = Tile<ENC>;
   constexpr int NT = T::kTokens;
+  constexpr int kThreads = T::kThreads, kWavesW = T::kWaves;
   constexpr bool fp8 = ENC == TSD_FP8_E4M3;
   __shared__ __align__(16) uint8_t k_s[NT * T::kPitch];
   __shared__ __align__(16) uint8_t v_s[T::kVBytes];
@@ -187,8 +194,10 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     m_s[tid] = -__builtin_inff();
     l_s[tid] = 0.f;
   }
-  // PV accumulators: O[4*grp + v][32*wave + 16*j + col]
-  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // PV accumulators: O[4*grp + v][kDW*wave + 16*j + col]
+  v4f acc[T::kJ];
+#pragma unroll
+  for (int j = 0; j < T::kJ; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int64_t base = lo; base < hi; base += NT) {
     const int tn = static_cast<int>(hi - base < NT ? hi - base : NT);
@@ -264,10 +273,10 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         zp_s[(4 * grp + v) * T::kZPitch + t] = live ? s[v] * f : -__builtin_inff();
     }
     __syncthreads();
-    // 4. online softmax per head (base 2): wave handles heads wave + 4*i
+    // 4. online softmax per head (base 2): wave handles heads wave + W*i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = wave + 4 * i;
+    for (int i = 0; i < 16 / kWavesW; ++i) {
+      const int hh = wave + kWavesW * i;
       if (hh < G) {
         float z[NT / 64];
         float tmax = -__builtin_inff();
@@ -307,8 +316,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
     for (int v = 0; v < 4; ++v) {
       const int hh = 4 * grp + v;
       const float a = hh < G ? alpha_s[hh] : 0.f;
-      acc[0][v] *= a;
-      acc[1][v] *= a;
+#pragma unroll
+      for (int j = 0; j < T::kJ; ++j) acc[j][v] *= a;
     }
     const bool arow = col < G;
     if constexpr (fp8) {
@@ -330,8 +339,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
           pa = v8bf{};
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint8_t* vc = v_s + T::vrow(t0) + 32 * wave + 16 * j + col;
+        for (int j = 0; j < T::kJ; ++j) {
+          const uint8_t* vc = v_s + T::vrow(t0) + T::kDW * wave + 16 * j + col;
           uint32_t w[2];
 #pragma unroll
           for (int h = 0; h < 2; ++h)
@@ -339,17 +348,11 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
                    static_cast<uint32_t>(vc[(4 * h + 1) * T::kPitch]) << 8 |
                    static_cast<uint32_t>(vc[(4 * h + 2) * T::kPitch]) << 16 |
                    static_cast<uint32_t>(vc[(4 * h + 3) * T::kPitch]) << 24;
-          float f[8];
-          fp8x4_to_f32(w[0], f);
-          fp8x4_to_f32(w[1], f + 4);
-          uint32_t bb[4];  // an E4M3 value is exact in bf16: its top 16 bits
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            bb[i] = (__float_as_uint(f[2 * i]) >> 16) |
-                    (__float_as_uint(f[2 * i + 1]) & 0xffff0000u);
+          // the FP8 V codes widened exactly to bf16
+          const uint4 bv = make_uint4(widen2<true, false>(w[0]), widen2<true, true>(w[0]),
+                                      widen2<true, false>(w[1]), widen2<true, true>(w[1]));
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa, __builtin_bit_cast(v8bf, make_uint4(bb[0], bb[1], bb[2], bb[3])),
-              acc[j], 0, 0, 0);
+              pa, __builtin_bit_cast(v8bf, bv), acc[j], 0, 0, 0);
         }
       }
     } else {
@@ -397,8 +400,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
         // rows t .. t+3; two loads give tokens t0 .. t0+7 of one dimension
         const int q = col;  // the lane's index in its group of 16
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint8_t* vb = v_s + 2 * (32 * wave + 16 * j + 4 * (q & 3));
+        for (int j = 0; j < T::kJ; ++j) {
+          const uint8_t* vb = v_s + 2 * (T::kDW * wave + 16 * j + 4 * (q & 3));
           const v4s lo = lds_read_tr16(vb + T::vrow(t0 + (q >> 2)));
           const v4s hi = lds_read_tr16(vb + T::vrow(t0 + 4 + (q >> 2)));
           const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
@@ -419,8 +422,8 @@ __global__ __launch_bounds__(kThreads) void sparse_gqa_kernel(
       const float l = l_s[hh];
       const float inv = l > 0.f ? 1.f / l : 0.f;
       float* o = o_part + ((static_cast<int64_t>(b) * H_q + h0 + hh) * C + c) * kD;
-      o[32 * wave + col] = acc[0][v] * inv;
-      o[32 * wave + 16 + col] = acc[1][v] * inv;
+#pragma unroll
+      for (int j = 0; j < T::kJ; ++j) o[T::kDW * wave + 16 * j + col] = acc[j][v] * inv;
     }
   }
   if (tid < G) {
@@ -434,7 +437,7 @@ template <int ENC, bool QBF>
 hipError_t launch_enc(const tsd_attn_args& a, hipStream_t s) {
   dim3 grid(static_cast<uint32_t>(a.chunks), static_cast<uint32_t>(a.H_kv),
             static_cast<uint32_t>(a.B));
-  hipLaunchKernelGGL((sparse_gqa_kernel<ENC, QBF>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((sparse_gqa_kernel<ENC, QBF>), grid, dim3(Tile<ENC>::kThreads), 0,
                      s, static_cast<const uint16_t*>(a.q), a.H_q, a.H_kv,
                      static_cast<const uint8_t*>(a.k_pool),
                      static_cast<const uint8_t*>(a.v_pool), a.k_scale,
