@@ -37,13 +37,12 @@ namespace tsd {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 constexpr int kChunk = kTopkChunk;     // elements per pass-1/2 workgroup
 constexpr int kPerThread = kChunk / kThreads;
 constexpr int kListCap = kTopkListCap;  // entries kept per chunk list
 constexpr int kB1 = kTopkB1, kB2 = kTopkB2, kB3 = kTopkB3;
 constexpr int kBins1 = kTopkBins1, kBins2 = kTopkBins2, kBins3 = kTopkBins3;
-constexpr int kShift1 = 32 - kB1, kShift2 = kB3;
+constexpr int kShift2 = kB3;
 constexpr int kRT = 1024;              // pass-3 threads
 constexpr int kSegBits = 1 << 19;      // indices per bitmap segment
 constexpr int kSegWords = kSegBits / 32;
@@ -83,25 +82,37 @@ __global__ __launch_bounds__(kThreads) void topk_clear_kernel(
 }
 
 // Pass 1: histogram of digit 1; a workgroup covers `cpw` consecutive chunks.
+// The first chunk's scores are loaded together with the row length (load i
+// reads entry min(i, cap - 1) of the row, cap = min(max_len, stride) >=
+// 24,577 here since shorter rows take the one-workgroup path; entries at or
+// past the length are not counted).
 __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
     const float* __restrict__ scores, int64_t stride,
     const int32_t* __restrict__ row_lens, int64_t cap, int k, int nch,
     int cpw, void* __restrict__ ws_base) {
   __shared__ __align__(16) uint32_t hist[kBins1];
   const int row = blockIdx.y;
-  const int64_t n = clamp_len(row_lens[row], cap);
+  const int32_t len_raw = row_lens[row];
   const int64_t start = static_cast<int64_t>(blockIdx.x) * cpw * kChunk;
-  if (n <= k || start >= n) return;
   const float* s = scores + row * stride;
+  float v[kPerThread];
+#pragma unroll
+  for (int j = 0; j < kPerThread; ++j) {
+    const int64_t i = start + threadIdx.x + j * kThreads;
+    v[j] = s[i < cap ? i : cap - 1];
+  }
+  const int64_t n = clamp_len(len_raw, cap);
+  if (n <= k || start >= n) return;
   zero_lds<kBins1, kThreads>(hist);
   for (int c = 0; c < cpw; ++c) {
     const int64_t c0 = start + static_cast<int64_t>(c) * kChunk;
     if (c0 >= n) break;
-    float v[kPerThread];
+    if (c > 0) {
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-      const int64_t i = c0 + threadIdx.x + j * kThreads;
-      v[j] = i < n ? s[i] : 0.f;
+      for (int j = 0; j < kPerThread; ++j) {
+        const int64_t i = c0 + threadIdx.x + j * kThreads;
+        v[j] = i < n ? s[i] : 0.f;
+      }
     }
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
@@ -139,23 +150,26 @@ __global__ __launch_bounds__(kFT) void topk_filter_kernel(
   __shared__ uint32_t lds[kFW];
   __shared__ BinPick pick;
   const int row = blockIdx.y;
-  const int64_t n = clamp_len(row_lens[row], cap);
+  const int32_t len_raw = row_lens[row];
   constexpr int kFChunks = FC;                     // chunks per pass
   constexpr int kFWavesPerChunk = kFW / kFChunks;
   constexpr int kFSub = kChunk / kFWavesPerChunk;  // elements per wave
   constexpr int kFPer = kFSub / kWave;             // elements per lane
   constexpr int64_t kSpan = static_cast<int64_t>(kFChunks) * kChunk;
   const int64_t start = static_cast<int64_t>(blockIdx.x) * passes * kSpan;
-  if (n <= k || start >= n) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
   const int q = w / kFWavesPerChunk, wq = w % kFWavesPerChunk;
   const float* s = scores + row * stride;
   const Ws ws = topk_ws(ws_base, gridDim.y, nch);
   // b1 from the row's H1: thread t holds bins [4096 - 4(t+1), 4096 - 4t).
-  // H1 is loaded before the scores and the score loads are unconditional
-  // (an index past the row reads its last score and is masked at use), so
-  // the wait for H1 leaves the scores in flight during the pick (loads
-  // complete in order).
+  // The row length, H1 and the first pass's scores are loaded in that order
+  // before any of them is used. The score loads are unconditional and do
+  // not wait for the length: load i reads entry min(i, cap - 1), inside the
+  // row's [0, cap) of the caller's buffer (cap = min(max_len, stride) >=
+  // 24,577 here: shorter rows take the one-workgroup path), and entries at
+  // or past the length are masked at use. Loads
+  // complete in order, so the early-exit test waits for the length only and
+  // the pick's wait for H1 leaves the scores in flight.
   constexpr int per1 = kBins1 / kFT;
   static_assert(per1 == 4, "one uint4 run per thread");
   const uint4 x = *reinterpret_cast<const uint4*>(
@@ -167,10 +181,12 @@ __global__ __launch_bounds__(kFT) void topk_filter_kernel(
 #pragma unroll
     for (int r = 0; r < kFPer; ++r) {
       const int64_t i = sub + r * kWave + lane;
-      v[r] = s[i < n ? i : n - 1];
+      v[r] = s[i < cap ? i : cap - 1];
     }
   };
   load_pass(start);
+  const int64_t n = clamp_len(len_raw, cap);
+  if (n <= k || start >= n) return;
   const uint32_t h[per1] = {x.w, x.z, x.y, x.x};  // from the top down
   for (int i = tid; i < kBins2; i += kFT) hist[i] = 0u;  // ordered by the pick
   const BinPick p1 =
@@ -689,12 +705,29 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   __shared__ uint32_t h1[kCopies * kCopyPitch];
   __shared__ __align__(16) uint32_t h2[kBins2];
   __shared__ __align__(16) uint32_t h3[kBins3];
-  __shared__ uint32_t gt_s[kBlocks], eq_s[kBlocks];
+  __shared__ uint32_t cnt_s[kBlocks];  // (ties << 16 | above) per block
   __shared__ uint32_t lds[kRT / kWave + 1];
   __shared__ BinPick pick;
   const int row = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-  const int64_t n = clamp_len(row_lens[row], cap);
+  // The row's scores are loaded together with its length, not after it:
+  // load i reads entry min(i, cap - 1), inside the row's [0, cap) of the
+  // caller's [rows, stride] buffer (cap = min(max_len, stride) <= 32,768),
+  // and entries at or past the length are masked below. Every load is
+  // unconditional, so the first histogram consumes the row while the rest
+  // of it is still in flight.
+  const float* s = scores + row * stride;
+  const int capi = static_cast<int>(cap);
+  const int32_t len_raw = row_lens[row];
+  uint32_t key[RPT];
+  if (capi > 0) {  // uniform; cap = 0 leaves every row empty
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int i = r * kRT + tid;
+      key[r] = __float_as_uint(s[i < capi ? i : capi - 1]);
+    }
+  }
+  const int64_t n = clamp_len(len_raw, cap);
   int32_t* out = idx + static_cast<int64_t>(row) * k;
   if (n <= k) {
     for (int64_t j = tid; j < k; j += kRT)
@@ -702,9 +735,6 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
     if (tid == 0 && count) count[row] = static_cast<int32_t>(n);
     return;
   }
-  // every load is unconditional (an index past the row reads its last
-  // element), so the first histogram consumes the row while the rest of it
-  // is still in flight
   const int n32 = static_cast<int>(n);  // n <= 32,768 here
   // rounds holding elements, a scalar; each pass takes a fresh copy so no
   // per-round condition is kept from one pass to the next
@@ -714,13 +744,6 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
     asm volatile("" : "+s"(v));
     return v;
   };
-  const float* s = scores + row * stride;
-  uint32_t key[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int i = r * kRT + tid;
-    key[r] = __float_as_uint(s[i < n32 ? i : n32 - 1]);
-  }
   for (int i = tid; i < kCopies * kCopyPitch; i += kRT) h1[i] = 0u;
   h2[tid] = 0u;
   h3[tid] = 0u;
@@ -771,37 +794,30 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   const BinPick p3 = pick_bin<kBins3, kRT>(h3, need2, lds, &pick);
   const uint32_t T = (pre << kB3) | p3.bin;
   const uint32_t need = need2 - p3.above;  // ties at T to keep
-  // counts above T and at T of every (round, wave) block
+  // counts above T and at T of every (round, wave) block, packed as
+  // (ties << 16 | above) and scanned once: both totals are at most
+  // n <= 32,768, so the low field never carries into the high one
   const int nr4 = rounds();
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const uint32_t g = static_cast<uint32_t>(__popcll(__ballot(key[r] > T)));
     const uint32_t q = static_cast<uint32_t>(__popcll(__ballot(key[r] == T)));
-    if (lane == 0) {
-      gt_s[r * kWavesR + wave] = r < nr4 ? g : 0u;
-      eq_s[r * kWavesR + wave] = r < nr4 ? q : 0u;
-    }
+    if (lane == 0) cnt_s[r * kWavesR + wave] = r < nr4 ? (q << 16) | g : 0u;
   }
   __syncthreads();
   {
-    const uint32_t g = tid < kBlocks ? gt_s[tid] : 0u;
-    const uint32_t q = tid < kBlocks ? eq_s[tid] : 0u;
-    const uint32_t gb = block_exclusive_scan<kRT>(g, lds);
-    const uint32_t qb = block_exclusive_scan<kRT>(q, lds);
-    if (tid < kBlocks) {
-      gt_s[tid] = gb;
-      eq_s[tid] = qb;
-    }
+    const uint32_t v = tid < kBlocks ? cnt_s[tid] : 0u;
+    const uint32_t vb = block_exclusive_scan<kRT>(v, lds);
+    if (tid < kBlocks) cnt_s[tid] = vb;
   }
   __syncthreads();
-  const int gbl = lane < RPT ? static_cast<int>(gt_s[lane * kWavesR + wave]) : 0;
-  const int qbl = lane < RPT ? static_cast<int>(eq_s[lane * kWavesR + wave]) : 0;
+  const int pbl = lane < RPT ? static_cast<int>(cnt_s[lane * kWavesR + wave]) : 0;
   const int nr5 = rounds();
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     if (r >= nr5) continue;
-    const uint32_t gb = static_cast<uint32_t>(__builtin_amdgcn_readlane(gbl, r));
-    const uint32_t qb = static_cast<uint32_t>(__builtin_amdgcn_readlane(qbl, r));
+    const uint32_t pb = static_cast<uint32_t>(__builtin_amdgcn_readlane(pbl, r));
+    const uint32_t gb = pb & 0xffffu, qb = pb >> 16;
     const bool gt = key[r] > T, eq = key[r] == T;
     const uint64_t me = __ballot(eq);
     const uint32_t rank = qb + static_cast<uint32_t>(__popcll(me & lt));
