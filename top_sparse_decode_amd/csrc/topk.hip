@@ -40,7 +40,7 @@ constexpr int kThreads = 256;
 constexpr int kChunk = kTopkChunk;     // elements per pass-1/2 workgroup
 constexpr int kPerThread = kChunk / kThreads;
 constexpr int kListCap = kTopkListCap;  // entries kept per chunk list
-constexpr int kB1 = kTopkB1, kB2 = kTopkB2, kB3 = kTopkB3;
+constexpr int kB2 = kTopkB2, kB3 = kTopkB3;
 constexpr int kBins1 = kTopkBins1, kBins2 = kTopkBins2, kBins3 = kTopkBins3;
 constexpr int kShift2 = kB3;
 constexpr int kRT = 1024;              // pass-3 threads
