@@ -1039,6 +1039,9 @@ def test_graph_replay_matches_eager():
     (DS8B, dict(B=2, lens=(30000, 12345), r=64, n_outlier=40, top_k=500,
                 chunks=4)),
     (DS8B, dict(B=1, H_q=48, H_kv=24, lens=(40000,), top_k=700, chunks=4)),
+    # the general label kernel (r not a multiple of 8) on such rows
+    (DS8B, dict(B=2, lens=(30000, 26000), r=24, n_outlier=24, top_k=500,
+                chunks=4)),
 ])
 def test_fused_score_select_matches_separate_calls(name, over):
     step = _step()
