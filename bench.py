@@ -56,12 +56,13 @@ def _cpu_model():
 
 def cpu_baseline(layer, seconds):
     """The CPU oracle as it stands (plain C, double accumulation) on whole
-    requests of one decode step: first one thread, request after request,
-    until about ``seconds`` of work; then every usable core, one request per
-    task from a pool of as many tasks as cores (at least one step's worth;
-    the oracle's calls release the interpreter lock, so the threads run in
-    parallel). Both scaled to steps/s (requests done / requests per step /
-    wall time)."""
+    requests of one decode step, about ``seconds`` of CPU work in all: first
+    one thread, request after request (cycling over the step's requests),
+    for two thirds of it; then every usable core, one request per task, for
+    about ``seconds`` more CPU-seconds (at least one task per core and one
+    step's worth; the oracle's calls release the interpreter lock, so the
+    threads run in parallel). Both scaled to steps/s (requests done /
+    requests per step / wall time)."""
     import concurrent.futures as cf
 
     import oracle
@@ -81,10 +82,10 @@ def cpu_baseline(layer, seconds):
 
     oracle._load()
     done, t0 = 0, time.perf_counter()
-    for b in range(B):
-        one(b)
+    while True:
+        one(done % B)
         done += 1
-        if time.perf_counter() - t0 >= seconds:
+        if time.perf_counter() - t0 >= seconds * 2 / 3:
             break
     el1 = time.perf_counter() - t0
     single = (done / B) / el1
@@ -92,7 +93,9 @@ def cpu_baseline(layer, seconds):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
-    tasks = max(B, cores)
+    per_request = el1 / done
+    tasks = max(B, cores, math.ceil(seconds / per_request))
+    tasks = (tasks + cores - 1) // cores * cores
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=cores) as ex:
         list(ex.map(one, [i % B for i in range(tasks)]))
@@ -101,9 +104,9 @@ def cpu_baseline(layer, seconds):
             f"attention over {h['H_q']} heads, merge")
     return {"value": (tasks / B) / elN, "unit": "steps/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{tasks} request-tasks of one step ({B} requests; each: "
+            "sample": f"{tasks} request-tasks ({B} requests per step; each: "
                       f"{what}) on {cores} threads in {elN:.1f} s; one "
-                      f"thread: {done} of {B} requests in {el1:.1f} s; "
+                      f"thread: {done} requests in {el1:.1f} s; "
                       f"scaled to steps/s",
             "single_thread": {"value": single, "unit": "steps/s", "cores": 1},
             "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
