@@ -1061,6 +1061,54 @@ def test_fused_score_select_matches_separate_calls(name, over):
     assert not _hist_words(b.ws, b.rows).any(), "histograms left nonzero"
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("ranges", [
+    ((0, 0, 8192),),                      # one whole scan workgroup's chunk
+    ((0, 6000, 14000), (1, 40000, 41000)),  # across chunks, two rows
+    ((0, 100000, 100040), (2, 29990, 30000)),  # a few tokens, a row's end
+])
+def test_fused_select_with_clustered_top_scores(ranges):
+    """Long decode rows (4 x 4,096 pages, the index scan building the
+    digit-1 histogram) whose top-k gathers in a few token ranges: the index
+    keys there are set to six times the mean of their request's index
+    heads. A chunk inside a long range keeps more survivors than its
+    512-entry list holds and is re-read raw by the resolve; a short range
+    puts a few of the top scores in one chunk. Scores, lengths and
+    selections equal the separate calls bit for bit, and the selection
+    equals the oracle's top-k of the GPU's own scores."""
+    step = _step()
+    wl = tsd_synth.make(tsd_synth.config(QSA, B=4, lens=(262144, 60000, 30000, 300),
+                                         top_k=2048, chunks=4, seed=150), DEV)
+    pt = wl["page_table"]
+    iq = wl["index_q"].view(torch.float8_e4m3fn).float()  # [B, 16, 128]
+    for b, lo, hi in ranges:
+        t = torch.arange(lo, hi, device=DEV)
+        slots = pt[b, t // 64].long() * 64 + t % 64
+        boost = (6.0 * iq[b].mean(dim=0)).clamp(-448, 448)
+        wl["index_k"][slots] = tsd_synth.fp8_codes(boost.expand(len(t), -1).contiguous())
+    a = step.StepBuffers(wl)
+    b_ = step.StepBuffers(wl)
+    a.scores.fill_(float("nan"))
+    b_.scores.fill_(float("nan"))
+    step.score(wl, a)
+    step.select(wl, a)
+    step.score_select(wl, b_)
+    torch.cuda.synchronize()
+    for x, y in ((a.row_lens, b_.row_lens), (a.idx, b_.idx), (a.count, b_.count)):
+        assert torch.equal(x, y)
+    assert torch.equal(torch.nan_to_num(a.scores, nan=-7.0),
+                       torch.nan_to_num(b_.scores, nan=-7.0))
+    assert not _hist_words(b_.ws, b_.rows).any(), "histograms left nonzero"
+    S = np.nan_to_num(b_.scores.cpu().numpy(), nan=0.0)
+    ridx, rcnt = oracle.topk(S, b_.row_lens.cpu().numpy(), 2048)
+    assert np.array_equal(b_.idx.cpu().numpy(), ridx)
+    assert np.array_equal(b_.count.cpu().numpy(), rcnt)
+    # the boosted range holds the top of row 0 (the case is what it says)
+    lo0, hi0 = ranges[0][1], ranges[0][2]
+    sel0 = b_.idx[0].cpu().numpy()
+    assert ((sel0 >= lo0) & (sel0 < hi0)).sum() >= 0.9 * min(2048, hi0 - lo0)
+
+
 def _prefill_case(lens, R, seed, stale_tail=False):
     cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=200, chunks=4,
                            seed=seed, stale_tail=stale_tail)
