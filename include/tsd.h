@@ -176,7 +176,9 @@ int sparse_index_score(const tsd_score_args *a, hipStream_t stream);
  * scores[row][0 .. n), in strictly ascending order; among equal scores the
  * lower index is taken. idx[row][m .. k) = -1; count[row] = m (count may be
  * NULL). Scores compare as floats: -0 and +0 are equal; +-inf are allowed;
- * NaN is outside the contract.
+ * NaN is outside the contract. Any entry of scores[row][0 .. min(max_len,
+ * stride)) may be read, whatever the row's length (entries at or past it
+ * are ignored), so the whole [rows, stride] buffer must be allocated.
  *   scores   [rows, stride] f32          row_lens [rows] int32
  *   idx      [rows, k] int32             count    [rows] int32 or NULL
  *   max_len  host-side bound on every row length (sizes the launch)
