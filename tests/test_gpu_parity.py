@@ -988,16 +988,21 @@ def test_selection_covering_context_is_dense_attention():
     assert np.abs(bufs.out_lse.cpu().numpy() - dlse).max() <= out_tol("fp8_e4m3")
 
 
-def test_graph_replay_matches_eager():
-    """The four calls captured in a HIP graph, replayed with fresh inputs
-    copied in between (and eager work between replays), match the eager
-    results of the same inputs on every replay."""
+@pytest.mark.parametrize("fused,first", [(False, 6000), (True, 40000)],
+                         ids=["separate-short", "fused-long"])
+def test_graph_replay_matches_eager(fused, first):
+    """The calls of a step captured in a HIP graph, replayed with fresh
+    inputs copied in between (and eager work between replays), match the
+    eager results of the same inputs on every replay: the separate calls on
+    short rows (one-workgroup top-k), and sparse_index_topk on a row long
+    enough for the chunked selection, whose histograms the in-scan pass
+    fills and the resolve leaves zero for the next replay."""
     step = _step()
-    cfg = tsd_synth.config(QSA, B=3, lens=(6000, 4097, 130), top_k=512,
+    cfg = tsd_synth.config(QSA, B=3, lens=(first, 4097, 130), top_k=512,
                            chunks=8, seed=130)
     wl = tsd_synth.make(cfg, DEV)
     bufs = step.StepBuffers(wl)
-    plan = step.Plan(wl, bufs)
+    plan = step.Plan(wl, bufs, fused=fused)
     plan.run()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -1011,7 +1016,7 @@ def test_graph_replay_matches_eager():
             torch.randn(wl["index_q"].shape, generator=gen, device=DEV)))
         wl["q"].copy_(torch.randn(wl["q"].shape, generator=gen,
                                   device=DEV).to(torch.bfloat16))
-        wl["seq_lens"].copy_(torch.tensor([6000 - 7 * rep, 4097 - rep, 130 + rep],
+        wl["seq_lens"].copy_(torch.tensor([first - 7 * rep, 4097 - rep, 130 + rep],
                                           dtype=torch.int32, device=DEV))
         g.replay()
         torch.cuda.synchronize()
@@ -1020,6 +1025,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(got, (bufs.idx, bufs.count, bufs.out, bufs.out_lse)):
             assert torch.equal(a, b), f"replay {rep} differs from eager"
+        assert not _hist_words(bufs.ws, bufs.rows).any(), "histograms left nonzero"
 
 
 @pytest.mark.parametrize("name,over", [
