@@ -5,11 +5,11 @@
 // for QSA attention and the sparse indexer": a sparse GQA call per block).
 //
 // One workgroup (8 waves for FP8 rows, 4 for 16-bit rows) per (request b,
-// KV head g, chunk c) handles the G
-// query heads of the group over the chunk's run of the ascending selection
-// list (every token 0 .. len-1 for a request at or below the sparse-decode
-// threshold), one tile of tokens at a time (128 tokens for FP8 rows, 64 for
-// 16-bit rows, so a tile's K and V fit LDS):
+// KV head g, chunk c) handles the G query heads of the group over the
+// chunk's run of the ascending selection list (every token 0 .. len-1 for a
+// request at or below the sparse-decode threshold), one tile of tokens at a
+// time (128 tokens for FP8 rows, 64 for 16-bit rows, so a tile's K and V
+// fit LDS):
 //   1. the tile's slots are resolved from the page table; an index outside
 //      [0, len) or a page outside [0, num_pages) is masked and never read;
 //   2. the K and V rows are gathered into LDS with 16-byte loads (a token's
@@ -21,9 +21,9 @@
 //   4. an online softmax (base 2) per head updates the running max and sum;
 //      the page's V scale is folded into the probabilities;
 //   5. O += P V on MFMA, each wave owning 128 / waves output dimensions of
-//      every head: for 16-bit caches on v_mfma_f32_16x16x32_{bf16,f16} with P as
-//      the sum of two 16-bit parts (within 2^-17 of P) and V as stored; for
-//      FP8 caches with P rounded once to bf16 and V widened exactly.
+//      every head: for 16-bit caches on v_mfma_f32_16x16x32_{bf16,f16} with
+//      P as the sum of two 16-bit parts (within 2^-17 of P) and V as stored;
+//      for FP8 caches with P rounded once to bf16 and V widened exactly.
 #include "device_common.h"
 #include "launch.h"
 
