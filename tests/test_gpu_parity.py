@@ -93,13 +93,16 @@ def test_qsa_stale_page_table_tail():
     _full_check(cfg)
 
 
-def test_qsa_invalid_pages_inside_rows_score_minus_inf():
+@pytest.mark.parametrize("first", [5000, 40000], ids=["short", "long"])
+def test_qsa_invalid_pages_inside_rows_score_minus_inf(first):
     """Page-table entries inside a row's length that are negative or past
     the pool: those tokens score -inf (the scan never reads them), every
     other score matches the oracle on the original table, and the fused
-    selection equals the top-k of those scores."""
+    selection equals the top-k of those scores (short rows: the
+    one-workgroup top-k; long rows: the in-scan digit-1 histogram, which
+    counts the -inf scores, then the filter and the resolve)."""
     import top_sparse_decode_amd as tsd
-    cfg = tsd_synth.config(QSA, B=2, lens=(5000, 300), top_k=256, chunks=4,
+    cfg = tsd_synth.config(QSA, B=2, lens=(first, 300), top_k=256, chunks=4,
                            seed=104)
     wl = tsd_synth.make(cfg, DEV)
     h = tsd_synth.to_host(wl)
@@ -137,12 +140,15 @@ def test_qsa_invalid_pages_inside_rows_score_minus_inf():
                          cnt.cpu().numpy())
 
 
-def test_qsa_empty_pool_scores_minus_inf():
+@pytest.mark.parametrize("first", [3000, 40000], ids=["short", "long"])
+def test_qsa_empty_pool_scores_minus_inf(first):
     """num_pages = 0: every token is on a page outside the pool, so every
     score is -inf and the selection is the first k tokens (lowest index
-    among equal scores); the pool is never read."""
+    among equal scores); the pool is never read. Long rows take the in-scan
+    digit-1 histogram (every score in one bin), the filter and the resolve,
+    whose ties at T are kept by index."""
     import top_sparse_decode_amd as tsd
-    cfg = tsd_synth.config(QSA, B=3, lens=(3000, 100, 0), top_k=128, chunks=2,
+    cfg = tsd_synth.config(QSA, B=3, lens=(first, 100, 0), top_k=128, chunks=2,
                            seed=105)
     wl = tsd_synth.make(cfg, DEV)
     B, k = cfg.B, cfg.top_k
