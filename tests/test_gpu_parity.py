@@ -80,6 +80,8 @@ DS7B = "ds_llama7b_b3_l20000_s200"
     ((2048, 700), 2048, 16),
     # 32 rows of a 4,096-page table: 64 pages per scan wave
     ((262144,) + tuple((i * 997) % 9000 for i in range(1, 32)), 256, 4),
+    # the largest k and chunk count the contract takes, on a chunked-top-k row
+    ((40000, 9000), 4096, 64),
 ])
 def test_qsa_decode_path(lens, k, C):
     cfg = tsd_synth.config(QSA, B=len(lens), lens=lens, top_k=k, chunks=C,
@@ -218,6 +220,8 @@ def test_qsa_causal_prefill_rows():
                 chunks=2)),
     (DS7B, dict(B=2, H_q=12, H_kv=12, lens=(9000, 130), top_k=300, chunks=5,
                 steps=0)),
+    # the largest k and chunk count, rows past the one-workgroup top-k
+    (DS8B, dict(B=2, lens=(40000, 5000), top_k=4096, chunks=64)),
 ])
 def test_ds_decode_path(name, over):
     cfg = tsd_synth.config(name, seed=111, **over)
