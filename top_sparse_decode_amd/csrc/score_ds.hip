@@ -23,6 +23,15 @@
 // qs sits in registers. A page's scores are staged in LDS and stored as 64
 // contiguous floats per (request, head) row.
 //
+// In the one-sub-block form, where each thread forms at most EC channels of the
+// group query from at most EG query heads (EC, EG = 1, 4 or 2, 1), the row
+// length, the thread's channel ids and the unit's page id are loaded
+// together; then the thread's query values at those channels, then the
+// unit's labels, all unconditional (clamped indices, masked at use). Loads
+// complete in order, so forming the group query waits for the query values
+// only and the labels are already in flight: the labels leave after one
+// dependent round trip instead of three (length, channels, query).
+//
 // ds_scan_kernel: the general form, one workgroup per page.
 #include "device_common.h"
 #include "launch.h"
@@ -120,7 +129,7 @@ constexpr int kSubVec = kThreads * 8;  // 16-byte vectors per sub-block
 // ONE: every workgroup streams a single unit, sub-block blockIdx.x % SB of
 // page blockIdx.x / SB (SB a power of two, so a unit holds 64 / SB whole
 // tokens), with no second register buffer, so more workgroups fit a CU.
-template <int VPI, bool QREG, bool ONE>
+template <int VPI, bool QREG, bool ONE, int EC, int EG>
 __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
     const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
     const int32_t* __restrict__ chan, int r,
@@ -140,15 +149,70 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
   const int64_t pp0 = ONE ? blockIdx.x / SB : static_cast<int64_t>(blockIdx.x) * P;
   const int sub0 = ONE ? static_cast<int>(blockIdx.x % SB) : 0;
   const int tpu = kPage / SB;                     // ONE: tokens of the unit
-  int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
+  constexpr bool EARLY = ONE && EC > 0;  // see the one-unit form above
+  uint4 xe[8];  // EARLY: the unit's labels, loaded in the prologue
+  int64_t n;
+  int npg = 1;
+  const int G = H_q / H_kv;
+  if constexpr (EARLY) {
+    const int32_t len_raw = seq_lens[b];
+    int32_t ch[EC];
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const int i = tid + j * kThreads;
+      ch[j] = chan[i < hc ? i : hc - 1];
+    }
+    const int32_t pe = page_table[static_cast<int64_t>(b) * pt_stride + pp0];
+    n = clamp_len(len_raw, pt_stride * kPage);
+    n = clamp_len(n, score_stride);
+    if (blockIdx.x == 0 && row_lens_out)
+      for (int g = tid; g < H_kv; g += kThreads)
+        row_lens_out[static_cast<int64_t>(b) * H_kv + g] = static_cast<int32_t>(n);
+    if (pp0 * kPage + sub0 * tpu >= n) return;  // uniform
+    uint16_t qraw[EC][EG];
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const int i0 = tid + j * kThreads;
+      const int i = i0 < hc ? i0 : hc - 1;
+      const int g = i / r;
+      const int c = ch[j] >= 0 && ch[j] < D ? ch[j] : 0;
+#pragma unroll
+      for (int h = 0; h < EG; ++h)
+        qraw[j][h] = q[(static_cast<int64_t>(b) * H_q + g * G + (h < G ? h : 0)) * D + c];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the labels are issued after the query
+    const bool pv = pe >= 0 && pe < num_pages;
+    const uint4* be = reinterpret_cast<const uint4*>(label) +
+                      static_cast<int64_t>(pv ? pe : 0) * VP;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int vv = sub0 * kSubVec + i * kThreads + tid;
+      vv = vv < VP ? vv : VP - 1;
+      const v4u tt = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(be + vv));
+      xe[i] = make_uint4(tt.x, tt.y, tt.z, tt.w);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < EC; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < hc) {
+        float acc = 0.f;
+        if (ch[j] >= 0 && ch[j] < D)
+          for (int h = 0; h < G; ++h) acc += half_to_f32(qraw[j][h], is_bf16);
+        qs[i] = acc;
+      }
+    }
+    if (tid == 0) pages_s[0] = pv ? pe : -1;
+    __syncthreads();
+  } else {
+  n = clamp_len(seq_lens[b], pt_stride * kPage);
   n = clamp_len(n, score_stride);
   if (blockIdx.x == 0 && row_lens_out)
     for (int g = tid; g < H_kv; g += kThreads)
       row_lens_out[static_cast<int64_t>(b) * H_kv + g] = static_cast<int32_t>(n);
   if (pp0 * kPage + sub0 * tpu >= n) return;  // uniform
   const int64_t left = (n - pp0 * kPage + kPage - 1) / kPage;
-  const int npg = ONE ? 1 : (left < P ? static_cast<int>(left) : P);
-  const int G = H_q / H_kv;
+  npg = ONE ? 1 : (left < P ? static_cast<int>(left) : P);
   for (int i = tid; i < hc; i += kThreads) {  // group query at the channels
     const int g = i / r;
     const int c = chan[i];
@@ -165,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
   }
   __syncthreads();
 
+  }
   const int units = ONE ? 1 : npg * SB;
   const int part = tid % VPI;                     // this lane's label vector
   float qr[8];  // QREG: this lane's slice of qs (head (tid / VPI) % H_kv)
@@ -214,7 +279,12 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
     }
   };
   uint4 xa[8];
-  load_unit(0, xa);
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xa[i] = xe[i];
+  } else {
+    load_unit(0, xa);
+  }
   if constexpr (QREG) {  // this lane always meets head (tid / VPI) % H_kv
     const int g = (tid / VPI) % H_kv;
 #pragma unroll
@@ -256,7 +326,13 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
 
 template <int VPI, bool QREG, bool ONE>
 void launch_vec3(const tsd_score_args& a, dim3 grid, size_t lds, int P, hipStream_t s) {
-  hipLaunchKernelGGL((ds_scan_vec_kernel<VPI, QREG, ONE>), grid, dim3(kThreads), lds, s,
+  // the early-label prologue where a thread's share of the group query is
+  // at most 1 channel x 4 heads or 2 channels x 1 head
+  const int hc = a.H_kv * a.r, G = a.H_q / a.H_kv;
+  auto kern = ds_scan_vec_kernel<VPI, QREG, ONE, 0, 0>;
+  if (ONE && hc <= 256 && G <= 4) kern = ds_scan_vec_kernel<VPI, QREG, ONE, 1, 4>;
+  else if (ONE && hc <= 512 && G <= 1) kern = ds_scan_vec_kernel<VPI, QREG, ONE, 2, 1>;
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s,
                      static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
                      a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
                      a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
