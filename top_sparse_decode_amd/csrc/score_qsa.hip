@@ -147,10 +147,33 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
   const bool row_ok = row < rows;
   const int chunk = wave - row * waves_per_row;
   const int b = row_ok ? row / rows_per_req : 0;
+  const int64_t page0 = static_cast<int64_t>(chunk) * G;
+  const int col = lane & 15;  // MFMA row (head) for A, column (key) for B
+  const int kb = lane >> 4;   // which 32-byte slice of the 128 dims
+  const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
 
+  // The row's length, the wave's page ids (lane l: page page0 + l, clamped
+  // inside the row's pt_stride entries; only those below the length are
+  // used), the row's index-query slice and its head weights are all loaded
+  // before the length is known, so the key loads wait for one round trip.
   int64_t n = 0;
+  int32_t pt_raw = -1;
+  v8i qa8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  float w[4] = {0.f, 0.f, 0.f, 0.f};
   if (row_ok) {
     n = seq_lens[b];
+    const int64_t pi = page0 + lane;
+    pt_raw = pt[pi < pt_stride ? pi : pt_stride - 1];
+    // A operand: index head `col` of this row (zero for padded heads);
+    // the weights of the 4 heads whose dots this lane receives
+    if (col < H_i)
+      qa8 = load_row_slice(
+          index_q + (static_cast<int64_t>(row) * H_i + col) * kDi, kb);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int h = 4 * kb + v;
+      w[v] = h < H_i ? index_w[static_cast<int64_t>(row) * H_i + h] : 0.f;
+    }
     if (q_pos) {
       const int64_t p1 = static_cast<int64_t>(q_pos[row]) + 1;
       n = p1 < n ? p1 : n;
@@ -160,7 +183,6 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     if (chunk == 0 && lane == 0 && row_lens_out)
       row_lens_out[row] = static_cast<int32_t>(n);
   }
-  const int64_t page0 = static_cast<int64_t>(chunk) * G;
   // live pages of this wave (the last one may be partial)
   int npg = 0;
   if (row_ok && page0 * kPage < n) {
@@ -177,28 +199,12 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
   }
 
   if (npg > 0) {
-    const int col = lane & 15;  // MFMA row (head) for A, column (key) for B
-    const int kb = lane >> 4;   // which 32-byte slice of the 128 dims
-
-    // A operand: index head `col` of this row (zero for padded heads).
-    v8i qa8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < H_i)
-      qa8 = load_row_slice(
-          index_q + (static_cast<int64_t>(row) * H_i + col) * kDi, kb);
     const Bf16Slice qa = widen_fp8(qa8);
-    // Weights of the 4 heads whose dots this lane receives.
-    float w[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int h = 4 * kb + v;
-      w[v] = h < H_i ? index_w[static_cast<int64_t>(row) * H_i + h] : 0.f;
-    }
-    const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
     float* res = res_s[wl];
     // every page id of the wave up front, lane l holding page l: a page-id
     // load inside the loop would make each wait on it also drain the other
     // register set's key loads (loads complete in order)
-    const int32_t my_page = lane < npg ? pt[page0 + lane] : -1;
+    const int32_t my_page = lane < npg ? pt_raw : -1;
 
     // loads of wave pages j, j+1. They are unconditional, so the compiler
     // knows how many loads follow the ones it waits for (loads complete in
