@@ -314,7 +314,8 @@ int topk_merge_sharded(const float *scores, int64_t stride,
  * Sparse-decode threshold ("Support double sparsity", Speedup Evaluation:
  * short contexts decode densely): a request whose length len (clamped to
  * pt_stride * 64) is at most dense_len attends to every token 0 .. len-1 as
- * its selection (m = len; idx and count are not read for it). dense_len = 0
+ * its selection (m = len; its idx entries and count are not used, though
+ * its row of idx, allocated like every other, may be loaded). dense_len = 0
  * turns this off.
  * Block selections (idx_block = Bs in {2, 4, ..., 64}; 0 or 1 = token
  * indices): idx row holds the first count ascending indices of selected

@@ -31,10 +31,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-# Every HIP source is compiled with packed-FP32 code generation disabled.
+# Every HIP source is compiled with packed-FP32 code generation disabled,
+# and with kernel-argument preloading: gfx950 loads the first kernel
+# arguments (up to 16 dwords, 14 here beside the argument-buffer pointer)
+# into scalar registers at wave launch, so a kernel's first memory loads
+# need not wait for a scalar load of the argument buffer (the kernels put
+# the arguments those loads need first). The code object keeps a prologue
+# that loads them itself where the firmware does not preload.
 DEVICE_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
                 "-Wall", "-Xclang", "-target-feature", "-Xclang",
-                "-packed-fp32-ops", "-I" + INCLUDE, "-I" + CSRC]
+                "-packed-fp32-ops", "-mllvm", "-amdgpu-kernarg-preload-count=16",
+                "-I" + INCLUDE, "-I" + CSRC]
 
 
 # Per-source extra flags. The index scans assume NaN-free scores (a NaN

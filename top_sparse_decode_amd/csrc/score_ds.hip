@@ -32,6 +32,9 @@
 // only and the labels are already in flight: the labels leave after one
 // dependent round trip instead of three (length, channels, query).
 //
+// The vector kernel's arguments that its first loads need come first, in
+// the 14 kernel-argument dwords the hardware preloads into scalar registers.
+//
 // ds_scan_kernel: the general form, one workgroup per page.
 #include "device_common.h"
 #include "launch.h"
@@ -131,12 +134,12 @@ constexpr int kSubVec = kThreads * 8;  // 16-byte vectors per sub-block
 // tokens), with no second register buffer, so more workgroups fit a CU.
 template <int VPI, bool QREG, bool ONE, int EC, int EG>
 __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
-    const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
-    const int32_t* __restrict__ chan, int r,
-    const uint16_t* __restrict__ label, const int32_t* __restrict__ page_table,
-    int64_t pt_stride, const int32_t* __restrict__ seq_lens,
-    int64_t num_pages, float* __restrict__ scores, int64_t score_stride,
-    int32_t* __restrict__ row_lens_out, int P) {
+    int H_kv, int r, int H_q, int D, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ chan, const int32_t* __restrict__ page_table,
+    int64_t pt_stride, int P, bool is_bf16, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ label, int64_t num_pages,
+    float* __restrict__ scores, int64_t score_stride,
+    int32_t* __restrict__ row_lens_out) {
   extern __shared__ __align__(16) float dyn_s[];
   const int hc = H_kv * r;
   float* qs = dyn_s;                              // [hc]
@@ -332,11 +335,11 @@ void launch_vec3(const tsd_score_args& a, dim3 grid, size_t lds, int P, hipStrea
   auto kern = ds_scan_vec_kernel<VPI, QREG, ONE, 0, 0>;
   if (ONE && hc <= 256 && G <= 4) kern = ds_scan_vec_kernel<VPI, QREG, ONE, 1, 4>;
   else if (ONE && hc <= 512 && G <= 1) kern = ds_scan_vec_kernel<VPI, QREG, ONE, 2, 1>;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s,
-                     static_cast<const uint16_t*>(a.q), a.q_dtype == TSD_BF16, a.H_q, a.H_kv,
-                     a.D, a.channel_idx, a.r, static_cast<const uint16_t*>(a.label_pool),
-                     a.page_table, a.pt_stride, a.seq_lens, a.num_pages, a.scores,
-                     a.score_stride, a.row_lens_out, P);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a.H_kv, a.r, a.H_q,
+                     a.D, a.seq_lens, a.channel_idx, a.page_table, a.pt_stride, P,
+                     a.q_dtype == TSD_BF16, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.label_pool), a.num_pages,
+                     a.scores, a.score_stride, a.row_lens_out);
 }
 
 // Runs of P pages per workgroup, P for about 1,536 workgroups or more; where

@@ -129,15 +129,20 @@ TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
 // workgroup, flushed with integer atomics). The launch then gives each row
 // a multiple of 4 waves so that a workgroup never spans two rows, and no
 // wave leaves before the barriers.
+//
+// The arguments that the first loads' addresses need come first: they fill
+// the 14 kernel-argument dwords the hardware preloads into scalar registers,
+// so those loads leave without waiting for the argument buffer.
 template <int G, bool HIST>
 __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
-    const uint8_t* __restrict__ index_q, const float* __restrict__ index_w,
-    const uint8_t* __restrict__ index_k, const int32_t* __restrict__ page_table,
-    int64_t pt_stride, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ q_pos, int64_t num_pages, int rows,
-    int rows_per_req, int H_i, int waves_per_row, float* __restrict__ scores,
-    int64_t score_stride, int32_t* __restrict__ row_lens_out,
-    void* __restrict__ topk_base, int hist_k) {
+    int rows, int rows_per_req, int H_i, int waves_per_row,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_table,
+    int64_t pt_stride, const uint8_t* __restrict__ index_q,
+    const float* __restrict__ index_w, const uint8_t* __restrict__ index_k,
+    const int32_t* __restrict__ q_pos, int64_t num_pages,
+    float* __restrict__ scores, int64_t score_stride,
+    int32_t* __restrict__ row_lens_out, void* __restrict__ topk_base,
+    int hist_k) {
   static_assert(G % 4 == 0 && G <= kWave, "pages per wave: one page id per lane");
   __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
   __shared__ float res_s[kWavesPerBlock][G * kPage];
@@ -540,10 +545,10 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                     kWavesPerBlock;
   const int64_t waves = waves_per_row * rows;
   const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  using Kern = void (*)(const uint8_t*, const float*, const uint8_t*,
-                        const int32_t*, int64_t, const int32_t*,
-                        const int32_t*, int64_t, int, int, int, int, float*,
-                        int64_t, int32_t*, void*, int);
+  using Kern = void (*)(int, int, int, int, const int32_t*, const int32_t*,
+                        int64_t, const uint8_t*, const float*, const uint8_t*,
+                        const int32_t*, int64_t, float*, int64_t, int32_t*,
+                        void*, int);
   Kern kern;
   if (topk_ws)
     kern = G == 64 ? qsa_scan_kernel<64, true>
@@ -556,10 +561,10 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
          : G == 16 ? qsa_scan_kernel<16, false>
          : G == 8  ? qsa_scan_kernel<8, false> : qsa_scan_kernel<4, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(kWavesPerBlock * kWave), 0, s, a.index_q, a.index_w,
-                     a.index_k_pool, a.page_table, a.pt_stride, a.seq_lens,
-                     a.q_pos, a.num_pages, rows, a.rows_per_req, a.H_i,
-                     static_cast<int>(waves_per_row), a.scores,
+                     dim3(kWavesPerBlock * kWave), 0, s, rows, a.rows_per_req,
+                     a.H_i, static_cast<int>(waves_per_row), a.seq_lens,
+                     a.page_table, a.pt_stride, a.index_q, a.index_w,
+                     a.index_k_pool, a.q_pos, a.num_pages, a.scores,
                      a.score_stride, a.row_lens_out, topk_ws, hist_k);
   return hipGetLastError();
 }

@@ -114,16 +114,19 @@ TSD_DEVICE v4f mfma_qk(uint4 a, uint4 b, v4f c) {
   }
 }
 
+// The arguments that the first loads' addresses need come first: they fill
+// the 14 kernel-argument dwords the hardware preloads into scalar registers,
+// so those loads leave without waiting for the argument buffer.
 template <int ENC, bool QBF>
 __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
-    const uint16_t* __restrict__ q, int H_q, int H_kv,
-    const uint8_t* __restrict__ k_pool, const uint8_t* __restrict__ v_pool,
-    const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    const int32_t* __restrict__ page_table, int64_t pt_stride,
-    const int32_t* __restrict__ seq_lens, int64_t num_pages,
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ count,
-    int H_sel, int k, int C, float softmax_scale, float* __restrict__ o_part,
-    float* __restrict__ lse_part, int dense_len, int lbs) {
+    int H_q, int H_kv, int H_sel, int k, int C, int lbs,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ count, const uint16_t* __restrict__ q,
+    int64_t pt_stride, const int32_t* __restrict__ page_table,
+    int64_t num_pages, const uint8_t* __restrict__ k_pool,
+    const uint8_t* __restrict__ v_pool, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, float softmax_scale, int dense_len,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
   using T = Tile<ENC>;
   constexpr int NT = T::kTokens;
   constexpr int kThreads = T::kThreads, kWavesW = T::kWaves;
@@ -146,11 +149,9 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
   // sel[p >> lbs] * 2^lbs + p % 2^lbs (only a last block can be partial).
   // The chunk bounds depend on the selection's length m, which is the full
   // capacity for every row long enough: the first tile's entries for that m
-  // are loaded together with the count (and, for blocks, the last entry) and
-  // kept wherever they match the real bounds.
-  const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
-  // at or below the sparse-decode threshold the selection is every token
-  const bool dense = n <= dense_len;
+  // (and, for blocks, the last entry) are loaded together with the length
+  // and the count, from the request's row of idx (allocated for every
+  // request), and kept wherever they match the real bounds.
   const int bsz = 1 << lbs;
   const int64_t cap = static_cast<int64_t>(k) << lbs;  // capacity in tokens
   auto token_at = [&](int64_t p) -> int64_t {
@@ -160,8 +161,11 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
   const int64_t lo_s = c * cap / C;
   const int64_t hi_s = (c + 1) * cap / C;
   int64_t t_spec = -1;
-  if (!dense && tid < NT && lo_s + tid < hi_s) t_spec = token_at(lo_s + tid);
-  const int32_t last_spec = (lbs > 0 && !dense) ? sel[k - 1] : -1;
+  if (tid < NT && lo_s + tid < hi_s) t_spec = token_at(lo_s + tid);
+  const int32_t last_spec = lbs > 0 ? sel[k - 1] : -1;
+  const int64_t n = clamp_len(seq_lens[b], pt_stride * kPage);
+  // at or below the sparse-decode threshold the selection is every token
+  const bool dense = n <= dense_len;
   int64_t m = n;
   if (!dense) {
     const int64_t cnt = clamp_len(count[static_cast<int64_t>(b) * H_sel + srow], k);
@@ -437,14 +441,15 @@ template <int ENC, bool QBF>
 hipError_t launch_enc(const tsd_attn_args& a, hipStream_t s) {
   dim3 grid(static_cast<uint32_t>(a.chunks), static_cast<uint32_t>(a.H_kv),
             static_cast<uint32_t>(a.B));
+  const int lbs = a.idx_block > 1 ? __builtin_ctz(static_cast<unsigned>(a.idx_block)) : 0;
   hipLaunchKernelGGL((sparse_gqa_kernel<ENC, QBF>), grid, dim3(Tile<ENC>::kThreads), 0,
-                     s, static_cast<const uint16_t*>(a.q), a.H_q, a.H_kv,
+                     s, a.H_q, a.H_kv, a.H_sel, a.k, a.chunks, lbs, a.idx,
+                     a.seq_lens, a.count, static_cast<const uint16_t*>(a.q),
+                     a.pt_stride, a.page_table, a.num_pages,
                      static_cast<const uint8_t*>(a.k_pool),
                      static_cast<const uint8_t*>(a.v_pool), a.k_scale,
-                     a.v_scale, a.page_table, a.pt_stride, a.seq_lens,
-                     a.num_pages, a.idx, a.count, a.H_sel, a.k, a.chunks,
-                     a.softmax_scale, a.o_part, a.lse_part, a.dense_len,
-                     a.idx_block > 1 ? __builtin_ctz(static_cast<unsigned>(a.idx_block)) : 0);
+                     a.v_scale, a.softmax_scale, a.dense_len, a.o_part,
+                     a.lse_part);
   return hipGetLastError();
 }
 
