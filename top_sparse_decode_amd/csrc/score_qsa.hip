@@ -146,7 +146,10 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
   static_assert(G % 4 == 0 && G <= kWave, "pages per wave: one page id per lane");
   __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
   __shared__ float res_s[kWavesPerBlock][G * kPage];
-  const int lane = threadIdx.x & (kWave - 1), wl = threadIdx.x >> 6;
+  const int lane = threadIdx.x & (kWave - 1);
+  // the wave's index is uniform: held in scalar registers, so the row and
+  // request divisions run once per wave on the scalar unit
+  const int wl = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave = blockIdx.x * kWavesPerBlock + wl;
   const int row = wave / waves_per_row;
   const bool row_ok = row < rows;

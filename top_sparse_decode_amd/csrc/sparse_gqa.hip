@@ -153,13 +153,14 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
   // and the count, from the request's row of idx (allocated for every
   // request), and kept wherever they match the real bounds.
   const int bsz = 1 << lbs;
-  const int64_t cap = static_cast<int64_t>(k) << lbs;  // capacity in tokens
+  // capacity in tokens, at most 4,096 * 64, so (c + 1) * cap fits 32 bits
+  const int cap = k << lbs;
   auto token_at = [&](int64_t p) -> int64_t {
     if (lbs == 0) return sel[p];
     return static_cast<int64_t>(sel[p >> lbs]) * bsz + (p & (bsz - 1));
   };
-  const int64_t lo_s = c * cap / C;
-  const int64_t hi_s = (c + 1) * cap / C;
+  const int lo_s = c * cap / C;
+  const int hi_s = (c + 1) * cap / C;
   int64_t t_spec = -1;
   if (tid < NT && lo_s + tid < hi_s) t_spec = token_at(lo_s + tid);
   const int32_t last_spec = lbs > 0 ? sel[k - 1] : -1;
@@ -176,7 +177,15 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
       m -= over < 0 ? 0 : (over > bsz ? bsz : over);
     }
   }
-  const int64_t lo = c * m / C, hi = (c + 1) * m / C;
+  int64_t lo, hi;
+  if (m <= (1 << 24)) {  // 32-bit division whenever (c + 1) * m fits
+    const int mi = static_cast<int>(m);
+    lo = c * mi / C;
+    hi = (c + 1) * mi / C;
+  } else {
+    lo = c * m / C;
+    hi = (c + 1) * m / C;
+  }
   const int32_t* pt = page_table + static_cast<int64_t>(b) * pt_stride;
   const float zscale = softmax_scale * kLog2e;
 
