@@ -442,6 +442,26 @@ def test_topk_one_workgroup_rows(max_len, k):
     np.testing.assert_array_equal(gidx, ridx)
 
 
+@pytest.mark.parametrize("c", [10000, 16388, 16389, 19000])
+def test_topk_one_workgroup_crowded_digit1_bin(c):
+    """One-workgroup rows whose k-th largest key lies in a digit-1 bin of
+    thousands of keys: c entries tie at 1.0 (one digit-1 bin) and the rest
+    lie above it (c = 10,000 leaves the k-th largest among them); the
+    second row's length cuts three entries. Against the oracle."""
+    rng = np.random.default_rng(c)
+    L, k = 20000, 4000
+    rows = 2
+    s = np.empty((rows, L), np.float32)
+    for r in range(rows):
+        s[r] = 2.0 + rng.random(L).astype(np.float32)
+        s[r, rng.permutation(L)[:c]] = 1.0
+    lens = [L, L - 3]
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(s, lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+
+
 def test_topk_one_workgroup_rows_clear_an_unflagged_workspace():
     """The one-workgroup path reads no workspace, yet an unflagged call still
     leaves the histogram words zero for the flagged calls that follow."""
