@@ -843,6 +843,21 @@ def test_dense_threshold_requests_attend_to_every_token(name, lens, dense_len):
                        bufs.lse_part.cpu().numpy(), out_tol(cfg.kv_enc))
     check_merge(bufs.o_part.cpu().numpy(), bufs.lse_part.cpu().numpy(),
                 bufs.out.cpu().numpy(), bufs.out_lse.cpu().numpy())
+    # a dense request's idx row may be loaded but is never used: garbage
+    # entries and counts there leave every partial bit for bit unchanged
+    import top_sparse_decode_amd.step as step
+    o0, l0 = bufs.o_part.clone(), bufs.lse_part.clone()
+    iv = bufs.idx.view(cfg.B, H_sel, cfg.top_k)
+    cv = bufs.count.view(cfg.B, H_sel)
+    for b, n in enumerate(lens):
+        if n <= dense_len:
+            iv[b] = torch.randint(-2 ** 31, 2 ** 31 - 1, iv[b].shape,
+                                  dtype=torch.int32, device=DEV)
+            cv[b] = 123457
+    step.attend(wl, bufs)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.o_part, o0)
+    assert torch.equal(bufs.lse_part, l0)
 
 
 # ------------------------------------------------------------ cache append
