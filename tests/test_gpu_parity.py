@@ -571,6 +571,37 @@ def test_merge_sharded_matches_unsharded_topk(W):
     np.testing.assert_array_equal(idx.cpu().numpy(), midx)
 
 
+def test_merge_sharded_sixteen_shards_and_unordered_lists():
+    """W = 16 shards of k = kl = 1,024 candidates (the most a row takes),
+    with ties: the merge of the shard top-k lists equals the oracle merge;
+    the same lists with their entries shuffled (not ascending, as
+    topk_select never writes them) give the same result."""
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(47)
+    W, rows, L, k = 16, 2, 6000, 1024
+    S = (rng.integers(0, 300, size=(W, rows, L)) / 300).astype(np.float32)
+    lens = np.full((W, rows), L, np.int32)
+    lens[3, 1] = 700  # a short shard: fewer than k candidates
+    Sg = torch.from_numpy(S).to(DEV)
+    il, cl = gpu_topk_stack(Sg, torch.from_numpy(lens).to(DEV), k)
+    midx, mcnt = oracle.topk_merge_sharded(S, il.cpu().numpy(), cl.cpu().numpy(), k)
+    for shuffle in (False, True):
+        if shuffle:
+            g = torch.Generator(device="cpu").manual_seed(5)
+            ilh = il.cpu()
+            for w in range(W):
+                for r in range(rows):
+                    c = int(cl[w, r])
+                    ilh[w, r, :c] = ilh[w, r, :c][torch.randperm(c, generator=g)]
+            il = ilh.to(DEV)
+        idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+        cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+        tsd.topk_merge_sharded(Sg, il, cl, k, idx, cnt)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(cnt.cpu().numpy(), mcnt)
+        np.testing.assert_array_equal(idx.cpu().numpy(), midx)
+
+
 def test_merge_sharded_short_lists_and_bad_entries():
     import top_sparse_decode_amd as tsd
     # hand-made candidate lists: counts below kl, -1 and out-of-range
