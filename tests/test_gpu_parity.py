@@ -442,6 +442,25 @@ def test_topk_one_workgroup_rows(max_len, k):
     np.testing.assert_array_equal(gidx, ridx)
 
 
+def test_topk_filter_runs_several_passes_per_workgroup():
+    """100 rows in a buffer of 1,048,576 entries: the filter's launch would
+    exceed 1,024 workgroups, so each workgroup walks 8 passes of 4 chunks
+    (two passes' scores in flight); rows of 30,000-150,000 entries end
+    inside a workgroup's passes, one row fills the buffer. Ties at the
+    threshold from 5,000 levels. Against the oracle."""
+    rng = np.random.default_rng(311)
+    rows, L, k = 100, 1 << 20, 2048
+    lens = rng.integers(30000, 150000, size=rows).tolist()
+    lens[37] = L
+    s = np.full((rows, L), np.nan, np.float32)
+    for r, n in enumerate(lens):
+        s[r, :n] = rng.integers(0, 5000, size=n) / 5000
+    gidx, gcnt = _topk_gpu(s, lens, k)
+    ridx, rcnt = oracle.topk(np.nan_to_num(s, nan=0.0), lens, k)
+    np.testing.assert_array_equal(gcnt, rcnt)
+    np.testing.assert_array_equal(gidx, ridx)
+
+
 @pytest.mark.parametrize("c", [10000, 16388, 16389, 19000])
 def test_topk_one_workgroup_crowded_digit1_bin(c):
     """One-workgroup rows whose k-th largest key lies in a digit-1 bin of
