@@ -128,10 +128,13 @@ __global__ __launch_bounds__(kThreads) void topk_hist1_kernel(
 // Pass 2: survivors (digit 1 >= b1) compacted in index order into each
 // chunk's list; digit-2 histogram of the candidates (digit 1 == b1).
 // A workgroup of 16 waves takes FC consecutive chunks per pass (16/FC
-// waves per chunk) and `passes` consecutive passes: FC = 2 while the
-// launch stays within about 1,024 workgroups (twice the workgroups of
-// FC = 4, 1.6 us faster on 8 rows of 262,144), else FC = 4 (fewer, longer
-// passes: 0.3 ms faster on 2,048 rows of a million). It
+// waves per chunk) and `passes` consecutive passes: FC = 1 while one chunk
+// per workgroup keeps the launch within 256 workgroups, one per CU (1.6 us
+// faster on one row of 1,048,576; at 512 workgroups, 8 rows of 262,144, it
+// is 2.3 us slower than FC = 2), FC = 2 while the launch stays within about
+// 1,024 workgroups (twice the workgroups of FC = 4, 1.6 us faster on 8 rows
+// of 262,144), else FC = 4 (fewer, longer passes: 0.3 ms faster on 2,048
+// rows of a million). It
 // resolves b1 itself from the row's H1 (one uint4 run of 4 bins per thread,
 // read while its first scores are in flight); the row's first workgroup
 // records (b1, above) for pass 3. Survivors are counted by ballots, the
@@ -886,13 +889,15 @@ hipError_t launch_topk_finish(const float* scores, int64_t stride, int rows,
                               int32_t* idx, int32_t* count, void* ws,
                               hipStream_t s) {
   const int nch = nch_for(max_len);
-  const int fc = filter_passes(nch, rows, 2) == 1 ? 2 : 4;
+  const int fc = static_cast<int64_t>(nch) * rows <= 256 ? 1
+                 : filter_passes(nch, rows, 2) == 1 ? 2 : 4;
   const int passes = filter_passes(nch, rows, fc);
   const int64_t cap = max_len < stride ? max_len : stride;
   const int64_t per_row = (nch + fc - 1) / fc;
   dim3 grid(static_cast<uint32_t>((per_row + passes - 1) / passes),
             static_cast<uint32_t>(rows));
-  hipLaunchKernelGGL(fc == 2 ? topk_filter_kernel<2> : topk_filter_kernel<4>, grid,
+  hipLaunchKernelGGL(fc == 1 ? topk_filter_kernel<1>
+                     : fc == 2 ? topk_filter_kernel<2> : topk_filter_kernel<4>, grid,
                      dim3(kFT), 0, s, scores, stride, row_lens, cap, k, nch,
                      passes, ws);
   const BlindPlan bp = blind_plan(nch, k, max_len);
