@@ -269,15 +269,19 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
       *reinterpret_cast<uint4*>(v_s + T::vrow(j) + 16 * v) = vx[it];
     }
     __syncthreads();
-    // 3. logits on MFMA: wave owns tokens [16*kBlocks*wave, +16*kBlocks)
+    // 3. logits on MFMA: wave owns tokens [16*kBlocks*wave, +16*kBlocks);
+    // a block wholly past the tile's tokens skips its MFMAs (a uniform
+    // branch) and only writes -inf
 #pragma unroll
     for (int blk = 0; blk < T::kBlocks; ++blk) {
       const int t0 = 16 * (T::kBlocks * wave + blk);
       const uint8_t* krow = k_s + (t0 + col) * T::kPitch;
       v4f s = {0.f, 0.f, 0.f, 0.f};
+      if (t0 < tn) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        s = mfma_qk<QBF>(qa[st], k8_as_q<ENC, QBF>(krow, 32 * grp + 8 * st), s);
+        for (int st = 0; st < 4; ++st)
+          s = mfma_qk<QBF>(qa[st], k8_as_q<ENC, QBF>(krow, 32 * grp + 8 * st), s);
+      }
       const int t = t0 + col;
       const bool live = t < tn && slot_s[t] >= 0;
       const float f = zscale * ks_s[t];
@@ -339,6 +343,7 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
       // (tokens x dims); lane group grp supplies tokens 8*grp .. 8*grp+7
 #pragma unroll
       for (int ks = 0; ks < NT / 32; ++ks) {
+        if (32 * ks >= tn) break;  // uniform: only zero probabilities left
         const int t0 = 32 * ks + 8 * grp;
         v8bf pa;
         if (arow) {
@@ -377,6 +382,7 @@ __global__ __launch_bounds__(Tile<ENC>::kThreads) void sparse_gqa_kernel(
       // 8*grp .. 8*grp+7
 #pragma unroll
       for (int ks = 0; ks < NT / 32; ++ks) {
+        if (32 * ks >= tn) break;  // uniform: only zero probabilities left
         const int t0 = 32 * ks + 8 * grp;
         uint4 ph = make_uint4(0u, 0u, 0u, 0u), pl = make_uint4(0u, 0u, 0u, 0u);
         if (arow) {
