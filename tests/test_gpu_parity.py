@@ -1028,10 +1028,15 @@ def test_topk_row_lens_clamped_to_max_len():
 
 
 # ----------------------------------------------------------- merge and misc
-def test_lse_merge_random_partials():
+@pytest.mark.parametrize("C,D", [(64, 128), (16, 128), (5, 128), (17, 128),
+                                 (24, 100), (33, 200), (63, 128)])
+def test_lse_merge_random_partials(C, D):
+    """Both merge forms (up to 16 chunks: one workgroup per row; more: one
+    wave per 16 output dimensions), ragged chunk groups and dimensions,
+    chunks and a whole row at lse = -inf, against the oracle merge."""
     import top_sparse_decode_amd as tsd
-    rng = np.random.default_rng(3)
-    rows, C, D = 70, 64, 128
+    rng = np.random.default_rng(3 + C + D)
+    rows = 70
     o = rng.normal(size=(rows, C, D)).astype(np.float32)
     lse = (rng.normal(size=(rows, C)) * 5).astype(np.float32)
     lse[rng.random((rows, C)) < 0.3] = -np.inf
