@@ -45,9 +45,9 @@
  *   - Lengths and indices live in device memory, so kernels bound every
  *     access themselves: a length is clamped to what the host arguments can
  *     hold (pt_stride * 64 tokens, score_stride / max_len entries); page-table
- *     entries at or past ceil(len / 64) are never used (a scan may load one
+ *     entries at or past ceil(len / 64) are never used (a scan may load any
  *     of the row's pt_stride entries before the length arrives, but never
- *     the page it names), so stale tails are fine; a page id outside
+ *     the pages they name), so stale tails are fine; a page id outside
  *     [0, num_pages) or a selected index outside [0, len) is skipped rather
  *     than dereferenced (that data is a caller error and its contribution
  *     is dropped).
