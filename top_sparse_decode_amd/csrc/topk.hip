@@ -692,8 +692,10 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(
 // which there are at least as many as are kept, so none is kept. Rounds
 // wholly past the row are skipped (a uniform branch).
 // Digit 1 is counted in four copies of the histogram, lane l adding to copy
-// l % 4, each copy starting one bank after the previous, so lanes of one
-// wave that share a bin mostly update different words.
+// l % 4, each copy starting four banks after the previous (a 16-byte
+// aligned pitch, so the pick reads a thread's 4 bins of a copy with one
+// 16-byte load instead of four strided words), so lanes of one wave that
+// share a bin mostly update different words.
 template <int RPT>
 __global__ __launch_bounds__(kRT) void topk_small_kernel(
     const float* __restrict__ scores, int64_t stride,
@@ -702,10 +704,10 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   constexpr int kWavesR = kRT / kWave;
   constexpr int kBlocks = RPT * kWavesR;  // (round, wave) blocks
   constexpr int kCopies = 4;
-  constexpr int kCopyPitch = kBins1 + 1;
+  constexpr int kCopyPitch = kBins1 + 4;
   static_assert(kBlocks <= kRT, "one block count per thread");
   static_assert(kBins1 == 4 * kRT && kBins2 == kRT && kBins3 == kRT, "bins");
-  __shared__ uint32_t h1[kCopies * kCopyPitch];
+  __shared__ __align__(16) uint32_t h1[kCopies * kCopyPitch];
   __shared__ __align__(16) uint32_t h2[kBins2];
   __shared__ __align__(16) uint32_t h3[kBins3];
   __shared__ uint32_t cnt_s[kBlocks];  // (ties << 16 | above) per block
@@ -765,14 +767,16 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   __syncthreads();
   BinPick p1;
   {
-    uint32_t h[kBins1 / kRT];  // this thread's run of bins, from the top down
-    const int base = kBins1 - (tid + 1) * (kBins1 / kRT);
+    static_assert(kBins1 / kRT == 4, "one 16-byte run of bins per thread and copy");
+    uint32_t h[4] = {0u, 0u, 0u, 0u};  // this thread's run of bins, from the top down
+    const int base = kBins1 - (tid + 1) * 4;
 #pragma unroll
-    for (int j = 0; j < kBins1 / kRT; ++j) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int q = 0; q < kCopies; ++q) c += h1[q * kCopyPitch + base + kBins1 / kRT - 1 - j];
-      h[j] = c;
+    for (int q = 0; q < kCopies; ++q) {
+      const uint4 x = *reinterpret_cast<const uint4*>(h1 + q * kCopyPitch + base);
+      h[0] += x.w;
+      h[1] += x.z;
+      h[2] += x.y;
+      h[3] += x.x;
     }
     p1 = pick_bin_runs<kBins1, kRT>(h, static_cast<uint32_t>(k), lds, &pick);
   }
