@@ -780,7 +780,6 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
     }
     p1 = pick_bin_runs<kBins1, kRT>(h, static_cast<uint32_t>(k), lds, &pick);
   }
-  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   {
     const int nr2 = rounds();
 #pragma unroll
@@ -820,6 +819,11 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   __syncthreads();
   const int pbl = lane < RPT ? static_cast<int>(cnt_s[lane * kWavesR + wave]) : 0;
   const int nr5 = rounds();
+  // set lanes of a wave mask below this lane
+  auto below = [](uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+  };
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     if (r >= nr5) continue;
@@ -827,11 +831,13 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
     const uint32_t gb = pb & 0xffffu, qb = pb >> 16;
     const bool gt = key[r] > T, eq = key[r] == T;
     const uint64_t me = __ballot(eq);
-    const uint32_t rank = qb + static_cast<uint32_t>(__popcll(me & lt));
-    const bool kept = gt || (eq && rank < need);
-    const uint64_t mk = __ballot(kept);
-    const uint32_t p = gb + (qb < need ? qb : need) +
-                       static_cast<uint32_t>(__popcll(mk & lt));
+    bool kept = gt;
+    uint64_t mk = __ballot(gt);
+    if (me != 0) {  // uniform; ties at T in this block (rare)
+      kept = gt || (eq && qb + below(me) < need);
+      mk = __ballot(kept);
+    }
+    const uint32_t p = gb + (qb < need ? qb : need) + below(mk);
     if (kept && p < static_cast<uint32_t>(k)) out[p] = r * kRT + tid;
   }
   if (tid == 0 && count) count[row] = k;
