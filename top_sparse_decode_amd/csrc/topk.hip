@@ -803,13 +803,17 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   // counts above T and at T of every (round, wave) block, packed as
   // (ties << 16 | above) and scanned once: both totals are at most
   // n <= 32,768, so the low field never carries into the high one
+  // lane r of `packed` collects round r's counts, so the wave stores them
+  // with one LDS write
   const int nr4 = rounds();
+  uint32_t packed = 0u;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const uint32_t g = static_cast<uint32_t>(__popcll(__ballot(key[r] > T)));
     const uint32_t q = static_cast<uint32_t>(__popcll(__ballot(key[r] == T)));
-    if (lane == 0) cnt_s[r * kWavesR + wave] = r < nr4 ? (q << 16) | g : 0u;
+    packed = lane == r ? (r < nr4 ? (q << 16) | g : 0u) : packed;
   }
+  if (lane < RPT) cnt_s[lane * kWavesR + wave] = packed;
   __syncthreads();
   {
     const uint32_t v = tid < kBlocks ? cnt_s[tid] : 0u;
@@ -819,6 +823,11 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
   __syncthreads();
   const int pbl = lane < RPT ? static_cast<int>(cnt_s[lane * kWavesR + wave]) : 0;
   const int nr5 = rounds();
+  // T again, opaque to the compiler: the comparisons below are recomputed
+  // instead of keeping the counting pass's 2 * RPT wave masks live across
+  // the scan (they spill)
+  uint32_t Tp = T;
+  asm volatile("" : "+v"(Tp));
   // set lanes of a wave mask below this lane
   auto below = [](uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -829,7 +838,7 @@ __global__ __launch_bounds__(kRT) void topk_small_kernel(
     if (r >= nr5) continue;
     const uint32_t pb = static_cast<uint32_t>(__builtin_amdgcn_readlane(pbl, r));
     const uint32_t gb = pb & 0xffffu, qb = pb >> 16;
-    const bool gt = key[r] > T, eq = key[r] == T;
+    const bool gt = key[r] > Tp, eq = key[r] == Tp;
     const uint64_t me = __ballot(eq);
     bool kept = gt;
     uint64_t mk = __ballot(gt);
