@@ -44,8 +44,38 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxHeadChan = 4096;  // H_kv * r held in LDS
-constexpr int kMaxScoreLds = 64 * 128;
+// Scores staged in LDS as [head][token] rows of kScPitch floats: the
+// lanes of one wave store one token's scores of many heads, which a
+// 64-float pitch would put in one bank (a many-way conflict); 65 spreads
+// them over distinct banks.
+constexpr int kScPitch = kPage + 1;
+constexpr int kMaxScoreLds = kScPitch * 128;
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+template <bool B>
+struct Bool {
+  static constexpr bool value = B;
+};
+
+// Sum over aligned groups of N lanes (N a power of two, at most 16) by DPP
+// moves: quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row
+// mirrors (after the quad steps the 4 lanes of a quad hold equal values, so
+// a mirror pairs every lane with an equal partner in the other half). Each
+// lane adds its partner's value to its own, as a lane exchange would.
+template <int CTRL>
+TSD_DEVICE float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+template <int N>
+TSD_DEVICE float group_sum(float v) {
+  static_assert(N >= 1 && N <= 16 && (N & (N - 1)) == 0, "group size");
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);
+  if constexpr (N >= 16) v += dpp_mov<0x140>(v);
+  return v;
+}
 
 __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
     const uint16_t* __restrict__ q, bool is_bf16, int H_q, int H_kv, int D,
@@ -104,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
                    half_to_f32(static_cast<uint16_t>(wds[e] >> 16), is_bf16);
           }
         }
-        sc[g * kPage + it / H_kv] = acc;
+        sc[g * kScPitch + it / H_kv] = acc;
       }
     } else {
       for (int it = threadIdx.x; it < items; it += kThreads) {
@@ -113,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
         const float* qg = qs + g * r;
         float acc = 0.f;
         for (int j = 0; j < r; ++j) acc += qg[j] * half_to_f32(src[j], is_bf16);
-        sc[g * kPage + it / H_kv] = acc;
+        sc[g * kScPitch + it / H_kv] = acc;
       }
     }
   }
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void ds_scan_kernel(
     const int64_t t = p * kPage + s;
     if (t < n)
       scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] =
-          valid ? sc[it] : -__builtin_inff();
+          valid ? sc[g * kScPitch + s] : -__builtin_inff();
   }
 }
 
@@ -143,8 +173,8 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
   extern __shared__ __align__(16) float dyn_s[];
   const int hc = H_kv * r;
   float* qs = dyn_s;                              // [hc]
-  float* sc = dyn_s + hc;                         // [2][64 * H_kv]
-  int32_t* pages_s = reinterpret_cast<int32_t*>(sc + 2 * kPage * H_kv);  // [P]
+  float* sc = dyn_s + hc;                         // [2][H_kv][kScPitch]
+  int32_t* pages_s = reinterpret_cast<int32_t*>(sc + 2 * kScPitch * H_kv);  // [P]
   const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int VP = 8 * hc;                          // vectors per page
@@ -250,21 +280,33 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
       x[i] = make_uint4(t.x, t.y, t.z, t.w);
     }
   };
-  auto sum_unit = [&](int u, const uint4 (&x)[8]) {
+  // A vector's (token, head) item is vv / VPI, head fastest; a lane's
+  // successive vectors lie kThreads / VPI items apart, so its head and token
+  // follow from its first item by a uniform step and a carry (no division
+  // per vector). The 16-bit type is fixed per call (BF), not per element.
+  constexpr int kIpv = kThreads / VPI;
+  const int dg = kIpv % H_kv, dt = kIpv / H_kv;
+  auto sum_unit = [&](auto bf, int u, const uint4 (&x)[8]) {
+    constexpr bool BF = decltype(bf)::value;
     const int pg = ONE ? 0 : u / SB, sub = ONE ? sub0 : u - pg * SB;
     const bool ok = pages_s[pg] >= 0;
-    float* scp = sc + (pg & 1) * kPage * H_kv;
+    float* scp = sc + (pg & 1) * kScPitch * H_kv;
+    const int it0 = (sub * kSubVec + tid) / VPI;
+    int g = it0 % H_kv, tok = it0 / H_kv;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int vv = sub * kSubVec + i * kThreads + tid;
-      const int item = vv / VPI;                  // (slot, head), head fastest
-      const int g = item % H_kv;
       float w[8];
       const uint32_t wd[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        w[2 * e] = half_to_f32(static_cast<uint16_t>(wd[e] & 0xFFFF), is_bf16);
-        w[2 * e + 1] = half_to_f32(static_cast<uint16_t>(wd[e] >> 16), is_bf16);
+        if constexpr (BF) {
+          w[2 * e] = __uint_as_float(wd[e] << 16);
+          w[2 * e + 1] = __uint_as_float(wd[e] & 0xFFFF0000u);
+        } else {
+          w[2 * e] = fp16_to_f32(static_cast<uint16_t>(wd[e] & 0xFFFF));
+          w[2 * e + 1] = fp16_to_f32(static_cast<uint16_t>(wd[e] >> 16));
+        }
       }
       float acc = 0.f;
       if constexpr (QREG) {
@@ -275,11 +317,22 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc += qg[e] * w[e];
       }
-#pragma unroll
-      for (int m = 1; m < VPI; m <<= 1) acc += __shfl_xor(acc, m);
+      acc = group_sum<VPI>(acc);
       if (part == 0 && vv < VP)
-        scp[g * kPage + item / H_kv] = ok ? acc : -__builtin_inff();
+        scp[g * kScPitch + tok] = ok ? acc : -__builtin_inff();
+      g += dg;
+      tok += dt;
+      if (g >= H_kv) {
+        g -= H_kv;
+        ++tok;
+      }
     }
+  };
+  auto sum_any = [&](int u, const uint4 (&x)[8]) {
+    if (is_bf16)
+      sum_unit(Bool<true>{}, u, x);
+    else
+      sum_unit(Bool<false>{}, u, x);
   };
   uint4 xa[8];
   if constexpr (EARLY) {
@@ -294,32 +347,32 @@ __global__ __launch_bounds__(kThreads) void ds_scan_vec_kernel(
     for (int e = 0; e < 8; ++e) qr[e] = qs[g * r + part * 8 + e];
   }
   if constexpr (ONE) {
-    sum_unit(0, xa);
+    sum_any(0, xa);
     __syncthreads();
     for (int it = tid; it < tpu * H_kv; it += kThreads) {
       const int g = it / tpu, sl = sub0 * tpu + it % tpu;
       const int64_t t = pp0 * kPage + sl;
-      if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = sc[g * kPage + sl];
+      if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = sc[g * kScPitch + sl];
     }
     return;
   } else {
   uint4 xb[8];
   for (int u = 0; u < units; u += 2) {
     if (u + 1 < units) load_unit(u + 1, xb);
-    sum_unit(u, xa);
+    sum_any(u, xa);
     if (u + 2 < units) load_unit(u + 2, xa);
-    if (u + 1 < units) sum_unit(u + 1, xb);
+    if (u + 1 < units) sum_any(u + 1, xb);
     // a page is complete after its last sub-block: store its scores
     for (int d = 0; d < 2; ++d) {
       const int uu = u + d;
       if (uu >= units || (uu + 1) % SB != 0) continue;  // uniform
       __syncthreads();
       const int pg = uu / SB;
-      const float* scp = sc + (pg & 1) * kPage * H_kv;
+      const float* scp = sc + (pg & 1) * kScPitch * H_kv;
       for (int it = tid; it < kPage * H_kv; it += kThreads) {
         const int g = it / kPage, sl = it % kPage;
         const int64_t t = (pp0 + pg) * kPage + sl;
-        if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = scp[it];
+        if (t < n) scores[(static_cast<int64_t>(b) * H_kv + g) * score_stride + t] = scp[g * kScPitch + sl];
       }
       __syncthreads();  // the buffer is written again two pages later
     }
@@ -356,7 +409,7 @@ bool launch_vec(const tsd_score_args& a, hipStream_t s) {
   // power-of-two number of full ones
   const bool one = P == 1 && (SB == 1 || ((8 * hc) % kSubVec == 0 &&
                                           (SB & (SB - 1)) == 0 && SB <= kPage));
-  const size_t lds = static_cast<size_t>(hc + 2 * kPage * a.H_kv + P) * 4;
+  const size_t lds = static_cast<size_t>(hc + 2 * kScPitch * a.H_kv + P) * 4;
   dim3 grid(static_cast<uint32_t>(one ? a.pt_stride * SB : (a.pt_stride + P - 1) / P),
             static_cast<uint32_t>(a.B));
   const bool qreg = (kThreads / VPI) % a.H_kv == 0;
