@@ -256,6 +256,35 @@ def test_ds_label_scan_vector_layouts(H_q, H_kv, r, lens):
     check_scores(S.cpu().numpy(), ref, want, score_tol("ds"))
 
 
+@pytest.mark.parametrize("enc", ["fp16", "bf16"])
+@pytest.mark.parametrize("r", [8, 16, 32, 64, 128])
+@pytest.mark.parametrize("H_kv", [8, 24])
+def test_ds_label_scan_types_and_label_widths(enc, r, H_kv):
+    """Both 16-bit label types at every vector width of a label (r / 8
+    lanes per label, 1 .. 16, their partial dots added across lanes), with
+    a head count that keeps every lane on one head (8) and one that does
+    not (24), two query heads per KV head: every score against the
+    oracle."""
+    import top_sparse_decode_amd as tsd
+    lens = (1500, 77)
+    cfg = tsd_synth.config(DS8B, B=len(lens), H_q=2 * H_kv, H_kv=H_kv, r=r,
+                           n_outlier=r, lens=lens, kv_enc=enc, top_k=64,
+                           chunks=2, seed=131 + r + H_kv)
+    wl = tsd_synth.make(cfg, DEV)
+    h = tsd_synth.to_host(wl)
+    ref = oracle_scores(h)
+    stride = wl["page_table"].shape[1] * 64
+    S = torch.full((cfg.B * H_kv, stride), float("nan"), device=DEV)
+    rl = torch.empty(cfg.B * H_kv, dtype=torch.int32, device=DEV)
+    tsd.sparse_index_score("ds", S, wl["page_table"], wl["seq_lens"], wl["num_pages"],
+                           q=wl["q"], channel_idx=wl["channel_idx"],
+                           label_pool=wl["label_pool"], row_lens_out=rl)
+    torch.cuda.synchronize()
+    want = np.repeat(np.array(lens), H_kv)
+    np.testing.assert_array_equal(rl.cpu().numpy(), want)
+    check_scores(S.cpu().numpy(), ref, want, score_tol("ds"))
+
+
 def test_ds_stale_tail_and_empty_request():
     cfg = tsd_synth.config(DS8B, B=3, lens=(0, 1000, 65), top_k=128, chunks=3,
                            stale_tail=True, seed=112)
