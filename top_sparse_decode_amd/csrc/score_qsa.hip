@@ -17,12 +17,20 @@
 // stays a single streaming pass over the index-K pages: every byte is read
 // once, the query rows sit in registers for the whole scan.
 //
-// Work split: one wave owns one query row and a run of up to 64 consecutive
+// Work split: one wave owns one query row and a run of up to 32 consecutive
 // 64-token pages; a page is 4 tiles of 16 keys. The 16x16 f32 result gives lane
 // l the dots of key (l % 16) with heads 4*(l/16) .. 4*(l/16)+3; the weighted
 // ReLU is applied per lane and a 3-shuffle reduce-scatter over the 4 lane
 // groups leaves lane l with the full score of key l of the page, so a page
 // stores 256 contiguous bytes of scores.
+//
+// A page is read as 8 contiguous 1 KB loads (lane l: bytes 16 l .. 16 l + 15
+// of each KB, whole 128-byte lines per instruction) and transposed through
+// LDS into the operand layout, lane (key c, k-group kb) taking bytes
+// 32 kb .. 32 kb + 31 of key c; the query row's lanes take the same bytes, so
+// every instruction pairs equal dims. Loads in the operand layout itself (64
+// bytes of each of 16 keys per instruction, half of every line) read the
+// pages 10-18 % slower on this part.
 //
 // The chunked-prefill kernel below is a dense contraction that is bound by
 // the matrix cores, and it keeps the FP8 instruction at twice the bf16 rate;
@@ -63,18 +71,20 @@ TSD_DEVICE float weighted_relu4(v4f d, float w0, float w1, float w2, float w3) {
   return fmaf(w3, m3, fmaf(w2, m2, fmaf(w0, m0, w1 * m1)));
 }
 
-// load_row_slice with non-temporal loads (data read once).
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-TSD_DEVICE v8i load_row_slice_nt(const uint8_t* row, int kb) {
-  const v4u lo = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + 16 * kb));
-  const v4u hi = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(row + 64 + 16 * kb));
+// Bytes 32 kb .. 32 kb + 31 of a 128-byte FP8 row: the decode scan's
+// operand slice, for its query rows (global memory) and its keys (LDS).
+TSD_DEVICE v8i load_row_chunk32(const uint8_t* row, int kb) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(row + 32 * kb);
+  const uint4 hi = *reinterpret_cast<const uint4*>(row + 32 * kb + 16);
   v8i v;
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
 }
 
-// The 32 FP8 codes of a lane's operand slice (as load_row_slice packs them)
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// The 32 FP8 codes of a lane's operand slice (as the row loaders pack them)
 // widened exactly to bf16 (every E4M3 value is a bf16 value) as the four
 // operands of the bf16 16x16x32 MFMA: operand s holds the codes of dwords
 // 2s and 2s + 1. Index heads and keys are widened the same way, so each
@@ -120,9 +130,13 @@ TSD_DEVICE v4f mfma_fp8(v8i a, v8i b) {
 
 // One wave owns G consecutive pages of one row. Pages are contracted in
 // pairs with the next pair's loads already in flight (two register sets of
-// 2 pages x 4 tiles), and the wave's scores are staged in LDS and stored in
-// one burst after its last page: stores issued between the loads would
-// share the loads' completion counter and stall every later wait on them.
+// 2 pages x 8 contiguous 16-byte loads per lane); each page passes through
+// the wave's LDS staging rows half a page (32 keys, two tiles) at a time, at
+// a 144-byte row pitch, so that the contiguous stores and the operand reads
+// (lanes c = 0..15 of one k-group at 36 c mod 64 banks) are conflict-free.
+// The wave's scores are staged in LDS and stored in one burst after its
+// last page: stores issued between the loads would share the loads'
+// completion counter and stall every later wait on them.
 //
 // HIST: also accumulate the first top-k radix digit of every written score
 // into the top-k workspace's digit-1 histograms (LDS-privatised per
@@ -144,8 +158,11 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     int32_t* __restrict__ row_lens_out, void* __restrict__ topk_base,
     int hist_k) {
   static_assert(G % 4 == 0 && G <= kWave, "pages per wave: one page id per lane");
+  constexpr int kStRows = kPage / 2;   // keys staged at a time
+  constexpr int kStPitch = kDi + 16;   // LDS bytes per staged key
   __shared__ __align__(16) uint32_t hist_s[HIST ? kTopkBins1 : 4];
   __shared__ float res_s[kWavesPerBlock][G * kPage];
+  __shared__ __align__(16) uint8_t kst_s[kWavesPerBlock][kStRows * kStPitch];
   const int lane = threadIdx.x & (kWave - 1);
   // the wave's index is uniform: held in scalar registers, so the row and
   // request divisions run once per wave on the scalar unit
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     // A operand: index head `col` of this row (zero for padded heads);
     // the weights of the 4 heads whose dots this lane receives
     if (col < H_i)
-      qa8 = load_row_slice(
+      qa8 = load_row_chunk32(
           index_q + (static_cast<int64_t>(row) * H_i + col) * kDi, kb);
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -220,7 +237,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
     // npg or outside [0, num_pages) reads page 0 (which exists, num_pages >=
     // 1 here) and scores -inf. The index keys are read once per step, so
     // the loads are non-temporal.
-    auto load2 = [&](int j, v8i (&kt)[2][4], bool (&valid)[2]) {
+    auto load2 = [&](int j, v4u (&kt)[2][8], bool (&valid)[2]) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         const bool live = j + d < npg;
@@ -230,19 +247,34 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
         const uint8_t* base =
             index_k + static_cast<int64_t>(valid[d] ? page : 0) * kPage * kDi;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          kt[d][i] = load_row_slice_nt(base + (16 * i + col) * kDi, kb);
+        for (int m = 0; m < 8; ++m)  // keys 8m .. 8m + 7, 16 bytes per lane
+          kt[d][m] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4u*>(base + 1024 * m) + lane);
       }
     };
-    auto score2 = [&](int j, const v8i (&kt)[2][4], const bool (&valid)[2]) {
+    uint8_t* kst = kst_s[wl];
+    auto score2 = [&](int j, const v4u (&kt)[2][8], const bool (&valid)[2]) {
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
         if (j + d >= npg) break;  // uniform
         float part[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4f dd = mfma_bf16_dot(qa, kt[d][i]);
-          part[i] = weighted_relu4(dd, w[0], w[1], w[2], w[3]);
+        for (int h = 0; h < 2; ++h) {  // keys 32h .. 32h + 31
+          // LDS operations of one wave run in order: every lane's staged
+          // bytes are in place before the operand reads, and the reads are
+          // done before the next half overwrites them
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<v4u*>(kst + (8 * m + (lane >> 3)) * kStPitch +
+                                    16 * (lane & 7)) = kt[d][4 * h + m];
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const v8i kb8 = load_row_chunk32(kst + (16 * i + col) * kStPitch, kb);
+            const v4f dd = mfma_bf16_dot(qa, kb8);
+            part[2 * h + i] = weighted_relu4(dd, w[0], w[1], w[2], w[3]);
+          }
+          __builtin_amdgcn_wave_barrier();
         }
         // reduce-scatter over the 4 lane groups: lane l gets key l
         const float red = reduce_scatter4(part);
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(kWavesPerBlock * kWave) void qsa_scan_kernel(
           atomicAdd(&hist_s[topk_digit1(order_key(sc))], 1u);
       }
     };
-    v8i ka[2][4], kc[2][4];
+    v4u ka[2][8], kc[2][8];
     bool va[2], vc[2];
     if (num_pages > 0) {
       load2(0, ka, va);
@@ -536,11 +568,11 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                        a.row_lens_out);
     return hipGetLastError();
   }
-  // pages per wave: 64 when that still gives >= 2,048 waves (two resident
-  // workgroups per CU, so the launch runs in a single pass), else the most
-  // (up to 32) that still gives >= 1,024 waves
+  // pages per wave: the most (up to 32) that still gives >= 1,024 waves;
+  // at 32 a workgroup's LDS (scores, staging rows, histogram: 66 KB) and
+  // its 4 waves' registers leave room for two workgroups per CU
   const int64_t pages = a.pt_stride * static_cast<int64_t>(rows);
-  int G = pages / 64 >= 2048 ? 64 : 32;
+  int G = 32;
   while (G > 4 && pages / G < 1024) G /= 2;
   int64_t waves_per_row = (a.pt_stride + G - 1) / G;
   if (topk_ws)  // whole workgroups per row
@@ -554,13 +586,11 @@ hipError_t launch_qsa_scan(const tsd_score_args& a, hipStream_t s,
                         void*, int);
   Kern kern;
   if (topk_ws)
-    kern = G == 64 ? qsa_scan_kernel<64, true>
-         : G == 32 ? qsa_scan_kernel<32, true>
+    kern = G == 32 ? qsa_scan_kernel<32, true>
          : G == 16 ? qsa_scan_kernel<16, true>
          : G == 8  ? qsa_scan_kernel<8, true> : qsa_scan_kernel<4, true>;
   else
-    kern = G == 64 ? qsa_scan_kernel<64, false>
-         : G == 32 ? qsa_scan_kernel<32, false>
+    kern = G == 32 ? qsa_scan_kernel<32, false>
          : G == 16 ? qsa_scan_kernel<16, false>
          : G == 8  ? qsa_scan_kernel<8, false> : qsa_scan_kernel<4, false>;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(blocks)),
