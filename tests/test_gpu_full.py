@@ -229,6 +229,18 @@ def test_full_qsa_decode_b8_l262144(fused):
 
 
 @FUSED
+def test_full_qsa_two_requests_eight_pages_per_scan_wave(fused):
+    """Two requests on a 4,096-page table (8,192 pages): the scan takes 8
+    pages per wave, the form the 8 x 262,144 (32) and 1 x 1,048,576 (16)
+    workloads and the small cases (4) leave out."""
+    wl = tsd_synth.make(tsd_synth.config("qsa_decode_b8_l262144_k2048", B=2,
+                                         lens=(262144, 150001), seed=161), DEV)
+    bufs = _run(wl, fused)
+    _check_layer(wl, bufs, full_rows=[1],
+                 label=f"qsa b2 {'fused' if fused else 'separate'}")
+
+
+@FUSED
 def test_full_qsa_decode_b1_l1048576(fused):
     wl = tsd_synth.make("qsa_decode_b1_l1048576_k2048", DEV)
     bufs = _run(wl, fused)

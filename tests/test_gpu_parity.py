@@ -1161,7 +1161,8 @@ def test_graph_replay_matches_eager(fused, first):
     (QSA, dict(B=3, lens=(9000, 4097, 130), top_k=512, chunks=8)),
     (QSA, dict(B=2, lens=(700, 129), top_k=100, chunks=4, stale_tail=True)),
     (QSA, dict(B=2, lens=(2048, 50), top_k=2048, chunks=16)),
-    # 64 pages per scan wave (32 rows of a 4,096-page table)
+    # 32 rows of a 4,096-page table: 4,096 scan waves of 32 pages, more
+    # than one pass of resident workgroups
     (QSA, dict(B=32, lens=(262144,) + tuple((i * 997) % 9000
                                              for i in range(1, 32)),
                top_k=256, chunks=4)),
