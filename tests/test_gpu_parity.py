@@ -78,7 +78,7 @@ DS7B = "ds_llama7b_b3_l20000_s200"
     ((1000, 0, 130), 300, 3),
     ((64, 65, 128), 64, 1),
     ((2048, 700), 2048, 16),
-    # 32 rows of a 4,096-page table: 64 pages per scan wave
+    # 32 rows of a 4,096-page table: 4,096 scan waves of 32 pages
     ((262144,) + tuple((i * 997) % 9000 for i in range(1, 32)), 256, 4),
     # the largest k and chunk count the contract takes, on a chunked-top-k row
     ((40000, 9000), 4096, 64),
