@@ -650,6 +650,28 @@ def test_merge_sharded_sixteen_shards_and_unordered_lists():
         np.testing.assert_array_equal(idx.cpu().numpy(), midx)
 
 
+def test_merge_sharded_rows_past_one_bitmap_segment():
+    """Four shards of 400,000 tokens: a row's global tokens run to 1.6M,
+    past the merge's 1,048,576-token output bitmap, so its kept tokens are
+    written over two segments; the result equals the oracle merge."""
+    import top_sparse_decode_amd as tsd
+    rng = np.random.default_rng(53)
+    W, rows, L, k = 4, 2, 400000, 2048
+    S = rng.standard_normal((W, rows, L)).astype(np.float32)
+    lens = np.full((W, rows), L, np.int32)
+    lens[2, 1] = 300000
+    Sg = torch.from_numpy(S).to(DEV)
+    il, cl = gpu_topk_stack(Sg, torch.from_numpy(lens).to(DEV), k)
+    midx, mcnt = oracle.topk_merge_sharded(S, il.cpu().numpy(), cl.cpu().numpy(), k)
+    assert (midx >= 1 << 20).any() and ((midx >= 0) & (midx < 1 << 20)).any()
+    idx = torch.full((rows, k), -7, dtype=torch.int32, device=DEV)
+    cnt = torch.full((rows,), -7, dtype=torch.int32, device=DEV)
+    tsd.topk_merge_sharded(Sg, il, cl, k, idx, cnt)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cnt.cpu().numpy(), mcnt)
+    np.testing.assert_array_equal(idx.cpu().numpy(), midx)
+
+
 def test_merge_sharded_short_lists_and_bad_entries():
     import top_sparse_decode_amd as tsd
     # hand-made candidate lists: counts below kl, -1 and out-of-range
